@@ -1,0 +1,176 @@
+"""Whole decode steps on the GPU against the oracle, step by step.
+
+Each step runs the four library calls; the oracle then checks every stage:
+scores within the fp32 accumulation bound, the top-k set bit-exact against
+the oracle's top-k of the GPU's own float32 scores and within the 1e-5
+swap tolerance against the oracle's fp64 scores, the working set bit-exact
+given the GPU's selection, the pool bytes, and the attention output within
+tolerance (computed by the oracle straight from the source K/V).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_sparse_kv_block_amd import binding as B
+from top_sparse_kv_block_amd import synth
+from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig, decode_step
+from gpu_util import dev, host, log, max_rel_row_err, topk_swaps_ok
+
+pytestmark = pytest.mark.gpu
+
+GAMMA = 16 * 2.0 ** -24
+
+
+def _abs(a):
+    return (a & np.uint16(0x7FFF)) if a.dtype == np.uint16 else np.abs(a)
+
+
+def _forced_sets(w, lens):
+    out = []
+    for b in range(w.batch):
+        L = int(lens[b])
+        nv = -(-L // 16)
+        f = set()
+        if nv > w.k_blocks:
+            if w.sink:
+                f |= set(range(-(-min(w.sink, L) // 16)))
+            if w.recent:
+                f |= set(range(max(0, L - w.recent) // 16, nv))
+        out += [f] * w.n_kv_heads
+    return out
+
+
+def run_workload(w, steps=None, rows=None, heads=None, check_scores=True):
+    """Run `steps` steps of workload `w`; check rows `rows` (None = all) of
+    the scores and (b, h) pairs `heads` (None = all) of the attention."""
+    steps = steps or w.steps
+    data = synth.gen_workload(w.scaled(steps=steps))
+    q, sq, K, V, lens = data["q"], data["score_q"], data["K"], data["V"], data["seq_lens"]
+    mode = B.SKV_SCORE_QUEST if w.scoring == "quest" else B.SKV_SCORE_BLOCKMAX
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
+                     mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent)
+    buf = LayerBuffers(cfg)
+    dK, dV, dlens = dev(K), dev(V), dev(lens)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    P = w.rows
+    if mode == B.SKV_SCORE_QUEST:
+        meta = torch.empty(w.batch, w.n_kv_heads, w.nb_max, 2, w.head_dim, dtype=cfg.torch_dtype, device="cuda")
+        B.sparse_kv_quest_meta(cfg.shape, dK, dlens, meta)
+        keys_or_meta = meta
+        meta_ref = oracle.quest_meta(K, lens)
+    else:
+        keys_or_meta = dK
+    lru = oracle.LRU(P, w.capacity)
+    forced = _forced_sets(w, lens)
+    rows = list(range(P)) if rows is None else rows
+    total_miss = 0
+    for t in range(steps):
+        log(w.name, "step", t, (w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx))
+        decode_step(buf, dev(q[t]), dev(sq[t]), keys_or_meta, dlens, dK, dV)
+        torch.cuda.synchronize()
+        g_scores = host(buf.scores).astype(np.float64)
+        g_sel, g_cnt = host(buf.sel_blocks), host(buf.sel_count)
+        # stage 1: sampled rows against the fp64 oracle
+        ora_rows = {}
+        if check_scores:
+            for r_ in rows:
+                b, j = divmod(r_, w.n_kv_heads)
+                G = w.group
+                qr = np.ascontiguousarray(sq[t][b:b + 1, :, j * G:(j + 1) * G])
+                if mode == B.SKV_SCORE_QUEST:
+                    mr = np.ascontiguousarray(meta_ref[b:b + 1, j:j + 1])
+                    ref = oracle.score_quest(qr, mr, lens[b:b + 1], scale, T=w.ctx)[0, 0]
+                    box = np.maximum(np.abs(mr[..., 0, :]), np.abs(mr[..., 1, :]))
+                    qa = np.abs(synth.bf16_bits_to_f32(qr) if qr.dtype == np.uint16 else qr).astype(np.float32)
+                    bound = oracle.score_quest(qa, np.stack([box, box], -2), lens[b:b + 1], scale, T=w.ctx)[0, 0]
+                else:
+                    kr = np.ascontiguousarray(K[b:b + 1, j:j + 1])
+                    ref = oracle.score_blockmax(qr, kr, lens[b:b + 1], scale)[0, 0]
+                    bound = oracle.score_blockmax(_abs(qr), _abs(kr), lens[b:b + 1], scale)[0, 0]
+                got = g_scores[b, j]
+                fin = np.isfinite(ref)
+                assert np.array_equal(fin, np.isfinite(got))
+                assert np.all(np.abs(got[fin] - ref[fin]) <= GAMMA * bound[fin] + 2.0 ** -23 * np.abs(ref[fin]))
+                ora_rows[r_] = ref
+        # stage 2: exact on the GPU's scores, tolerance rule on fp64 scores
+        s_sel, s_cnt = oracle.topk(g_scores, lens, w.k_blocks, w.ctx, sink=w.sink, recent=w.recent)
+        np.testing.assert_array_equal(g_cnt, s_cnt)
+        np.testing.assert_array_equal(g_sel, s_sel)
+        for r_ in sorted(ora_rows):
+            b = r_ // w.n_kv_heads
+            o_sel, o_cnt = oracle.topk(ora_rows[r_][None, None], lens[b:b + 1], w.k_blocks, w.ctx, sink=w.sink,
+                                       recent=w.recent)
+            bad = topk_swaps_ok(g_sel.reshape(P, -1)[r_:r_ + 1], g_cnt.reshape(P)[r_:r_ + 1], o_sel[0], o_cnt[0],
+                                ora_rows[r_][None], forced=[forced[r_]])
+            assert not bad, bad[:5]
+        # stage 3: bit-exact given the GPU's selection
+        out = lru.step(g_sel.reshape(P, -1), g_cnt.reshape(P), w.nb_max)
+        np.testing.assert_array_equal(host(buf.miss_count).reshape(P), out["miss_count"])
+        np.testing.assert_array_equal(host(buf.sel_slot).reshape(P, -1), out["sel_slot"])
+        np.testing.assert_array_equal(host(buf.sel_hit).reshape(P, -1), out["sel_hit"])
+        np.testing.assert_array_equal(host(buf.miss_block).reshape(P, -1), out["miss_block"])
+        np.testing.assert_array_equal(host(buf.miss_slot).reshape(P, -1), out["miss_slot"])
+        np.testing.assert_array_equal(host(buf.slot_block).reshape(P, -1), lru.slot_block())
+        total_miss += int(out["miss_count"].sum())
+        # pool bytes of the sampled rows equal the source blocks they hold
+        pk, pv = host(buf.pool_k).reshape(P, w.capacity, 16, w.head_dim), host(buf.pool_v).reshape(
+            P, w.capacity, 16, w.head_dim)
+        sb = lru.slot_block()
+        for r_ in rows[:4]:
+            b, j = divmod(r_, w.n_kv_heads)
+            for s_, blk in enumerate(sb[r_]):
+                if blk >= 0:
+                    assert np.array_equal(pk[r_, s_], K[b, j, blk * 16:blk * 16 + 16])
+                    assert np.array_equal(pv[r_, s_], V[b, j, blk * 16:blk * 16 + 16])
+        # stage 4: attention from the source by block id
+        g_out = host(buf.out)
+        hs = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)] if heads is None else heads
+        for b in sorted({b for b, _ in hs}):
+            o_ref, _ = oracle.attention(q[t][b:b + 1], K[b:b + 1], V[b:b + 1], g_sel[b:b + 1], g_cnt[b:b + 1],
+                                        lens[b:b + 1], scale)
+            hh = [h for bb, h in hs if bb == b]
+            err = max_rel_row_err(g_out[b, hh], o_ref[0, hh])
+            if w.dtype == "f32":
+                assert np.abs(g_out[b, hh] - o_ref[0, hh]).max() <= 1e-4
+            assert err <= 2e-2 and err <= 1e-4, err
+    return total_miss
+
+
+def test_tiny_workload_all_steps():
+    run_workload(synth.WORKLOADS["tiny"])
+
+
+def test_tiny_workload_capacity_equals_budget_transfer_invariant():
+    w = synth.WORKLOADS["tiny"].scaled(capacity=8)
+    run_workload(w)
+
+
+def test_llama8b_reduced_context():
+    w = synth.WORKLOADS["llama8b_32k"].scaled(batch=2, ctx=4096, budget=512)
+    run_workload(w, steps=6)
+
+
+def test_llama8b_ragged_lengths():
+    w = synth.WORKLOADS["llama8b_32k"].scaled(batch=3, ctx=2048 + 16 * 7, budget=256, capacity=40, ragged=True)
+    run_workload(w, steps=4)
+
+
+def test_quest_reduced():
+    w = synth.WORKLOADS["quest_128k"].scaled(batch=2, ctx=8192)
+    run_workload(w, steps=5)
+
+
+def test_lookahead_drafts_reduced():
+    w = synth.WORKLOADS["lookahead_1m"].scaled(ctx=16384)
+    run_workload(w, steps=3)
+
+
+def test_llama8b_full_size_sampled():
+    # full throughput workload (launch configuration of the benchmark); the
+    # oracle checks sampled score rows and attention heads, and every row of
+    # top-k (on the GPU's scores) and of the working set
+    w = synth.WORKLOADS["llama8b_32k"]
+    run_workload(w, steps=3, rows=[0, 21, 63], heads=[(0, 0), (2, 13), (7, 31)])

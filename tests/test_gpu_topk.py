@@ -1,0 +1,68 @@
+"""GPU parity of stage 2 (per-row top-k) against the oracle.
+
+Given the same float32 scores the selection is an integer result decided in
+the kernel's precision, so the oracle runs on the GPU's own scores (widened
+exactly to fp64) and the sets must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_sparse_kv_block_amd import binding as B
+from gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(scores, lens, k, sink=0, recent=0, Hkv=None):
+    B_, hkv, nb = scores.shape
+    shape = B.make_shape(B_, hkv, hkv, 64, nb * 16, "f32")
+    sel = torch.empty(B_, hkv, k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B_, hkv, dtype=torch.int32, device="cuda")
+    log("topk", (B_, hkv, nb), "k", k, "sink", sink, "recent", recent)
+    B.sparse_kv_topk(shape, dev(scores.astype(np.float32)), dev(np.asarray(lens, np.int32)), k, sink, recent, sel, cnt)
+    torch.cuda.synchronize()
+    ref_sel, ref_cnt = oracle.topk(scores.astype(np.float32).astype(np.float64), np.asarray(lens, np.int32), k,
+                                   nb * 16, sink=sink, recent=recent)
+    np.testing.assert_array_equal(host(cnt), ref_cnt)
+    np.testing.assert_array_equal(host(sel), ref_sel)
+
+
+@pytest.mark.parametrize("nb,k", [(64, 8), (2048, 128), (3000, 100), (8192, 32), (20000, 300), (65536, 128)])
+def test_topk_random_scores(nb, k):
+    r = np.random.default_rng(nb + k)
+    s = r.standard_normal((2, 3, nb)).astype(np.float32)
+    _run(s, [nb * 16, nb * 16 - 100], k)
+
+
+def test_topk_heavy_ties_break_to_lower_ids():
+    r = np.random.default_rng(7)
+    s = (np.round(r.standard_normal((2, 4, 2048)) * 2) / 2).astype(np.float32)  # few distinct values
+    s[1, 0, :] = 1.0  # a whole row of equal scores: the lowest ids win
+    s[1, 1, :] = 0.0
+    s[1, 1, ::2] = -0.0  # signed zeros compare equal
+    _run(s, [32768, 32768], 128)
+
+
+def test_topk_ragged_lengths_and_small_rows():
+    r = np.random.default_rng(8)
+    s = r.standard_normal((6, 2, 1024)).astype(np.float32)
+    _run(s, [0, 1, 100, 16 * 130, 16 * 129 + 1, 16 * 1024], 130)
+
+
+@pytest.mark.parametrize("sink,recent", [(4, 128), (20, 0), (0, 40), (16, 17)])
+def test_topk_sink_and_recent(sink, recent):
+    r = np.random.default_rng(9)
+    s = r.standard_normal((3, 2, 8192)).astype(np.float32)
+    s[:, :, 0] = -50  # forced blocks must be kept whatever their score
+    _run(s, [131072, 131072 - 5, 1000], 32, sink=sink, recent=recent)
+
+
+def test_topk_rejects_too_many_forced_blocks():
+    shape = B.make_shape(1, 1, 1, 64, 1024, "f32")
+    t = lambda *a, **kw: torch.zeros(*a, device="cuda", **kw)
+    with pytest.raises(B.SparseKVError) as e:
+        B.sparse_kv_topk(shape, t(1, 1, 64), t(1, dtype=torch.int32), 4, 16, 64, t(1, 1, 4, dtype=torch.int32),
+                         t(1, 1, dtype=torch.int32))
+    assert e.value.status == 4

@@ -1,0 +1,215 @@
+// C ABI of the sparse KV-cache decode step: argument validation on the host,
+// then stream-ordered kernel launches.  Nothing here allocates, synchronises
+// or keeps state between calls.
+#include "sparse_kv.h"
+#include "skv_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#define SKV_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using skv::Dims;
+
+skv_status check_shape(const skv_shape *s, Dims &d) {
+    if (!s)
+        return SKV_ERR_NULL;
+    if (s->dtype != SKV_F32 && s->dtype != SKV_BF16)
+        return SKV_ERR_DTYPE;
+    if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->n_q_heads % s->n_kv_heads != 0)
+        return SKV_ERR_SHAPE;
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return SKV_ERR_SHAPE;
+    if (s->block_size != 16 || s->max_ctx < 16 || s->max_ctx % 16 != 0)
+        return SKV_ERR_SHAPE;
+    if ((long long)s->batch * s->n_kv_heads > 65535)
+        return SKV_ERR_SHAPE;
+    d.B = s->batch;
+    d.Hq = s->n_q_heads;
+    d.Hkv = s->n_kv_heads;
+    d.D = s->head_dim;
+    d.T = s->max_ctx;
+    d.NB = s->max_ctx / 16;
+    d.dtype = s->dtype;
+    return SKV_OK;
+}
+
+skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_HIP; }
+
+int nb_blocks(int tokens) { return (tokens + 15) / 16; }
+
+}  // namespace
+
+SKV_API skv_status sparse_kv_score(const skv_shape *shape, int32_t mode, const void *q, int32_t n_queries,
+                                   const void *keys_or_meta, const int32_t *seq_lens, float scale, float *scores,
+                                   void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!q || !keys_or_meta || !seq_lens || !scores)
+        return SKV_ERR_NULL;
+    if (n_queries < 1 || n_queries > 4 || n_queries * d.G() > skv::kMaxQueryRows)
+        return SKV_ERR_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == SKV_SCORE_BLOCKMAX)
+        return hip_status(skv::launch_score_blockmax(d, q, n_queries, keys_or_meta, seq_lens, scale, scores, s));
+    if (mode == SKV_SCORE_QUEST)
+        return hip_status(skv::launch_score_quest(d, q, n_queries, keys_or_meta, seq_lens, scale, scores, s));
+    return SKV_ERR_UNSUPPORTED;
+}
+
+SKV_API skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                                  int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t *sel_blocks,
+                                  int32_t *sel_count, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!scores || !seq_lens || !sel_blocks || !sel_count)
+        return SKV_ERR_NULL;
+    if (d.NB > skv::kMaxTopkBlocks)
+        return SKV_ERR_UNSUPPORTED;
+    if (k_blocks < 1 || k_blocks > d.NB || k_blocks > skv::kMaxK || sink_tokens < 0 || recent_tokens < 0)
+        return SKV_ERR_SHAPE;
+    if (sink_tokens > 0 || recent_tokens > 0) {
+        const long long forced_max = (long long)nb_blocks(sink_tokens) + nb_blocks(recent_tokens) + 1;
+        if (forced_max > k_blocks)
+            return SKV_ERR_CAPACITY;
+    }
+    return hip_status(skv::launch_topk(d, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, sel_blocks,
+                                       sel_count, (hipStream_t)stream));
+}
+
+SKV_API skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
+                                          const int32_t *sel_blocks, const int32_t *sel_count, int32_t *slot_block,
+                                          uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot,
+                                          uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot,
+                                          int32_t *miss_count, const void *src_k, const void *src_v,
+                                          int32_t src_kind, void *pool_k, void *pool_v, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!sel_blocks || !sel_count || !slot_block || !slot_stamp || !clock || !sel_slot || !sel_hit || !miss_block ||
+        !miss_slot || !miss_count)
+        return SKV_ERR_NULL;
+    if (k_blocks < 1 || k_blocks > skv::kMaxK || capacity < 1)
+        return SKV_ERR_SHAPE;
+    if (capacity < k_blocks)
+        return SKV_ERR_CAPACITY;
+    if (capacity > skv::kMaxCapacity)
+        return SKV_ERR_UNSUPPORTED;
+    if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
+        return SKV_ERR_SHAPE;
+    const bool fetch = src_k || src_v;
+    if (fetch && (!src_k || !src_v || !pool_k || !pool_v))
+        return SKV_ERR_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = skv::launch_cache_update(d, k_blocks, capacity, sel_blocks, sel_count, slot_block, slot_stamp,
+                                            clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, s);
+    if (e != hipSuccess || !fetch)
+        return hip_status(e);
+    return hip_status(
+        skv::launch_gather(d, k_blocks, capacity, miss_block, miss_slot, miss_count, src_k, src_v, pool_k, pool_v, s));
+}
+
+SKV_API int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k_blocks) {
+    Dims d;
+    if (check_shape(shape, d) != SKV_OK || k_blocks < 1)
+        return 0;
+    return skv::attention_auto_splits(d.rows(), k_blocks);
+}
+
+SKV_API size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits) {
+    Dims d;
+    if (check_shape(shape, d) != SKV_OK || k_blocks < 1 || num_splits < 0 || num_splits > k_blocks)
+        return 0;
+    const int splits = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
+    return skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
+}
+
+SKV_API skv_status sparse_decode_attention(const skv_shape *shape, const void *q, const void *pool_k,
+                                           const void *pool_v, int32_t capacity, const int32_t *sel_blocks,
+                                           const int32_t *sel_slot, const int32_t *sel_count,
+                                           const int32_t *seq_lens, int32_t k_blocks, float scale,
+                                           int32_t num_splits, float *out, float *lse, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!q || !pool_k || !pool_v || !sel_blocks || !sel_slot || !sel_count || !seq_lens || !out)
+        return SKV_ERR_NULL;
+    if (k_blocks < 1 || k_blocks > skv::kMaxK || capacity < 1 || num_splits < 0 || num_splits > k_blocks)
+        return SKV_ERR_SHAPE;
+    if (d.G() > skv::kMaxGroup)
+        return SKV_ERR_UNSUPPORTED;
+    const int splits = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
+    const size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return SKV_ERR_WORKSPACE;
+    return hip_status(skv::launch_attention(d, q, pool_k, pool_v, capacity, sel_blocks, sel_slot, sel_count, seq_lens,
+                                            k_blocks, scale, splits, out, lse, (float *)workspace,
+                                            (hipStream_t)stream));
+}
+
+SKV_API skv_status sparse_kv_quest_meta(const skv_shape *shape, const void *keys, const int32_t *seq_lens, void *meta,
+                                        void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!keys || !seq_lens || !meta)
+        return SKV_ERR_NULL;
+    return hip_status(skv::launch_quest_meta(d, keys, seq_lens, meta, (hipStream_t)stream));
+}
+
+SKV_API skv_status sparse_kv_host_alloc(size_t bytes, void **host_ptr, void **device_ptr) {
+    if (!host_ptr || !device_ptr)
+        return SKV_ERR_NULL;
+    *host_ptr = nullptr;
+    *device_ptr = nullptr;
+    if (bytes == 0)
+        return SKV_ERR_SHAPE;
+    void *h = nullptr;
+    if (hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocPortable) != hipSuccess)
+        return SKV_ERR_HIP;
+    void *dptr = nullptr;
+    if (hipHostGetDevicePointer(&dptr, h, 0) != hipSuccess) {
+        (void)hipHostFree(h);
+        return SKV_ERR_HIP;
+    }
+    *host_ptr = h;
+    *device_ptr = dptr;
+    return SKV_OK;
+}
+
+SKV_API skv_status sparse_kv_host_free(void *host_ptr) {
+    if (!host_ptr)
+        return SKV_ERR_NULL;
+    return hip_status(hipHostFree(host_ptr));
+}
+
+SKV_API const char *sparse_kv_status_string(skv_status s) {
+    switch (s) {
+    case SKV_OK:
+        return "ok";
+    case SKV_ERR_NULL:
+        return "a required pointer is NULL";
+    case SKV_ERR_SHAPE:
+        return "sizes are inconsistent or outside the supported range";
+    case SKV_ERR_DTYPE:
+        return "unsupported dtype";
+    case SKV_ERR_CAPACITY:
+        return "capacity smaller than k_blocks, or forced blocks exceed k_blocks";
+    case SKV_ERR_WORKSPACE:
+        return "workspace missing, misaligned or too small";
+    case SKV_ERR_UNSUPPORTED:
+        return "request not supported by this library";
+    case SKV_ERR_HIP:
+        return "HIP runtime error at launch";
+    }
+    return "unknown status";
+}

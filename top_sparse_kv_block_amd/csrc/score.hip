@@ -1,0 +1,328 @@
+// Stage 1: block scoring on gfx950.
+//
+// Exact block-max: a block's score is scale times the largest q.k over its
+// valid tokens, the GQA group's heads ("KV Cache 塞不进 HBM 了", §3 step 3:
+// element-wise max inside the group) and the scoring queries (lookahead
+// drafts: OasisKV summary, key module 2).
+// Quest bound: sum_d max(q_d*min_d, q_d*max_d) over a block's element-wise key
+// box, an upper bound of every q.k in the block.
+//
+// Layout on the chip.  A (b, kv-head) row of keys is T*D contiguous
+// elements; one 16-token block is 16*D*e contiguous bytes (4 KiB for bf16,
+// D=128).  A wave reads a block with fully coalesced 16-byte lane loads:
+// LPT = D*e/16 lanes share a token (each holds EPL consecutive elements),
+// TPL = 64/LPT tokens per wave load, 16/TPL loads per block.  Each lane
+// keeps the matching 16-byte slice of every query row in registers, forms
+// partial dot products (packed bf16 dot2 or fp32 FMA), and the LPT-lane
+// partials are summed with DPP row rotations; no LDS is used.  The work is
+// HBM-bound (about 4 flop per byte at G=4), so the kernel is organised
+// around keeping many 16-byte loads in flight: 4 waves per workgroup walk
+// interleaved blocks of one row, non-temporal loads for the key stream.
+#include "skv_device.h"
+#include "skv_launch.h"
+
+namespace skv {
+
+template <int LPT> __device__ __forceinline__ float groups_max(float v);
+template <> __device__ __forceinline__ float groups_max<8>(float v) {
+    v = fmaxf(v, dpp<DPP_ROW_ROR8>(v));
+    return rows_max(v);
+}
+template <> __device__ __forceinline__ float groups_max<16>(float v) { return rows_max(v); }
+template <> __device__ __forceinline__ float groups_max<32>(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+
+constexpr int kScoreWaves = 4;
+constexpr int kScoreBlocksPerWave = 8;
+
+template <typename E, int D, int RMAX>
+__global__ __launch_bounds__(256) void score_blockmax_kernel(const uint8_t *__restrict__ q,
+                                                             const uint8_t *__restrict__ keys,
+                                                             const int32_t *__restrict__ seq_lens,
+                                                             float *__restrict__ scores, int Hq, int Hkv, int NQ,
+                                                             int T, int NB, float scale) {
+    constexpr int LPT = D * E::bytes / 16;
+    constexpr int TPL = 64 / LPT;
+    constexpr int LPB = 16 / TPL;
+    const int row = blockIdx.y;
+    const int b = row / Hkv, j = row - b * Hkv;
+    const int G = Hq / Hkv;
+    const int R = NQ * G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % LPT, tg = lane / LPT;
+
+    u32x4 qf[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        if (r < R) {
+            const int rq = r / G, g = r - rq * G;
+            qf[r] = load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + sub * E::EPL) * E::bytes);
+        } else {
+            qf[r] = u32x4{0, 0, 0, 0};
+        }
+    }
+    const int len = min(max(seq_lens[b], 0), T);
+    const int nvalid = nb_of(len);
+    const uint8_t *krow = keys + (size_t)row * T * D * E::bytes;
+    float *srow = scores + (size_t)row * NB;
+    const int n0 = blockIdx.x * (kScoreWaves * kScoreBlocksPerWave);
+    const int n1 = min(n0 + kScoreWaves * kScoreBlocksPerWave, NB);
+
+    for (int n = n0 + wave; n < n1; n += kScoreWaves) {
+        if (n >= nvalid) {
+            if (lane == 0)
+                srow[n] = -__builtin_inff();
+            continue;
+        }
+        u32x4 kv[LPB];
+#pragma unroll
+        for (int i = 0; i < LPB; ++i)
+            kv[i] = load_nt(krow + ((size_t)(n * 16 + i * TPL + tg) * D + sub * E::EPL) * E::bytes);
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < LPB; ++i) {
+            float best = -__builtin_inff();
+#pragma unroll
+            for (int r = 0; r < RMAX; ++r) {
+                if (r < R)
+                    best = fmaxf(best, group_sum<LPT>(dot_chunk<E>(kv[i], qf[r], 0.0f)));
+            }
+            if (n * 16 + i * TPL + tg < len)
+                m = fmaxf(m, best);
+        }
+        m = groups_max<LPT>(m);
+        if (lane == 0)
+            srow[n] = m * scale;
+    }
+}
+
+// Quest bound.  max(q*lo, q*hi) = q * (q >= 0 ? hi : lo), so each lane
+// selects, per element, the box corner the query's sign points to (one
+// bit-select per packed word) and takes a plain dot product with q.
+template <typename E> __device__ __forceinline__ uint32_t neg_mask(uint32_t qw);
+template <> __device__ __forceinline__ uint32_t neg_mask<BF16>(uint32_t qw) {
+    return ((qw & 0x80008000u) >> 15) * 0xffffu;
+}
+template <> __device__ __forceinline__ uint32_t neg_mask<F32>(uint32_t qw) {
+    return (uint32_t)((int32_t)qw >> 31);
+}
+
+template <typename E, int D, int RMAX>
+__global__ __launch_bounds__(256) void score_quest_kernel(const uint8_t *__restrict__ q,
+                                                          const uint8_t *__restrict__ meta,
+                                                          const int32_t *__restrict__ seq_lens,
+                                                          float *__restrict__ scores, int Hq, int Hkv, int NQ, int T,
+                                                          int NB, float scale) {
+    constexpr int LPT = D * E::bytes / 16;  // lanes covering one D-vector
+    constexpr int BPL = 64 / LPT;           // blocks per wave iteration
+    const int row = blockIdx.y;
+    const int b = row / Hkv, j = row - b * Hkv;
+    const int G = Hq / Hkv;
+    const int R = NQ * G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % LPT, bg = lane / LPT;
+
+    u32x4 qf[RMAX], qm[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+        if (r < R) {
+            const int rq = r / G, g = r - rq * G;
+            qf[r] = load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + sub * E::EPL) * E::bytes);
+        } else {
+            qf[r] = u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            qm[r][w] = neg_mask<E>(qf[r][w]);
+    }
+    const int len = min(max(seq_lens[b], 0), T);
+    const int nvalid = nb_of(len);
+    const size_t vec_bytes = (size_t)D * E::bytes;
+    const uint8_t *mrow = meta + (size_t)row * NB * 2 * vec_bytes;
+    float *srow = scores + (size_t)row * NB;
+    const int per_wg = kScoreWaves * BPL * kScoreBlocksPerWave;
+    const int n0 = blockIdx.x * per_wg;
+    const int n1 = min(n0 + per_wg, NB);
+
+    for (int nb = n0 + wave * BPL; nb < n1; nb += kScoreWaves * BPL) {
+        const int n = nb + bg;
+        const bool in = n < n1 && n < nvalid;
+        u32x4 lo = u32x4{0, 0, 0, 0}, hi = u32x4{0, 0, 0, 0};
+        if (in) {
+            lo = load_nt(mrow + (size_t)n * 2 * vec_bytes + sub * 16);
+            hi = load_nt(mrow + (size_t)n * 2 * vec_bytes + vec_bytes + sub * 16);
+        }
+        float best = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < RMAX; ++r) {
+            if (r < R) {
+                u32x4 corner;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    corner[w] = (lo[w] & qm[r][w]) | (hi[w] & ~qm[r][w]);
+                best = fmaxf(best, group_sum<LPT>(dot_chunk<E>(corner, qf[r], 0.0f)));
+            }
+        }
+        if (sub == 0 && n < n1)
+            srow[n] = in ? best * scale : -__builtin_inff();
+    }
+}
+
+// Element-wise min / max of each block's valid keys (exact: the results are
+// stored values).  One wave per block.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void quest_meta_kernel(const uint8_t *__restrict__ keys,
+                                                         const int32_t *__restrict__ seq_lens,
+                                                         uint8_t *__restrict__ meta, int Hkv, int T, int NB) {
+    constexpr int LPT = D * E::bytes / 16;
+    constexpr int TPL = 64 / LPT;
+    constexpr int LPB = 16 / TPL;
+    const int row = blockIdx.y;
+    const int b = row / Hkv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % LPT, tg = lane / LPT;
+    const int n = blockIdx.x * 4 + wave;
+    if (n >= NB)
+        return;
+    const int len = min(max(seq_lens[b], 0), T);
+    const size_t vec_bytes = (size_t)D * E::bytes;
+    uint8_t *out = meta + ((size_t)row * NB + n) * 2 * vec_bytes;
+    if (n >= nb_of(len)) {
+        if (tg == 0) {
+            store16(out + sub * 16, u32x4{0, 0, 0, 0});
+            store16(out + vec_bytes + sub * 16, u32x4{0, 0, 0, 0});
+        }
+        return;
+    }
+    float lo[E::EPL], hi[E::EPL];
+#pragma unroll
+    for (int e = 0; e < E::EPL; ++e) {
+        lo[e] = __builtin_inff();
+        hi[e] = -__builtin_inff();
+    }
+    const uint8_t *krow = keys + (size_t)row * T * vec_bytes;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+        const int t = n * 16 + i * TPL + tg;
+        if (t < len) {
+            u32x4 v = load16(krow + (size_t)t * vec_bytes + sub * 16);
+#pragma unroll
+            for (int e = 0; e < E::EPL; ++e) {
+                float x;
+                if constexpr (E::bytes == 2)
+                    x = (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+                else
+                    x = __uint_as_float(v[e]);
+                lo[e] = fminf(lo[e], x);
+                hi[e] = fmaxf(hi[e], x);
+            }
+        }
+    }
+    // combine the token groups of the wave (LPT-lane groups)
+#pragma unroll
+    for (int e = 0; e < E::EPL; ++e) {
+        for (int off = LPT; off < 64; off <<= 1) {
+            lo[e] = fminf(lo[e], __shfl_xor(lo[e], off));
+            hi[e] = fmaxf(hi[e], __shfl_xor(hi[e], off));
+        }
+    }
+    if (tg == 0) {
+        u32x4 a, c;
+        if constexpr (E::bytes == 2) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                a[w] = (__float_as_uint(lo[2 * w]) >> 16) | (__float_as_uint(lo[2 * w + 1]) & 0xffff0000u);
+                c[w] = (__float_as_uint(hi[2 * w]) >> 16) | (__float_as_uint(hi[2 * w + 1]) & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                a[w] = __float_as_uint(lo[w]);
+                c[w] = __float_as_uint(hi[w]);
+            }
+        }
+        store16(out + sub * 16, a);
+        store16(out + vec_bytes + sub * 16, c);
+    }
+}
+
+// ------------------------------------------------------------------ launch
+template <typename E, int D, int RMAX>
+static hipError_t blockmax_t(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
+                             float scale, float *scores, hipStream_t st) {
+    const int per_wg = kScoreWaves * kScoreBlocksPerWave;
+    dim3 grid((d.NB + per_wg - 1) / per_wg, d.rows());
+    hipLaunchKernelGGL((score_blockmax_kernel<E, D, RMAX>), grid, dim3(256), 0, st, (const uint8_t *)q,
+                       (const uint8_t *)keys, lens, scores, d.Hq, d.Hkv, nq, d.T, d.NB, scale);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t blockmax_r(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
+                             float scale, float *scores, hipStream_t st) {
+    const int R = nq * d.G();
+    if (R <= 4)
+        return blockmax_t<E, D, 4>(d, q, nq, keys, lens, scale, scores, st);
+    if (R <= 8)
+        return blockmax_t<E, D, 8>(d, q, nq, keys, lens, scale, scores, st);
+    if (R <= 16)
+        return blockmax_t<E, D, 16>(d, q, nq, keys, lens, scale, scores, st);
+    return blockmax_t<E, D, 32>(d, q, nq, keys, lens, scale, scores, st);
+}
+
+hipError_t launch_score_blockmax(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
+                                 float scale, float *scores, hipStream_t st) {
+    if (d.dtype == 1)
+        return d.D == 128 ? blockmax_r<BF16, 128>(d, q, nq, keys, lens, scale, scores, st)
+                          : blockmax_r<BF16, 64>(d, q, nq, keys, lens, scale, scores, st);
+    return d.D == 128 ? blockmax_r<F32, 128>(d, q, nq, keys, lens, scale, scores, st)
+                      : blockmax_r<F32, 64>(d, q, nq, keys, lens, scale, scores, st);
+}
+
+template <typename E, int D, int RMAX>
+static hipError_t quest_t(const Dims &d, const void *q, int nq, const void *meta, const int32_t *lens, float scale,
+                          float *scores, hipStream_t st) {
+    constexpr int LPT = D * E::bytes / 16;
+    const int per_wg = kScoreWaves * (64 / LPT) * kScoreBlocksPerWave;
+    dim3 grid((d.NB + per_wg - 1) / per_wg, d.rows());
+    hipLaunchKernelGGL((score_quest_kernel<E, D, RMAX>), grid, dim3(256), 0, st, (const uint8_t *)q,
+                       (const uint8_t *)meta, lens, scores, d.Hq, d.Hkv, nq, d.T, d.NB, scale);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t quest_r(const Dims &d, const void *q, int nq, const void *meta, const int32_t *lens, float scale,
+                          float *scores, hipStream_t st) {
+    const int R = nq * d.G();
+    if (R <= 4)
+        return quest_t<E, D, 4>(d, q, nq, meta, lens, scale, scores, st);
+    if (R <= 8)
+        return quest_t<E, D, 8>(d, q, nq, meta, lens, scale, scores, st);
+    if (R <= 16)
+        return quest_t<E, D, 16>(d, q, nq, meta, lens, scale, scores, st);
+    return quest_t<E, D, 32>(d, q, nq, meta, lens, scale, scores, st);
+}
+
+hipError_t launch_score_quest(const Dims &d, const void *q, int nq, const void *meta, const int32_t *lens,
+                              float scale, float *scores, hipStream_t st) {
+    if (d.dtype == 1)
+        return d.D == 128 ? quest_r<BF16, 128>(d, q, nq, meta, lens, scale, scores, st)
+                          : quest_r<BF16, 64>(d, q, nq, meta, lens, scale, scores, st);
+    return d.D == 128 ? quest_r<F32, 128>(d, q, nq, meta, lens, scale, scores, st)
+                      : quest_r<F32, 64>(d, q, nq, meta, lens, scale, scores, st);
+}
+
+template <typename E, int D>
+static hipError_t meta_t(const Dims &d, const void *keys, const int32_t *lens, void *meta, hipStream_t st) {
+    dim3 grid((d.NB + 3) / 4, d.rows());
+    hipLaunchKernelGGL((quest_meta_kernel<E, D>), grid, dim3(256), 0, st, (const uint8_t *)keys, lens,
+                       (uint8_t *)meta, d.Hkv, d.T, d.NB);
+    return hipGetLastError();
+}
+
+hipError_t launch_quest_meta(const Dims &d, const void *keys, const int32_t *lens, void *meta, hipStream_t st) {
+    if (d.dtype == 1)
+        return d.D == 128 ? meta_t<BF16, 128>(d, keys, lens, meta, st) : meta_t<BF16, 64>(d, keys, lens, meta, st);
+    return d.D == 128 ? meta_t<F32, 128>(d, keys, lens, meta, st) : meta_t<F32, 64>(d, keys, lens, meta, st);
+}
+
+}  // namespace skv

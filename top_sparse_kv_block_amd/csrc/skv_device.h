@@ -1,0 +1,126 @@
+// Device-side helpers shared by the gfx950 kernels: element traits for
+// float32 / bf16 storage, 16-byte vector loads, and wave64 cross-lane
+// reductions built on DPP row operations (lanes are grouped in rows of 16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Element storage traits.  EPL = elements in one 16-byte lane load.
+struct F32 {
+    static constexpr int bytes = 4;
+    static constexpr int EPL = 4;
+};
+struct BF16 {
+    static constexpr int bytes = 2;
+    static constexpr int EPL = 8;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Streaming 16-byte load that should not displace reused lines.
+__device__ __forceinline__ u32x4 load_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+
+// Dot product of one 16-byte chunk of keys with the matching chunk of a
+// query row, accumulated into acc.  bf16 uses the packed dot2 instruction
+// (products of bf16 values are exact in fp32); float32 uses FMAs.
+template <typename E> __device__ __forceinline__ float dot_chunk(u32x4 k, u32x4 q, float acc);
+
+// The whole 16-byte vector is reinterpreted as 8 bf16 and split into pairs
+// with shuffles.  (Bit-casting the individual 32-bit elements instead makes
+// this compiler feed element 0 to all four dot2 instructions.)
+template <> __device__ __forceinline__ float dot_chunk<BF16>(u32x4 k, u32x4 q, float acc) {
+    const bf16x8 kb = __builtin_bit_cast(bf16x8, k), qb = __builtin_bit_cast(bf16x8, q);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 0, 1), __builtin_shufflevector(qb, qb, 0, 1),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 2, 3), __builtin_shufflevector(qb, qb, 2, 3),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 4, 5), __builtin_shufflevector(qb, qb, 4, 5),
+                                          acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kb, kb, 6, 7), __builtin_shufflevector(qb, qb, 6, 7),
+                                          acc, false);
+    return acc;
+}
+
+template <> __device__ __forceinline__ float dot_chunk<F32>(u32x4 k, u32x4 q, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        acc = __builtin_fmaf(__uint_as_float(k[i]), __uint_as_float(q[i]), acc);
+    return acc;
+}
+
+// DPP controls (gfx9 encoding)
+enum : int {
+    DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+    DPP_ROW_ROR1 = 0x121,
+    DPP_ROW_ROR2 = 0x122,
+    DPP_ROW_ROR4 = 0x124,
+    DPP_ROW_ROR8 = 0x128,
+    DPP_ROW_HALF_MIRROR = 0x141,
+};
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of L lanes (L = 8, 16 or 32); every lane of the
+// group receives the group's total.  The order of the additions is fixed,
+// so the result is deterministic.
+template <int L> __device__ __forceinline__ float group_sum(float v);
+
+template <> __device__ __forceinline__ float group_sum<16>(float v) {
+    v += dpp<DPP_ROW_ROR8>(v);
+    v += dpp<DPP_ROW_ROR4>(v);
+    v += dpp<DPP_ROW_ROR2>(v);
+    v += dpp<DPP_ROW_ROR1>(v);
+    return v;
+}
+
+template <> __device__ __forceinline__ float group_sum<8>(float v) {
+    v += dpp<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp<DPP_QUAD_XOR2>(v);
+    v += dpp<DPP_QUAD_XOR1>(v);
+    return v;
+}
+
+template <> __device__ __forceinline__ float group_sum<32>(float v) {
+    v = group_sum<16>(v);
+    return v + __shfl_xor(v, 16);
+}
+
+// max over the whole wave (all lanes receive it)
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<DPP_ROW_ROR8>(v));
+    v = fmaxf(v, dpp<DPP_ROW_ROR4>(v));
+    v = fmaxf(v, dpp<DPP_ROW_ROR2>(v));
+    v = fmaxf(v, dpp<DPP_ROW_ROR1>(v));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+
+// max across the lanes l, l^16, l^32, l^48 (the four rows of the wave)
+__device__ __forceinline__ float rows_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float rows_sum(float v) {
+    v += __shfl_xor(v, 16);
+    return v + __shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ int nb_of(int len) { return (len + 15) >> 4; }
+
+}  // namespace skv

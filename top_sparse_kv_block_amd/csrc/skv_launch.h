@@ -1,0 +1,49 @@
+// Internal launchers (host side) for the gfx950 kernels.  The C ABI in
+// abi.hip validates arguments and then calls these; each returns the
+// hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace skv {
+
+struct Dims {
+    int B, Hq, Hkv, D, T, NB, dtype;  // dtype: 0 = f32, 1 = bf16
+    int rows() const { return B * Hkv; }
+    int G() const { return Hq / Hkv; }
+    int elem_bytes() const { return dtype == 0 ? 4 : 2; }
+};
+
+hipError_t launch_score_blockmax(const Dims &d, const void *q, int n_queries, const void *keys,
+                                 const int32_t *seq_lens, float scale, float *scores, hipStream_t st);
+hipError_t launch_score_quest(const Dims &d, const void *q, int n_queries, const void *meta,
+                              const int32_t *seq_lens, float scale, float *scores, hipStream_t st);
+hipError_t launch_quest_meta(const Dims &d, const void *keys, const int32_t *seq_lens, void *meta,
+                             hipStream_t st);
+hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *seq_lens, int k, int sink,
+                       int recent, int32_t *sel_blocks, int32_t *sel_count, hipStream_t st);
+hipError_t launch_cache_update(const Dims &d, int k, int cap, const int32_t *sel_blocks,
+                               const int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
+                               uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                               int32_t *miss_slot, int32_t *miss_count, hipStream_t st);
+hipError_t launch_gather(const Dims &d, int k, int cap, const int32_t *miss_block, const int32_t *miss_slot,
+                         const int32_t *miss_count, const void *src_k, const void *src_v, void *pool_k,
+                         void *pool_v, hipStream_t st);
+hipError_t launch_attention(const Dims &d, const void *q, const void *pool_k, const void *pool_v, int cap,
+                            const int32_t *sel_blocks, const int32_t *sel_slot, const int32_t *sel_count,
+                            const int32_t *seq_lens, int k, float scale, int splits, float *out, float *lse,
+                            float *ws, hipStream_t st);
+
+// limits shared by validation and launch code
+constexpr int kMaxQueryRows = 32;  // G * n_queries for scoring
+constexpr int kMaxTopkBlocks = 65536;
+constexpr int kMaxK = 1024;
+constexpr int kMaxCapacity = 1024;
+constexpr int kMaxGroup = 16;  // G for attention
+
+int attention_auto_splits(int rows, int k);
+size_t attention_ws_bytes(int rows, int G, int D, int splits);
+
+}  // namespace skv

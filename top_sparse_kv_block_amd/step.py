@@ -1,0 +1,121 @@
+"""One sparse decode step for one attention layer, on top of the C ABI.
+
+:class:`LayerBuffers` owns the device buffers of one layer (torch allocates
+them; torch is only the allocator and the stream provider here) and
+:func:`decode_step` enqueues the four library calls on the current stream:
+score -> top-k -> cache update (+ miss fetch) -> sparse attention.  Nothing
+here computes; there is no host synchronisation inside a step.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class StepConfig:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    max_ctx: int
+    dtype: str  # "f32" | "bf16"
+    k_blocks: int
+    capacity: int
+    mode: int = B.SKV_SCORE_BLOCKMAX
+    n_queries: int = 1
+    sink: int = 0
+    recent: int = 0
+    num_splits: int = 0
+    scale: float | None = None
+
+    @property
+    def shape(self) -> B.skv_shape:
+        return B.make_shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.max_ctx, self.dtype)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def nb(self) -> int:
+        return self.max_ctx // 16
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+
+class LayerBuffers:
+    """Selection, working-set state, pool, outputs and workspace of one layer."""
+
+    def __init__(self, cfg: StepConfig, device="cuda", pool=True):
+        self.cfg = cfg
+        self.shape = cfg.shape
+        b, hkv, hq, d, k, c = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim, cfg.k_blocks, cfg.capacity
+        i32 = dict(dtype=torch.int32, device=device)
+        self.scores = torch.empty(b, hkv, cfg.nb, dtype=torch.float32, device=device)
+        self.sel_blocks = torch.empty(b, hkv, k, **i32)
+        self.sel_count = torch.empty(b, hkv, **i32)
+        self.slot_block = torch.full((b, hkv, c), -1, **i32)
+        self.slot_stamp = torch.zeros(b, hkv, c, **i32)
+        self.clock = torch.zeros(b, hkv, **i32)
+        self.sel_slot = torch.empty(b, hkv, k, **i32)
+        self.sel_hit = torch.empty(b, hkv, k, dtype=torch.uint8, device=device)
+        self.miss_block = torch.empty(b, hkv, k, **i32)
+        self.miss_slot = torch.empty(b, hkv, k, **i32)
+        self.miss_count = torch.empty(b, hkv, **i32)
+        if pool:
+            self.pool_k = torch.zeros(b, hkv, c, 16, d, dtype=cfg.torch_dtype, device=device)
+            self.pool_v = torch.zeros(b, hkv, c, 16, d, dtype=cfg.torch_dtype, device=device)
+        else:
+            self.pool_k = self.pool_v = None
+        self.out = torch.empty(b, hq, d, dtype=torch.float32, device=device)
+        self.lse = torch.empty(b, hq, dtype=torch.float32, device=device)
+        self.splits = cfg.num_splits or B.sparse_decode_attention_splits(self.shape, k)
+        ws = B.sparse_decode_attention_workspace_bytes(self.shape, k, self.splits)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+
+    def reset(self):
+        """Empty working set (slot table -1, stamps and clock 0)."""
+        self.slot_block.fill_(-1)
+        self.slot_stamp.zero_()
+        self.clock.zero_()
+
+    # stage wrappers -------------------------------------------------------
+    def score(self, score_q, keys_or_meta, seq_lens, stream=None):
+        c = self.cfg
+        B.sparse_kv_score(self.shape, c.mode, score_q, c.n_queries, keys_or_meta, seq_lens, c.softmax_scale,
+                          self.scores, stream)
+
+    def topk(self, seq_lens, stream=None):
+        c = self.cfg
+        B.sparse_kv_topk(self.shape, self.scores, seq_lens, c.k_blocks, c.sink, c.recent, self.sel_blocks,
+                         self.sel_count, stream)
+
+    def cache_update(self, src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None):
+        c = self.cfg
+        B.sparse_kv_cache_update(self.shape, c.k_blocks, c.capacity, self.sel_blocks, self.sel_count, self.slot_block,
+                                 self.slot_stamp, self.clock, self.sel_slot, self.sel_hit, self.miss_block,
+                                 self.miss_slot, self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
+                                 stream)
+
+    def attention(self, q, seq_lens, stream=None):
+        c = self.cfg
+        B.sparse_decode_attention(self.shape, q, self.pool_k, self.pool_v, c.capacity, self.sel_blocks, self.sel_slot,
+                                  self.sel_count, seq_lens, c.k_blocks, c.softmax_scale, self.splits, self.out,
+                                  self.lse, self.workspace, stream)
+
+
+def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE,
+                stream=None):
+    """Enqueue one full step: score, top-k, cache update + fetch, attention."""
+    buf.score(score_q, keys_or_meta, seq_lens, stream)
+    buf.topk(seq_lens, stream)
+    buf.cache_update(src_k, src_v, src_kind, stream)
+    buf.attention(q, seq_lens, stream)
