@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse KV-cache decode step on one MI355X.
+
+A step is one pass of the whole path for one attention layer over one batch:
+block scoring -> top-k under the budget -> working-set update + miss fetch ->
+split-K GQA attention (four library calls, six kernels).  The default
+workload is the Llama-3.1-8B-shaped layer: batch 8, 32 q-heads / 8 kv-heads,
+head_dim 128, bf16 K/V, 32768-token context in 16-token blocks, a
+2048-token budget (128 blocks) and a 128-slot working set per (sequence,
+kv-head).  Inputs are seeded synthetic tensors of that shape, resident in
+HBM before timing starts; queries follow an AR(1) chain so consecutive
+steps overlap (>80%) the way the method expects.
+
+Output: one JSON line with steps/s (value), ms per step, achieved
+algorithmic HBM GB/s for the whole step, the roofline of the dominant
+kernel (the block-scoring scan) timed live with HIP events on its stream,
+and the oracle's throughput on the host cores on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "sparse decode steps/s + achieved HBM GB/s (32K ctx, 2048-token budget)"
+SCORE_SOURCES = ("top_sparse_kv_block_amd/csrc/score.hip", "top_sparse_kv_block_amd/csrc/skv_device.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_blockmax_llama8b_32k_traffic.json")
+
+
+# ---------------------------------------------------------------- byte model
+def kv_cache_bytes(seq_len, layers, kv_heads, head_dim, bytes_per_elem):
+    """KV-cache size: 2 (K and V) * L * layers * kv_heads * head_dim * bytes."""
+    return 2 * seq_len * layers * kv_heads * head_dim * bytes_per_elem
+
+
+def step_bytes(w, misses: float) -> dict:
+    """Algorithmic HBM bytes of one step (what the method must move).
+
+    score scan: every key of every row once (P*T*D*e); Quest reads the
+    per-block min/max instead (P*NB*2*D*e); scoring queries; scores written.
+    top-k: scores read, selection written.  working set: each miss reads
+    its K and V block from the source and writes it into the pool.
+    attention: the selected blocks' K and V read once per kv group, q read,
+    output and lse written.  Small state arrays (slot tables, lists) are
+    left out (<0.1%).
+    """
+    P, e, D, T = w.rows, w.elem_bytes, w.head_dim, w.ctx
+    nb, k = w.nb_max, w.k_blocks
+    blk = 16 * D * e
+    scan = P * nb * 2 * D * e if w.scoring == "quest" else P * T * D * e
+    score_q = w.batch * w.n_score_queries * w.n_q_heads * D * e
+    scores = P * nb * 4
+    topk = P * nb * 4 + P * k * 4
+    fetch = misses * blk * 2 * 2
+    attn = P * k * blk * 2 + w.batch * w.n_q_heads * D * e + w.batch * w.n_q_heads * (D + 1) * 4
+    return dict(score=scan + score_q + scores, topk=topk, fetch=fetch, attention=attn,
+                total=scan + score_q + scores + topk + fetch + attn)
+
+
+def score_launch_bytes(w) -> int:
+    """Bytes one scoring launch must move: per block 16*D*e of keys plus its
+    4-byte score, times P*NB blocks, plus the scoring queries."""
+    return w.rows * w.nb_max * (16 * w.head_dim * w.elem_bytes + 4) + \
+        w.batch * w.n_score_queries * w.n_q_heads * w.head_dim * w.elem_bytes
+
+
+def _sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in SCORE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(w):
+    """Counter-derived HBM bytes per scoring launch, if the counters were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != _sources_sha() or t.get("workload") != w.name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- oracle leg
+def cpu_baseline(w, data, seconds: float):
+    """The oracle, as it stands, on the host cores: whole steps (fp64 scores
+    for every row, top-k, linked-list LRU, block copies, attention) until
+    `seconds` of wall time have passed."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0)))
+    q, sq, K, V, lens = data["q"], data["score_q"], data["K"], data["V"], data["seq_lens"]
+    scale = 1.0 / math.sqrt(w.head_dim)
+    lru = oracle.LRU(w.rows, w.capacity)
+    npdt = np.float32 if w.dtype == "f32" else np.uint16
+    pool_k = np.zeros((w.batch, w.n_kv_heads, w.capacity, 16, w.head_dim), dtype=npdt)
+    pool_v = np.zeros_like(pool_k)
+    t0 = time.perf_counter()
+    steps, misses = 0, 0
+    while True:
+        t = steps % q.shape[0]
+        if w.scoring == "quest":
+            raise NotImplementedError("cpu baseline runs the exact-score workloads")
+        s = oracle.score_blockmax(sq[t], K, lens, scale)
+        sel, cnt = oracle.topk(s, lens, w.k_blocks, w.ctx, sink=w.sink, recent=w.recent)
+        out = lru.step(sel.reshape(w.rows, -1), cnt.reshape(-1), w.nb_max)
+        oracle.gather(out["miss_block"], out["miss_slot"], out["miss_count"], K, V, pool_k, pool_v)
+        oracle.attention(q[t], K, V, sel, cnt, lens, scale)
+        misses += int(out["miss_count"].sum())
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=round(steps / el, 4), unit="steps/s", cores=threads, kind="oracle",
+                sample=f"{steps} whole steps (all {w.rows} rows, fp64) of the {w.name} workload, "
+                       f"{el:.1f} s wall on {threads} OpenMP threads",
+                gbps=round(step_bytes(w, misses / steps)["total"] * steps / el / 1e9, 3))
+
+
+# ---------------------------------------------------------------- GPU leg
+def run(args):
+    import torch
+
+    from top_sparse_kv_block_amd import binding as B
+    from top_sparse_kv_block_amd import synth
+    from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
+
+    w = synth.WORKLOADS[args.workload]
+    if w.scoring == "given":
+        raise SystemExit("the host-tier workload has no scoring stage; use bench_host_tier")
+    nsteps = args.warmup + args.steps
+    wq = w.scaled(steps=max(nsteps, 1))
+    t_gen = time.time()
+    data = synth.gen_workload(wq)
+    print(f"[bench] generated {w.name} inputs in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    dev = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+                     if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a))).cuda()
+    q_all, sq_all = dev(data["q"]), dev(data["score_q"])
+    dK, dV, dlens = dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
+    mode = B.SKV_SCORE_QUEST if w.scoring == "quest" else B.SKV_SCORE_BLOCKMAX
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
+                     mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent, num_splits=args.splits)
+    buf = LayerBuffers(cfg)
+    keys_or_meta = dK
+    if mode == B.SKV_SCORE_QUEST:
+        keys_or_meta = torch.empty(w.batch, w.n_kv_heads, w.nb_max, 2, w.head_dim, dtype=cfg.torch_dtype,
+                                   device="cuda")
+        B.sparse_kv_quest_meta(cfg.shape, dK, dlens, keys_or_meta)
+    miss_log = torch.zeros(nsteps, w.batch, w.n_kv_heads, dtype=torch.int32, device="cuda")
+    shape, st = cfg.shape, None
+    scale = cfg.softmax_scale
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record()
+        B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
+        if ev is not None:
+            ev[1].record()
+        B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
+                         buf.sel_count, st)
+        B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count, buf.slot_block,
+                                 buf.slot_stamp, buf.clock, buf.sel_slot, buf.sel_hit, buf.miss_block, buf.miss_slot,
+                                 miss_log[t], dK, dV, B.SKV_SRC_DEVICE, buf.pool_k, buf.pool_v, st)
+        B.sparse_decode_attention(shape, q_all[t], buf.pool_k, buf.pool_v, cfg.capacity, buf.sel_blocks,
+                                  buf.sel_slot, buf.sel_count, dlens, cfg.k_blocks, scale, buf.splits, buf.out,
+                                  buf.lse, buf.workspace, st)
+
+    # cold start, warm-up (not timed)
+    buf.reset()
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    score_ms = [a.elapsed_time(b) for a, b in evs]
+    elapsed = max(wall, gpu_ms / 1e3)
+
+    misses = miss_log[args.warmup:].sum().item()
+    bytes_total = step_bytes(w, misses / args.steps)["total"] * args.steps
+    score_avg_s = float(np.mean(score_ms)) / 1e3
+    sbytes = score_launch_bytes(w)
+    achieved = sbytes / score_avg_s / 1e9
+    traffic = _traffic(w)
+    steps_per_s = args.steps / elapsed
+    res = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "ctx": w.ctx, "block": 16, "budget_tokens": w.budget,
+                   "k_blocks": w.k_blocks, "capacity_slots": w.capacity, "scoring": w.scoring,
+                   "n_score_queries": w.n_score_queries, "attn_splits": buf.splits, "parallelism": "single-gpu"},
+        "hbm_gbps": round(bytes_total / elapsed / 1e9, 1),
+        "hbm_frac": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": int(bytes_total / args.steps),
+        "miss_blocks_per_step": round(misses / args.steps, 1),
+        "roofline": {"bound": "hbm", "kernel": "score_blockmax_kernel" if mode == B.SKV_SCORE_BLOCKMAX
+                     else "score_quest_kernel",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(score_avg_s * 1e6, 2),
+                     "bytes_per_launch": sbytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds)
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the step runs on a single MI355X and has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        return 2
+    res = run(args)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
