@@ -2,8 +2,9 @@
 """Benchmark of the sparse KV-cache decode step on one MI355X.
 
 A step is one pass of the whole path for one attention layer over one batch:
-block scoring -> top-k under the budget -> working-set update + miss fetch ->
-split-K GQA attention (four library calls, six kernels).  The default
+block scoring -> top-k under the budget -> working-set update -> split-K GQA
+attention that also fetches the step's misses into the pool (four library
+calls, four kernels).  The default
 workload is the Llama-3.1-8B-shaped layer: batch 8, 32 q-heads / 8 kv-heads,
 head_dim 128, bf16 K/V, 32768-token context in 16-token blocks, a
 2048-token budget (128 blocks) and a 128-slot working set per (sequence,
@@ -50,11 +51,11 @@ def step_bytes(w, misses: float) -> dict:
 
     score scan: every key of every row once (P*T*D*e); Quest reads the
     per-block min/max instead (P*NB*2*D*e); scoring queries; scores written.
-    top-k: scores read, selection written.  working set: each miss reads
-    its K and V block from the source and writes it into the pool.
-    attention: the selected blocks' K and V read once per kv group, q read,
-    output and lse written.  Small state arrays (slot tables, lists) are
-    left out (<0.1%).
+    top-k: scores read, selection written.  attention: every selected
+    block's K and V read once per kv group (from the pool for hits, from the
+    source for misses), q read, output and lse written.  fetch: each miss's
+    K and V block written into its pool slot.  Small state arrays (slot
+    tables, lists) are left out (<0.1%).
     """
     P, e, D, T = w.rows, w.elem_bytes, w.head_dim, w.ctx
     nb, k = w.nb_max, w.k_blocks
@@ -63,7 +64,7 @@ def step_bytes(w, misses: float) -> dict:
     score_q = w.batch * w.n_score_queries * w.n_q_heads * D * e
     scores = P * nb * 4
     topk = P * nb * 4 + P * k * 4
-    fetch = misses * blk * 2 * 2
+    fetch = misses * blk * 2
     attn = P * k * blk * 2 + w.batch * w.n_q_heads * D * e + w.batch * w.n_q_heads * (D + 1) * 4
     return dict(score=scan + score_q + scores, topk=topk, fetch=fetch, attention=attn,
                 total=scan + score_q + scores + topk + fetch + attn)
@@ -176,12 +177,13 @@ def run(args):
             ev[1].record()
         B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
                          buf.sel_count, st)
+        # list-only cache update; the attention kernel fetches the misses
         B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count, buf.slot_block,
                                  buf.slot_stamp, buf.clock, buf.sel_slot, buf.sel_hit, buf.miss_block, buf.miss_slot,
-                                 miss_log[t], dK, dV, B.SKV_SRC_DEVICE, buf.pool_k, buf.pool_v, st)
+                                 miss_log[t], None, None, B.SKV_SRC_DEVICE, buf.pool_k, buf.pool_v, st)
         B.sparse_decode_attention(shape, q_all[t], buf.pool_k, buf.pool_v, cfg.capacity, buf.sel_blocks,
-                                  buf.sel_slot, buf.sel_count, dlens, cfg.k_blocks, scale, buf.splits, buf.out,
-                                  buf.lse, buf.workspace, st)
+                                  buf.sel_slot, buf.sel_hit, buf.sel_count, dlens, cfg.k_blocks, scale, buf.splits,
+                                  dK, dV, B.SKV_SRC_DEVICE, buf.out, buf.lse, buf.workspace, st)
 
     # cold start, warm-up (not timed)
     buf.reset()

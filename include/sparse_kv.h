@@ -206,21 +206,32 @@ skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int3
  * are merged with the usual log-sum-exp rescaling.  A row with no valid
  * token gives out = 0 and lse = -inf.
  *
+ * Fetch on attend: when src_k/src_v are given (device or host-mapped, as
+ * in sparse_kv_cache_update), every selected block with sel_hit == 0 is
+ * read from the source by its block id instead of from the pool, and is
+ * also written into its pool slot.  Use it with a list-only cache update
+ * (NULL sources there) to move each miss once; with NULL sources here the
+ * pool must already hold every selected block.
+ *
  * q           [B, Hq, D] dtype
- * pool_k/v    [B, Hkv, capacity, 16, D] dtype
- * sel_blocks, sel_slot [B, Hkv, k_blocks] int32; sel_count [B, Hkv] int32
- * seq_lens    [B] int32
+ * pool_k/v    [B, Hkv, capacity, 16, D] dtype (written only for fetched misses)
+ * sel_blocks, sel_slot [B, Hkv, k_blocks] int32; sel_hit [B, Hkv, k_blocks]
+ *             uint8 (only read with sources, may be NULL otherwise);
+ *             sel_count [B, Hkv] int32; seq_lens [B] int32
  * out         [B, Hq, D] float32; lse [B, Hq] float32 or NULL
- * num_splits  0 = choose (sparse_decode_attention_splits), else 1..k_blocks
+ * num_splits  0 = choose (sparse_decode_attention_splits), else
+ *             1..min(k_blocks, 128)
  * workspace   >= sparse_decode_attention_workspace_bytes(shape, k_blocks,
- *             num_splits) bytes of device memory, 256-byte aligned
+ *             num_splits) bytes of device memory, 256-byte aligned (the
+ *             per-split partials); calls that share a workspace must not
+ *             overlap in time (enqueue them on one stream).
  * Entries with a slot outside [0, capacity) or a negative block are skipped.
  */
-skv_status sparse_decode_attention(const skv_shape *shape, const void *q, const void *pool_k,
-                                   const void *pool_v, int32_t capacity, const int32_t *sel_blocks,
-                                   const int32_t *sel_slot, const int32_t *sel_count,
-                                   const int32_t *seq_lens, int32_t k_blocks, float scale,
-                                   int32_t num_splits, float *out, float *lse, void *workspace,
+skv_status sparse_decode_attention(const skv_shape *shape, const void *q, void *pool_k, void *pool_v,
+                                   int32_t capacity, const int32_t *sel_blocks, const int32_t *sel_slot,
+                                   const uint8_t *sel_hit, const int32_t *sel_count, const int32_t *seq_lens,
+                                   int32_t k_blocks, float scale, int32_t num_splits, const void *src_k,
+                                   const void *src_v, int32_t src_kind, float *out, float *lse, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
 /* Number of splits num_splits = 0 resolves to. */

@@ -49,4 +49,5 @@ def test_host_side_validation_needs_no_gpu():
     ok = binding.make_shape(8, 32, 8, 128, 32768, "bf16")
     splits = binding.sparse_decode_attention_splits(ok, 128)
     assert splits == 16
+    # the per-split partials: rows x splits x G x (D + 2) floats
     assert binding.sparse_decode_attention_workspace_bytes(ok, 128, 0) == 64 * 16 * 4 * 130 * 4

@@ -26,8 +26,9 @@ def test_score_scan_is_the_k_half_of_one_layers_cache():
     assert by["score"] == k_half + scan_extra
     # the selected K and V: 128 blocks of 16 tokens per row
     assert by["attention"] >= w.rows * w.k_blocks * 16 * w.head_dim * 2 * 2
-    # one miss moves its K and V block twice (read source, write pool)
-    assert bench.step_bytes(w, 10)["fetch"] == 10 * 4 * 16 * w.head_dim * 2
+    # a miss's K and V are read once (counted with attention's reads) and
+    # written once into the pool
+    assert bench.step_bytes(w, 10)["fetch"] == 10 * 2 * 16 * w.head_dim * 2
 
 
 def test_multi_gpu_request_exits_with_message(capsys):

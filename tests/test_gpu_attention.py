@@ -22,7 +22,7 @@ from gpu_util import dev, host, log, max_rel_row_err, to_dtype
 pytestmark = pytest.mark.gpu
 
 
-def _case(Bsz, Hq, Hkv, D, T, cap, k, dtype, lens, splits, seed, fill=1.0):
+def _case(Bsz, Hq, Hkv, D, T, cap, k, dtype, lens, splits, seed, fill=1.0, fetch=False, steps=1):
     r = np.random.default_rng(seed)
     rows = Bsz * Hkv
     nb = T // 16
@@ -43,11 +43,26 @@ def _case(Bsz, Hq, Hkv, D, T, cap, k, dtype, lens, splits, seed, fill=1.0):
     buf.sel_blocks.copy_(dev(sel).view(Bsz, Hkv, k))
     buf.sel_count.copy_(dev(cnt).view(Bsz, Hkv))
     seq = dev(lens)
-    log("attention", dtype, (Bsz, Hq, Hkv, D, T, cap, k), "splits", buf.splits, "seed", seed)
-    buf.cache_update(dev(sk), dev(sv))
-    buf.attention(dev(q), seq)
+    log("attention", dtype, (Bsz, Hq, Hkv, D, T, cap, k), "splits", buf.splits, "seed", seed, "fetch", fetch)
+    dk, dv = dev(sk), dev(sv)
+    for _ in range(steps):
+        if fetch:  # list-only update, misses fetched by the attention kernel
+            buf.cache_update(None, None)
+            buf.attention(dev(q), seq, dk, dv)
+        else:
+            buf.cache_update(dk, dv)
+            buf.attention(dev(q), seq)
     torch.cuda.synchronize()
     scale = 1.0 / math.sqrt(D)
+    # every resident slot holds the bytes of its source block
+    sb = host(buf.slot_block).reshape(rows, cap)
+    pk, pv = host(buf.pool_k).reshape(rows, cap, 16, D), host(buf.pool_v).reshape(rows, cap, 16, D)
+    for r_ in range(rows):
+        for s_, blk in enumerate(sb[r_]):
+            if blk >= 0:
+                b_, j_ = divmod(r_, Hkv)
+                assert np.array_equal(pk[r_, s_], sk[b_, j_, 16 * blk:16 * blk + 16])
+                assert np.array_equal(pv[r_, s_], sv[b_, j_, 16 * blk:16 * blk + 16])
     out_ref, lse_ref = oracle.attention(q, sk, sv, sel.reshape(Bsz, Hkv, k), cnt.reshape(Bsz, Hkv), lens, scale)
     got, lse = host(buf.out), host(buf.lse)
     if dtype == "f32":
@@ -66,9 +81,17 @@ def _case(Bsz, Hq, Hkv, D, T, cap, k, dtype, lens, splits, seed, fill=1.0):
     return buf
 
 
+@pytest.mark.parametrize("fetch", [False, True])
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
-def test_attention_dtypes(dtype, D):
-    _case(2, 8, 2, D, 1024, 16, 8, dtype, [1024, 700], 0, seed=1)
+def test_attention_dtypes(dtype, D, fetch):
+    _case(2, 8, 2, D, 1024, 16, 8, dtype, [1024, 700], 0, seed=1, fetch=fetch)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_fetch_on_attend_repeated_calls(splits):
+    # the same selection three times: later calls find every block resident
+    # (no fetch) and must give the same output
+    _case(2, 32, 8, 128, 4096, 40, 32, "bf16", [4096, 2900], splits, seed=7, fetch=True, steps=3)
 
 
 @pytest.mark.parametrize("splits", [1, 2, 5, 32])
@@ -87,8 +110,9 @@ def test_attention_ragged_partial_and_empty_rows():
     _case(5, 8, 2, 128, 2048, 40, 40, "bf16", [0, 1, 17, 1000, 2048], 0, seed=4, fill=0.9)
 
 
-def test_attention_llama8b_row_shape():
-    _case(2, 32, 8, 128, 32768, 128, 128, "bf16", [32768, 32768], 0, seed=5)
+@pytest.mark.parametrize("fetch", [False, True])
+def test_attention_llama8b_row_shape(fetch):
+    _case(2, 32, 8, 128, 32768, 128, 128, "bf16", [32768, 32768], 0, seed=5, fetch=fetch)
 
 
 def test_full_budget_equals_dense_attention():

@@ -43,7 +43,7 @@ def _forced_sets(w, lens):
     return out
 
 
-def run_workload(w, steps=None, rows=None, heads=None, check_scores=True):
+def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_on_attend=True):
     """Run `steps` steps of workload `w`; check rows `rows` (None = all) of
     the scores and (b, h) pairs `heads` (None = all) of the attention."""
     steps = steps or w.steps
@@ -69,7 +69,7 @@ def run_workload(w, steps=None, rows=None, heads=None, check_scores=True):
     total_miss = 0
     for t in range(steps):
         log(w.name, "step", t, (w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx))
-        decode_step(buf, dev(q[t]), dev(sq[t]), keys_or_meta, dlens, dK, dV)
+        decode_step(buf, dev(q[t]), dev(sq[t]), keys_or_meta, dlens, dK, dV, fetch_on_attend=fetch_on_attend)
         torch.cuda.synchronize()
         g_scores = host(buf.scores).astype(np.float64)
         g_sel, g_cnt = host(buf.sel_blocks), host(buf.sel_count)
@@ -148,9 +148,10 @@ def test_tiny_workload_capacity_equals_budget_transfer_invariant():
     run_workload(w)
 
 
-def test_llama8b_reduced_context():
+@pytest.mark.parametrize("fetch_on_attend", [True, False])
+def test_llama8b_reduced_context(fetch_on_attend):
     w = synth.WORKLOADS["llama8b_32k"].scaled(batch=2, ctx=4096, budget=512)
-    run_workload(w, steps=6)
+    run_workload(w, steps=6, fetch_on_attend=fetch_on_attend)
 
 
 def test_llama8b_ragged_lengths():

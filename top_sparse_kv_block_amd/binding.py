@@ -64,7 +64,8 @@ def load():
     L.sparse_kv_topk.argtypes = [S, _p, _p, _i32, _i32, _i32, _p, _p, _p]
     L.sparse_kv_cache_update.argtypes = [S, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
                                          _p]
-    L.sparse_decode_attention.argtypes = [S, _p, _p, _p, _i32, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _p, _sz, _p]
+    L.sparse_decode_attention.argtypes = [S, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _i32, _p, _p,
+                                          _p, _sz, _p]
     L.sparse_decode_attention_splits.argtypes = [S, _i32]
     L.sparse_decode_attention_splits.restype = _i32
     L.sparse_decode_attention_workspace_bytes.argtypes = [S, _i32, _i32]
@@ -180,20 +181,29 @@ def sparse_kv_cache_update(shape, k_blocks, capacity, sel_blocks, sel_count, slo
     _check("sparse_kv_cache_update", rc)
 
 
-def sparse_decode_attention(shape, q, pool_k, pool_v, capacity, sel_blocks, sel_slot, sel_count, seq_lens, k_blocks,
-                            scale, num_splits, out, lse, workspace, stream=None):
+def sparse_decode_attention(shape, q, pool_k, pool_v, capacity, sel_blocks, sel_slot, sel_hit, sel_count, seq_lens,
+                            k_blocks, scale, num_splits, src_k, src_v, src_kind, out, lse, workspace, stream=None):
+    """``src_k``/``src_v`` (device tensors, integer addresses of mapped host
+    memory, or None) turn on fetch-on-attend for the blocks with sel_hit == 0."""
     dt = _torch_dtype(shape.dtype)
-    b, hq, d = shape.batch, shape.n_q_heads, shape.head_dim
+    b, hq, d, t = shape.batch, shape.n_q_heads, shape.head_dim, shape.max_ctx
     P = b * shape.n_kv_heads
     pk, pc = P * k_blocks, P * capacity
+
+    def src(x, name):
+        if x is None or isinstance(x, int):
+            return x
+        return _ptr(x, dt, name, numel=P * t * d)
+
     rc = load().sparse_decode_attention(
         C.byref(shape), _ptr(q, dt, "q", numel=b * hq * d), _ptr(pool_k, dt, "pool_k", numel=pc * 16 * d),
         _ptr(pool_v, dt, "pool_v", numel=pc * 16 * d), int(capacity),
         _ptr(sel_blocks, torch.int32, "sel_blocks", numel=pk), _ptr(sel_slot, torch.int32, "sel_slot", numel=pk),
+        _ptr(sel_hit, torch.uint8, "sel_hit", allow_none=True, numel=pk),
         _ptr(sel_count, torch.int32, "sel_count", numel=P), _ptr(seq_lens, torch.int32, "seq_lens", numel=b),
-        int(k_blocks), float(scale), int(num_splits), _ptr(out, torch.float32, "out", numel=b * hq * d),
-        _ptr(lse, torch.float32, "lse", allow_none=True, numel=b * hq), _ptr(workspace, None, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+        int(k_blocks), float(scale), int(num_splits), src(src_k, "src_k"), src(src_v, "src_v"), int(src_kind),
+        _ptr(out, torch.float32, "out", numel=b * hq * d), _ptr(lse, torch.float32, "lse", allow_none=True, numel=b * hq),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("sparse_decode_attention", rc)
 
 

@@ -124,35 +124,43 @@ SKV_API int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k
 
 SKV_API size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits) {
     Dims d;
-    if (check_shape(shape, d) != SKV_OK || k_blocks < 1 || num_splits < 0 || num_splits > k_blocks)
+    if (check_shape(shape, d) != SKV_OK || k_blocks < 1 || num_splits < 0 || num_splits > k_blocks ||
+        num_splits > skv::kMaxSplits)
         return 0;
     const int splits = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
     return skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
 }
 
-SKV_API skv_status sparse_decode_attention(const skv_shape *shape, const void *q, const void *pool_k,
-                                           const void *pool_v, int32_t capacity, const int32_t *sel_blocks,
-                                           const int32_t *sel_slot, const int32_t *sel_count,
-                                           const int32_t *seq_lens, int32_t k_blocks, float scale,
-                                           int32_t num_splits, float *out, float *lse, void *workspace,
-                                           size_t workspace_bytes, void *stream) {
+SKV_API skv_status sparse_decode_attention(const skv_shape *shape, const void *q, void *pool_k, void *pool_v,
+                                           int32_t capacity, const int32_t *sel_blocks, const int32_t *sel_slot,
+                                           const uint8_t *sel_hit, const int32_t *sel_count, const int32_t *seq_lens,
+                                           int32_t k_blocks, float scale, int32_t num_splits, const void *src_k,
+                                           const void *src_v, int32_t src_kind, float *out, float *lse,
+                                           void *workspace, size_t workspace_bytes, void *stream) {
     Dims d;
     skv_status st = check_shape(shape, d);
     if (st != SKV_OK)
         return st;
     if (!q || !pool_k || !pool_v || !sel_blocks || !sel_slot || !sel_count || !seq_lens || !out)
         return SKV_ERR_NULL;
-    if (k_blocks < 1 || k_blocks > skv::kMaxK || capacity < 1 || num_splits < 0 || num_splits > k_blocks)
+    if (k_blocks < 1 || k_blocks > skv::kMaxK || capacity < 1 || num_splits < 0 || num_splits > k_blocks ||
+        num_splits > skv::kMaxSplits)
         return SKV_ERR_SHAPE;
+    if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
+        return SKV_ERR_SHAPE;
+    const bool fetch = src_k || src_v;
+    if (fetch && (!src_k || !src_v || !sel_hit))
+        return SKV_ERR_NULL;
     if (d.G() > skv::kMaxGroup)
         return SKV_ERR_UNSUPPORTED;
     const int splits = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
     const size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return SKV_ERR_WORKSPACE;
-    return hip_status(skv::launch_attention(d, q, pool_k, pool_v, capacity, sel_blocks, sel_slot, sel_count, seq_lens,
-                                            k_blocks, scale, splits, out, lse, (float *)workspace,
-                                            (hipStream_t)stream));
+    skv::AttnArgs a{q,         pool_k, pool_v,       capacity, sel_blocks, sel_slot, sel_hit, sel_count,
+                    seq_lens,  k_blocks, scale,      splits,   src_k,      src_v,    out,     lse,
+                    workspace};
+    return hip_status(skv::launch_attention(d, a, (hipStream_t)stream));
 }
 
 SKV_API skv_status sparse_kv_quest_meta(const skv_shape *shape, const void *keys, const int32_t *seq_lens, void *meta,

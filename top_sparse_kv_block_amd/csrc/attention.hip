@@ -6,19 +6,28 @@
 // indirection: KV-Cache 压缩技术的工程原理 §5.2), so the result does not
 // depend on which tier the blocks came from (HiSparse promo, insight 1).
 //
-// attn_splitk_kernel: grid (splits, rows), 256 threads.  The workgroup of
-// split s walks its contiguous share of the row's selection; its 4 waves
-// take interleaved blocks.  A wave loads a block's K and V (16 tokens) with
-// the same coalesced 16-byte lane layout as the scoring kernel and uses
-// them for all G query heads of the kv group at once (each K/V byte is
-// read once per group).  Logits are kept in base-2 units
-// (scale*log2(e)*q.k), the running max is per head and wave-uniform, and
-// each lane accumulates its own tokens' share of l and of the output, so
-// the only per-block cross-lane traffic is the dot-product sums and one max
-// per head.  The waves are merged through LDS and the workgroup writes
-// (max, sum, unnormalised output) for each head to the workspace.
-// attn_merge_kernel: one workgroup per (b, h) rescales the splits'
-// partials by exp2(m_s - m*) and normalises.
+// attn_kernel: grid (splits, rows), 8 waves.  The workgroup of split s owns
+// a contiguous share of the row's selection and each wave takes one block
+// of it at a time, so a workgroup has all of its blocks' K and V loads in
+// flight at once.  A wave loads the block's K and V (16 tokens) with the
+// coalesced 16-byte lane layout of the scoring kernel and uses them for all
+// G query heads of the kv group (each byte is read once per group).
+// Logits are kept in base-2 units (scale*log2(e)*q.k); the running max is
+// per head and wave-uniform; each lane accumulates its own tokens' share of
+// l and of the output, so per block the only cross-lane work is the
+// dot-product sums and one max per head.  Waves are combined in LDS; with
+// one split the workgroup writes the output directly, otherwise it writes
+// (max, sum, unnormalised output) per head to the workspace.
+// attn_merge_kernel: one workgroup per (b, h) loads every split's (max, sum)
+// in one round of independent loads, forms the weights exp2(m_s - m*) in
+// LDS, and each thread sums its output element over the splits.  (A merge
+// by the last workgroup of each row would need a device-scope release per
+// workgroup, which on this chip writes back the whole L2 each time.)
+//
+// Fetch on attend (optional): when a source cache is given, a selected
+// block that was not resident (sel_hit == 0) is read from the source by
+// block id and also written into its pool slot, so the miss costs one read
+// and one write and no separate copy pass.
 #include "skv_device.h"
 #include "skv_launch.h"
 
@@ -47,24 +56,30 @@ template <typename E> __device__ __forceinline__ float elem(u32x4 v, int e) {
         return __uint_as_float(v[e]);
 }
 
-constexpr int kAttnWaves = 4;
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr float kLn2 = 0.69314718055994531f;
 
 template <typename E, int D, int GMAX>
-__global__ __launch_bounds__(256) void attn_splitk_kernel(
-    const uint8_t *__restrict__ q, const uint8_t *__restrict__ pool_k, const uint8_t *__restrict__ pool_v, int C,
-    const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_slot,
-    const int32_t *__restrict__ sel_count, const int32_t *__restrict__ seq_lens, int Hq, int Hkv, int k,
-    int splits, int per_split, float scale_log2, float *__restrict__ ws) {
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
+    const uint8_t *__restrict__ q, uint8_t *__restrict__ pool_k, uint8_t *__restrict__ pool_v, int C,
+    const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_slot, const uint8_t *__restrict__ sel_hit,
+    const int32_t *__restrict__ sel_count, const int32_t *__restrict__ seq_lens, int Hq, int Hkv, int T, int k,
+    int splits, int per_split, float scale_log2, const uint8_t *__restrict__ src_k, const uint8_t *__restrict__ src_v,
+    float *__restrict__ part, float *__restrict__ out, float *__restrict__ lse) {
     constexpr int LPT = D * E::bytes / 16;
     constexpr int TPL = 64 / LPT;
     constexpr int LPB = 16 / TPL;
     constexpr int EPL = E::EPL;
+    constexpr size_t kBlockBytes = (size_t)16 * D * E::bytes;
     __shared__ float sm[kAttnWaves][GMAX][D + 2];
+    __shared__ float shM[GMAX], shL[GMAX];
 
     const int row = blockIdx.y, split = blockIdx.x;
     const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int NB = T / 16;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane % LPT, tg = lane / LPT;
 
     u32x4 qf[GMAX];
@@ -79,7 +94,6 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(
     const int i1 = min(i0 + per_split, n);
     const int32_t *sblk = sel_blocks + (size_t)row * k;
     const int32_t *sslot = sel_slot + (size_t)row * k;
-    const size_t block_bytes = (size_t)16 * D * E::bytes;
 
     float m[GMAX], l[GMAX], acc[GMAX][EPL];
 #pragma unroll
@@ -95,17 +109,32 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(
         const int blk = sblk[i], s = sslot[i];
         if (blk < 0 || s < 0 || s >= C)
             continue;
+        const bool fetch = src_k != nullptr && blk < NB && sel_hit[(size_t)row * k + i] == 0;
         const int nv = min(max(len - blk * 16, 0), 16);
-        if (nv == 0)
+        if (nv == 0 && !fetch)
             continue;
-        const size_t base = ((size_t)row * C + s) * block_bytes;
+        uint8_t *pk = pool_k + ((size_t)row * C + s) * kBlockBytes;
+        uint8_t *pv = pool_v + ((size_t)row * C + s) * kBlockBytes;
+        const uint8_t *rk = fetch ? src_k + ((size_t)row * T + (size_t)blk * 16) * D * E::bytes : pk;
+        const uint8_t *rv = fetch ? src_v + ((size_t)row * T + (size_t)blk * 16) * D * E::bytes : pv;
+        const size_t lo = ((size_t)tg * D + sub * EPL) * E::bytes;
+        constexpr size_t step = (size_t)TPL * D * E::bytes;
         u32x4 kv[LPB], vv[LPB];
 #pragma unroll
         for (int li = 0; li < LPB; ++li)
-            kv[li] = load16(pool_k + base + ((size_t)(li * TPL + tg) * D + sub * EPL) * E::bytes);
+            kv[li] = fetch ? load_nt(rk + lo + li * step) : load16(rk + lo + li * step);
 #pragma unroll
         for (int li = 0; li < LPB; ++li)
-            vv[li] = load16(pool_v + base + ((size_t)(li * TPL + tg) * D + sub * EPL) * E::bytes);
+            vv[li] = fetch ? load_nt(rv + lo + li * step) : load16(rv + lo + li * step);
+        if (fetch) {
+#pragma unroll
+            for (int li = 0; li < LPB; ++li) {
+                store16(pk + lo + li * step, kv[li]);
+                store16(pv + lo + li * step, vv[li]);
+            }
+        }
+        if (nv == 0)
+            continue;
 
         float z[LPB][GMAX];
 #pragma unroll
@@ -149,7 +178,7 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(
         }
     }
 
-    // combine the token groups of the wave, then the waves through LDS
+    // combine the token groups of each wave, then the waves through LDS
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
         if (g >= G)
@@ -169,110 +198,139 @@ __global__ __launch_bounds__(256) void attn_splitk_kernel(
         }
     }
     __syncthreads();
-    float *wout = ws + ((size_t)row * splits + split) * G * (D + 2);
-    for (int idx = threadIdx.x; idx < G * (D + 2); idx += 256) {
+    // per head: max over waves, then sum and output rescaled to it
+    const int W = G * (D + 2);
+    float *wpart = part + ((size_t)row * splits + split) * W;
+    for (int idx = tid; idx < W; idx += kAttnThreads) {
         const int g = idx / (D + 2), c = idx - g * (D + 2);
         float M = -__builtin_inff();
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w)
             M = fmaxf(M, sm[w][g][D]);
-        float r;
-        if (c == D) {
-            r = M;
-        } else if (M == -__builtin_inff()) {
+        float r = M;
+        if (c != D) {
             r = 0.0f;
-        } else {
-            r = 0.0f;
+            if (M != -__builtin_inff()) {
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) {
-                const float f = exp2f(sm[w][g][D] - M);
-                r = __builtin_fmaf(f, c == D + 1 ? sm[w][g][D + 1] : sm[w][g][c], r);
+                for (int w = 0; w < kAttnWaves; ++w)
+                    r = __builtin_fmaf(exp2f(sm[w][g][D] - M), sm[w][g][c], r);
             }
         }
-        wout[idx] = r;
+        if (splits == 1) {
+            if (c == D + 1)
+                shL[g] = r;
+            else if (c == D)
+                shM[g] = r;
+            else
+                sm[0][g][c] = r;  // only this thread reads sm[.][g][c] for this c < D
+        } else {
+            wpart[idx] = r;
+        }
+    }
+    const size_t obase = ((size_t)b * Hq + (size_t)j * G) * D;
+    if (splits == 1) {
+        __syncthreads();
+        for (int idx = tid; idx < G * D; idx += kAttnThreads) {
+            const int g = idx / D, d = idx - g * D;
+            const float L = shL[g];
+            out[obase + idx] = L > 0.0f ? sm[0][g][d] / L : 0.0f;
+        }
+        if (lse && tid < G)
+            lse[(size_t)b * Hq + (size_t)j * G + tid] = shL[tid] > 0.0f ? shM[tid] * kLn2 + logf(shL[tid])
+                                                                          : -__builtin_inff();
+        return;
     }
 }
 
 // one workgroup per (b, h); thread d owns output element d
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict__ ws, int Hq, int Hkv, int D,
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int D,
                                                          int splits, float *__restrict__ out,
                                                          float *__restrict__ lse) {
+    __shared__ float sw[kMaxSplits];  // weight of split s: exp2(m_s - M)
+    __shared__ float sl[kMaxSplits];
+    __shared__ float shM, shL;
     const int bh = blockIdx.x;
     const int b = bh / Hq, h = bh - b * Hq;
     const int G = Hq / Hkv;
     const int j = h / G, g = h - j * G;
-    const int row = b * Hkv + j;
-    const float *p = ws + (size_t)row * splits * G * (D + 2) + (size_t)g * (D + 2);
-    const size_t stride = (size_t)G * (D + 2);
-    float M = -__builtin_inff();
-    for (int s = 0; s < splits; ++s)
-        M = fmaxf(M, p[s * stride + D]);
-    float L = 0.0f;
-    if (M != -__builtin_inff())
+    const size_t W = (size_t)G * (D + 2);
+    const float *p = part + (size_t)(b * Hkv + j) * splits * W + (size_t)g * (D + 2);
+    for (int s = threadIdx.x; s < splits; s += blockDim.x) {
+        sw[s] = p[s * W + D];
+        sl[s] = p[s * W + D + 1];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float M = -__builtin_inff();
         for (int s = 0; s < splits; ++s)
-            L = __builtin_fmaf(exp2f(p[s * stride + D] - M), p[s * stride + D + 1], L);
-    const bool empty = !(L > 0.0f);
+            M = fmaxf(M, sw[s]);
+        float L = 0.0f;
+        if (M != -__builtin_inff())
+            for (int s = 0; s < splits; ++s)
+                L = __builtin_fmaf(exp2f(sw[s] - M), sl[s], L);
+        shM = M;
+        shL = L;
+    }
+    __syncthreads();
+    const float M = shM, L = shL;
+    for (int s = threadIdx.x; s < splits; s += blockDim.x)
+        sw[s] = L > 0.0f ? exp2f(sw[s] - M) : 0.0f;
+    __syncthreads();
     for (int d = threadIdx.x; d < D; d += blockDim.x) {
         float a = 0.0f;
-        if (!empty)
-            for (int s = 0; s < splits; ++s)
-                a = __builtin_fmaf(exp2f(p[s * stride + D] - M), p[s * stride + d], a);
-        out[(size_t)bh * D + d] = empty ? 0.0f : a / L;
+#pragma unroll 8
+        for (int s = 0; s < splits; ++s)
+            a = __builtin_fmaf(sw[s], p[s * W + d], a);
+        out[(size_t)bh * D + d] = L > 0.0f ? a / L : 0.0f;
     }
     if (lse && threadIdx.x == 0)
-        lse[bh] = empty ? -__builtin_inff() : M * 0.69314718055994531f + logf(L);
+        lse[bh] = L > 0.0f ? M * kLn2 + logf(L) : -__builtin_inff();
 }
 
 int attention_auto_splits(int rows, int k) {
-    int s = (1024 + rows - 1) / rows;
-    const int cap = k / 4 > 1 ? k / 4 : 1;
-    if (s > cap)
-        s = cap;
-    return s < 1 ? 1 : s;
+    (void)rows;
+    int s = (k + kAttnWaves - 1) / kAttnWaves;  // one block per wave
+    return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
 size_t attention_ws_bytes(int rows, int G, int D, int splits) {
+    if (splits <= 1)
+        return 256;
     size_t b = (size_t)rows * splits * G * (D + 2) * sizeof(float);
     return (b + 255) & ~(size_t)255;
 }
 
 template <typename E, int D, int GMAX>
-static hipError_t attn_t(const Dims &d, const void *q, const void *pk, const void *pv, int cap, const int32_t *sb,
-                         const int32_t *ss, const int32_t *sc, const int32_t *lens, int k, float scale, int splits,
-                         float *out, float *lse, float *ws, hipStream_t st) {
-    const int per = (k + splits - 1) / splits;
-    const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((attn_splitk_kernel<E, D, GMAX>), dim3(splits, d.rows()), dim3(256), 0, st,
-                       (const uint8_t *)q, (const uint8_t *)pk, (const uint8_t *)pv, cap, sb, ss, sc, lens, d.Hq,
-                       d.Hkv, k, splits, per, scale_log2, ws);
+static hipError_t attn_t(const Dims &d, const AttnArgs &a, hipStream_t st) {
+    const int per = (a.k + a.splits - 1) / a.splits;
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+    float *part = (float *)a.ws;
+    hipLaunchKernelGGL((attn_kernel<E, D, GMAX>), dim3(a.splits, d.rows()), dim3(kAttnThreads), 0, st,
+                       (const uint8_t *)a.q, (uint8_t *)a.pool_k, (uint8_t *)a.pool_v, a.cap, a.sel_blocks, a.sel_slot,
+                       a.sel_hit, a.sel_count, a.seq_lens, d.Hq, d.Hkv, d.T, a.k, a.splits, per, scale_log2,
+                       (const uint8_t *)a.src_k, (const uint8_t *)a.src_v, part, a.out, a.lse);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+    if (e != hipSuccess || a.splits == 1)
         return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(d.B * d.Hq), dim3(128), 0, st, (const float *)ws, d.Hq, d.Hkv, D,
-                       splits, out, lse);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(d.B * d.Hq), dim3(128), 0, st, (const float *)part, d.Hq, d.Hkv, D,
+                       a.splits, a.out, a.lse);
     return hipGetLastError();
 }
 
 template <typename E, int D>
-static hipError_t attn_g(const Dims &d, const void *q, const void *pk, const void *pv, int cap, const int32_t *sb,
-                         const int32_t *ss, const int32_t *sc, const int32_t *lens, int k, float scale, int splits,
-                         float *out, float *lse, float *ws, hipStream_t st) {
+static hipError_t attn_g(const Dims &d, const AttnArgs &a, hipStream_t st) {
     const int G = d.G();
     if (G <= 4)
-        return attn_t<E, D, 4>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st);
+        return attn_t<E, D, 4>(d, a, st);
     if (G <= 8)
-        return attn_t<E, D, 8>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st);
-    return attn_t<E, D, 16>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st);
+        return attn_t<E, D, 8>(d, a, st);
+    return attn_t<E, D, 16>(d, a, st);
 }
 
-hipError_t launch_attention(const Dims &d, const void *q, const void *pk, const void *pv, int cap,
-                            const int32_t *sb, const int32_t *ss, const int32_t *sc, const int32_t *lens, int k,
-                            float scale, int splits, float *out, float *lse, float *ws, hipStream_t st) {
+hipError_t launch_attention(const Dims &d, const AttnArgs &a, hipStream_t st) {
     if (d.dtype == 1)
-        return d.D == 128 ? attn_g<BF16, 128>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st)
-                          : attn_g<BF16, 64>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st);
-    return d.D == 128 ? attn_g<F32, 128>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st)
-                      : attn_g<F32, 64>(d, q, pk, pv, cap, sb, ss, sc, lens, k, scale, splits, out, lse, ws, st);
+        return d.D == 128 ? attn_g<BF16, 128>(d, a, st) : attn_g<BF16, 64>(d, a, st);
+    return d.D == 128 ? attn_g<F32, 128>(d, a, st) : attn_g<F32, 64>(d, a, st);
 }
 
 }  // namespace skv

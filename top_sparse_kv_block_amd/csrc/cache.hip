@@ -22,10 +22,14 @@
 //            ascending); a hit claims S[i] with an LDS compare-and-swap, so
 //            a block resident twice is detected.
 //   misses:  S indices without a slot, compacted in ascending order with a
-//            wave ballot / prefix count.
+//            workgroup prefix count.
 //   victims: candidate slots (empty, or occupied and not hit) ranked by the
-//            key (occupied, stamp, block-or-slot); rank r < #misses takes
-//            miss r.
+//            64-bit key (occupied, stamp, block-or-slot) precomputed in LDS;
+//            rank r < #misses takes miss r.
+//   The count, selection and slot table are read in one round of
+//   independent loads and the clock atomic is issued as soon as the row is
+//   known to be valid (after hit detection), so its latency overlaps the
+//   rest.
 // gather_kernel: one wave per miss copies the block's K and V rows (16*D
 // elements each) from the source (HBM, or mapped pinned host memory read
 // over PCIe) into its slot with 16-byte loads and stores.
@@ -87,30 +91,35 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     __shared__ uint8_t sHit[kMaxK];
     __shared__ int32_t sMissI[kMaxK];   // S index of miss m
     __shared__ int32_t sBlk[kMaxCapacity];
-    __shared__ uint32_t sStamp[kMaxCapacity];
-    __shared__ uint8_t sTaken[kMaxCapacity];  // slot holds a hit
+    __shared__ uint64_t sKey[kMaxCapacity];  // LRU key of a candidate slot, ~0 otherwise
     __shared__ int wsum[kCacheWaves];
     __shared__ uint32_t sClock;
 
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
-    const int n = sel_count[row];
     const int32_t *S = sel_blocks + (size_t)row * k;
     int32_t *sb = slot_block + (size_t)row * C;
     uint32_t *ss = slot_stamp + (size_t)row * C;
 
-    int bad = (n < 0 || n > k || n > C) ? 1 : 0;
-    const int nn = bad ? 0 : n;
+    // one round of independent global loads: count, selection, slot table
+    const int n = sel_count[row];
     for (int i = tid; i < k; i += kCacheThreads) {
-        sS[i] = i < nn ? S[i] : -1;
+        sS[i] = S[i];
         sSlotOf[i] = -1;
     }
-    for (int s = tid; s < C; s += kCacheThreads) {
-        sBlk[s] = sb[s];
-        sStamp[s] = ss[s];
-        sTaken[s] = 0;
+    uint32_t stamp_reg[(kMaxCapacity + kCacheThreads - 1) / kCacheThreads];
+#pragma unroll
+    for (int u = 0; u < (kMaxCapacity + kCacheThreads - 1) / kCacheThreads; ++u) {
+        const int s = tid + u * kCacheThreads;
+        if (s < C) {
+            sBlk[s] = sb[s];
+            stamp_reg[u] = ss[s];
+        }
     }
     __syncthreads();
+    const bool bad_count = n < 0 || n > k || n > C;
+    const int nn = bad_count ? 0 : n;
+    int bad = bad_count ? 1 : 0;
     for (int i = tid; i < nn; i += kCacheThreads) {
         const int32_t v = sS[i];
         if (v < 0 || v >= NB || (i > 0 && v <= sS[i - 1]))
@@ -124,25 +133,24 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
             miss_count[row] = -1;
         return;
     }
-
-    // hits
+    // hits: each occupied slot looks its block up in the ascending selection
     int dup = 0;
     for (int s = tid; s < C; s += kCacheThreads) {
         const int32_t blk = sBlk[s];
-        if (blk >= 0) {
-            const int i = find_sorted(sS, nn, blk);
-            if (i >= 0) {
-                if (atomicCAS(&sSlotOf[i], -1, s) != -1)
-                    dup = 1;
-                sTaken[s] = 1;
-            }
-        }
+        const int i = blk >= 0 ? find_sorted(sS, nn, blk) : -1;
+        if (i >= 0 && atomicCAS(&sSlotOf[i], -1, s) != -1)
+            dup = 1;
     }
-    if (__syncthreads_or(dup)) {
+    if (__syncthreads_or(dup)) {  // a block resident twice: nothing written yet
         if (tid == 0)
             miss_count[row] = -1;
         return;
     }
+    // the row is valid: advance its clock now; the value is needed only at
+    // the end, so the atomic's latency overlaps the work below
+    uint32_t now = 0;
+    if (tid == 0)
+        now = atomicAdd(&clock[row], 1u) + 1u;
 
     // misses, compacted in ascending S order: thread t owns S indices
     // [t*per, t*per+per)
@@ -163,32 +171,42 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
         if (i < nn && !sHit[i])
             sMissI[pos++] = i;
     }
+    // LRU keys of the candidate slots (empty, or occupied and not selected):
+    // empty slots first by slot index, then (stamp, block) ascending
+#pragma unroll
+    for (int u = 0; u < (kMaxCapacity + kCacheThreads - 1) / kCacheThreads; ++u) {
+        const int s = tid + u * kCacheThreads;
+        if (s < C) {
+            const int32_t blk = sBlk[s];
+            const bool taken = blk >= 0 && find_sorted(sS, nn, blk) >= 0;
+            sKey[s] = taken ? ~0ull
+                            : (blk < 0 ? (uint64_t)s
+                                       : ((1ull << 63) | ((uint64_t)stamp_reg[u] << 31) | (uint64_t)blk));
+        }
+    }
     __syncthreads();
 
-    // victims: rank the candidate slots by (occupied, stamp, block | slot)
+    // victims: candidate rank r < #misses takes miss r.  Keys of a valid
+    // table are distinct; the slot index breaks ties of a corrupt one.
     if (nm > 0) {
         for (int s = tid; s < C; s += kCacheThreads) {
-            if (sTaken[s])
+            const uint64_t key = sKey[s];
+            if (key == ~0ull)
                 continue;
-            const bool occ = sBlk[s] >= 0;
-            const uint64_t key = occ ? ((1ull << 63) | ((uint64_t)sStamp[s] << 31) | (uint64_t)sBlk[s]) : (uint64_t)s;
             int rank = 0;
-            for (int o = 0; o < C && rank < nm; ++o) {
-                if (sTaken[o])
-                    continue;
-                const bool oo = sBlk[o] >= 0;
-                const uint64_t ok =
-                    oo ? ((1ull << 63) | ((uint64_t)sStamp[o] << 31) | (uint64_t)sBlk[o]) : (uint64_t)o;
-                rank += (ok < key || (ok == key && o < s)) ? 1 : 0;  // slot breaks ties of a corrupt table
+#pragma unroll 8
+            for (int o = 0; o < C; ++o) {
+                const uint64_t ok = sKey[o];
+                rank += (ok < key || (ok == key && o < s)) ? 1 : 0;
             }
             if (rank < nm)
                 sSlotOf[sMissI[rank]] = s;
         }
     }
     if (tid == 0)
-        sClock = atomicAdd(&clock[row], 1u) + 1u;
+        sClock = now;
     __syncthreads();
-    const uint32_t now = sClock;
+    now = sClock;
 
     int32_t *o_slot = sel_slot + (size_t)row * k;
     uint8_t *o_hit = sel_hit + (size_t)row * k;

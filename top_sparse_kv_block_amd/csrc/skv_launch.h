@@ -31,10 +31,21 @@ hipError_t launch_cache_update(const Dims &d, int k, int cap, const int32_t *sel
 hipError_t launch_gather(const Dims &d, int k, int cap, const int32_t *miss_block, const int32_t *miss_slot,
                          const int32_t *miss_count, const void *src_k, const void *src_v, void *pool_k,
                          void *pool_v, hipStream_t st);
-hipError_t launch_attention(const Dims &d, const void *q, const void *pool_k, const void *pool_v, int cap,
-                            const int32_t *sel_blocks, const int32_t *sel_slot, const int32_t *sel_count,
-                            const int32_t *seq_lens, int k, float scale, int splits, float *out, float *lse,
-                            float *ws, hipStream_t st);
+struct AttnArgs {
+    const void *q;
+    void *pool_k, *pool_v;
+    int cap;
+    const int32_t *sel_blocks, *sel_slot;
+    const uint8_t *sel_hit;  // needed only with a source
+    const int32_t *sel_count, *seq_lens;
+    int k;
+    float scale;
+    int splits;
+    const void *src_k, *src_v;  // NULL: every selected block is already in the pool
+    float *out, *lse;
+    void *ws;
+};
+hipError_t launch_attention(const Dims &d, const AttnArgs &a, hipStream_t st);
 
 // limits shared by validation and launch code
 constexpr int kMaxQueryRows = 32;  // G * n_queries for scoring
@@ -42,6 +53,7 @@ constexpr int kMaxTopkBlocks = 65536;
 constexpr int kMaxK = 1024;
 constexpr int kMaxCapacity = 1024;
 constexpr int kMaxGroup = 16;  // G for attention
+constexpr int kMaxSplits = 128;
 
 int attention_auto_splits(int rows, int k);
 size_t attention_ws_bytes(int rows, int G, int D, int splits);

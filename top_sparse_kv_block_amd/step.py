@@ -105,17 +105,27 @@ class LayerBuffers:
                                  self.miss_slot, self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
                                  stream)
 
-    def attention(self, q, seq_lens, stream=None):
+    def attention(self, q, seq_lens, src_k=None, src_v=None, src_kind=B.SKV_SRC_DEVICE, stream=None):
+        """With src_k/src_v the misses are fetched here (fetch on attend)."""
         c = self.cfg
         B.sparse_decode_attention(self.shape, q, self.pool_k, self.pool_v, c.capacity, self.sel_blocks, self.sel_slot,
-                                  self.sel_count, seq_lens, c.k_blocks, c.softmax_scale, self.splits, self.out,
-                                  self.lse, self.workspace, stream)
+                                  self.sel_hit, self.sel_count, seq_lens, c.k_blocks, c.softmax_scale, self.splits,
+                                  src_k, src_v, src_kind, self.out, self.lse, self.workspace, stream)
 
 
 def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE,
-                stream=None):
-    """Enqueue one full step: score, top-k, cache update + fetch, attention."""
+                stream=None, fetch_on_attend=True):
+    """Enqueue one full step: score, top-k, cache update, attention.
+
+    The misses are copied into the pool either by the attention kernel while
+    it reads them (fetch_on_attend, the default: one read and one write per
+    missed block) or by the cache update's own copy pass.
+    """
     buf.score(score_q, keys_or_meta, seq_lens, stream)
     buf.topk(seq_lens, stream)
-    buf.cache_update(src_k, src_v, src_kind, stream)
-    buf.attention(q, seq_lens, stream)
+    if fetch_on_attend:
+        buf.cache_update(None, None, src_kind, stream)
+        buf.attention(q, seq_lens, src_k, src_v, src_kind, stream)
+    else:
+        buf.cache_update(src_k, src_v, src_kind, stream)
+        buf.attention(q, seq_lens, stream=stream)
