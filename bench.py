@@ -14,8 +14,11 @@ steps overlap (>80%) the way the method expects.
 
 Output: one JSON line with steps/s (value), ms per step, achieved
 algorithmic HBM GB/s for the whole step, the roofline of the dominant
-kernel (the block-scoring scan) timed live with HIP events on its stream,
-and the oracle's throughput on the host cores on a bounded sample.
+kernel (the block-scoring scan) and a per-call breakdown, both timed with
+HIP events on the stream the kernels run on during a second pass of the
+same steps right after the timed region (event markers inside the timed
+region would add queue gaps to it), and the oracle's throughput on the
+host cores on a bounded sample.
 """
 
 from __future__ import annotations
@@ -170,6 +173,7 @@ def run(args):
     scale = cfg.softmax_scale
 
     def step(t, ev=None):
+        # ev: optional list of 5 events bracketing the four calls (profiling pass only)
         if ev is not None:
             ev[0].record()
         B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
@@ -177,13 +181,19 @@ def run(args):
             ev[1].record()
         B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
                          buf.sel_count, st)
+        if ev is not None:
+            ev[2].record()
         # list-only cache update; the attention kernel fetches the misses
         B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count, buf.slot_block,
                                  buf.slot_stamp, buf.clock, buf.sel_slot, buf.sel_hit, buf.miss_block, buf.miss_slot,
                                  miss_log[t], None, None, B.SKV_SRC_DEVICE, buf.pool_k, buf.pool_v, st)
+        if ev is not None:
+            ev[3].record()
         B.sparse_decode_attention(shape, q_all[t], buf.pool_k, buf.pool_v, cfg.capacity, buf.sel_blocks,
                                   buf.sel_slot, buf.sel_hit, buf.sel_count, dlens, cfg.k_blocks, scale, buf.splits,
                                   dK, dV, B.SKV_SRC_DEVICE, buf.out, buf.lse, buf.workspace, st)
+        if ev is not None:
+            ev[4].record()
 
     # cold start, warm-up (not timed)
     buf.reset()
@@ -191,24 +201,54 @@ def run(args):
         step(t)
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronised on both sides
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # timed region: exactly `steps` steps, synchronised on both sides.  By
+    # default the steps are captured once into a HIP graph and the graph is
+    # replayed (the host then only submits one launch); --eager enqueues the
+    # four calls per step from Python instead.
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(args.warmup + i)
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
+    t_enq = time.perf_counter() - t0
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
-    score_ms = [a.elapsed_time(b) for a, b in evs]
     elapsed = max(wall, gpu_ms / 1e3)
-
     misses = miss_log[args.warmup:].sum().item()
+
+    # profiling passes right after the timed region, on the same stream:
+    # (a) the scoring kernel alone, `steps` launches back to back between two
+    #     events -> its average launch duration (the roofline point);
+    # (b) the same steps again with each call bracketed by events -> a
+    #     per-call breakdown (each bracket also holds one event marker).
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(args.steps):
+        B.sparse_kv_score(shape, mode, sq_all[args.warmup + i], cfg.n_queries, keys_or_meta, dlens, scale,
+                          buf.scores, st)
+    s1.record()
+    torch.cuda.synchronize()
+    score_avg_s = s0.elapsed_time(s1) / 1e3 / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    stage = np.array([[ev[c].elapsed_time(ev[c + 1]) for c in range(4)] for ev in evs]) * 1e3  # us
+
     bytes_total = step_bytes(w, misses / args.steps)["total"] * args.steps
-    score_avg_s = float(np.mean(score_ms)) / 1e3
     sbytes = score_launch_bytes(w)
     achieved = sbytes / score_avg_s / 1e9
     traffic = _traffic(w)
@@ -234,6 +274,10 @@ def run(args):
         "hbm_frac": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_total / args.steps),
         "miss_blocks_per_step": round(misses / args.steps, 1),
+        "mode": "hip-graph replay" if graph is not None else "eager",
+        "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
+        "stage_us": {name: round(float(v), 2) for name, v in
+                     zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))},
         "roofline": {"bound": "hbm", "kernel": "score_blockmax_kernel" if mode == B.SKV_SCORE_BLOCKMAX
                      else "score_quest_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -253,6 +297,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = library default)")
+    ap.add_argument("--eager", action="store_true", help="enqueue every call from Python instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)
