@@ -3,8 +3,9 @@
 
 A step is one pass of the whole path for one attention layer over one batch:
 block scoring -> top-k under the budget -> working-set update -> split-K GQA
-attention that also fetches the step's misses into the pool (four library
-calls, four kernels).  The default
+attention that also fetches the step's misses into the pool.  By default
+stages 2-4 run as the library's fused select-attend call (same results as
+the three separate calls; --four-calls runs those instead).  The default
 workload is the Llama-3.1-8B-shaped layer: batch 8, 32 q-heads / 8 kv-heads,
 head_dim 128, bf16 K/V, 32768-token context in 16-token blocks, a
 2048-token budget (128 blocks) and a 128-slot working set per (sequence,
@@ -173,6 +174,8 @@ def run(args):
     scale = cfg.softmax_scale
 
     def step(t, ev=None):
+        if args.fused:
+            return step_fused(t, ev)
         # ev: optional list of 5 events bracketing the four calls (profiling pass only)
         if ev is not None:
             ev[0].record()
@@ -194,6 +197,23 @@ def run(args):
                                   dK, dV, B.SKV_SRC_DEVICE, buf.out, buf.lse, buf.workspace, st)
         if ev is not None:
             ev[4].record()
+
+    def step_fused(t, ev=None):
+        # score, then top-k + working-set update + attention (fetching the
+        # misses) as the single fused call; ev brackets the two calls
+        if ev is not None:
+            ev[0].record()
+        B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
+        if ev is not None:
+            ev[1].record()
+        B.sparse_kv_select_attend(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, cfg.capacity,
+                                  buf.sel_blocks, buf.sel_count, buf.slot_block, buf.slot_stamp, buf.clock,
+                                  buf.sel_slot, buf.sel_hit, buf.miss_block, buf.miss_slot, miss_log[t], q_all[t],
+                                  buf.pool_k, buf.pool_v, dK, dV, B.SKV_SRC_DEVICE, scale, buf.fused_splits,
+                                  buf.out, buf.lse, buf.workspace, st)
+        if ev is not None:
+            for e in ev[2:]:
+                e.record()
 
     # cold start, warm-up (not timed)
     buf.reset()
@@ -269,15 +289,19 @@ def run(args):
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "ctx": w.ctx, "block": 16, "budget_tokens": w.budget,
                    "k_blocks": w.k_blocks, "capacity_slots": w.capacity, "scoring": w.scoring,
-                   "n_score_queries": w.n_score_queries, "attn_splits": buf.splits, "parallelism": "single-gpu"},
+                   "n_score_queries": w.n_score_queries, "attn_splits": buf.fused_splits if args.fused else buf.splits,
+                   "parallelism": "single-gpu"},
         "hbm_gbps": round(bytes_total / elapsed / 1e9, 1),
         "hbm_frac": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_total / args.steps),
         "miss_blocks_per_step": round(misses / args.steps, 1),
         "mode": "hip-graph replay" if graph is not None else "eager",
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
-        "stage_us": {name: round(float(v), 2) for name, v in
-                     zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))},
+        "path": "score + fused select/update/attend" if args.fused else "four calls",
+        "stage_us": ({"score": round(float(stage[:, 0].mean()), 2),
+                      "select_update_attend": round(float(stage[:, 1].mean()), 2)} if args.fused else
+                     {name: round(float(v), 2) for name, v in
+                      zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))}),
         "roofline": {"bound": "hbm", "kernel": "score_blockmax_kernel" if mode == B.SKV_SCORE_BLOCKMAX
                      else "score_quest_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -298,6 +322,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = library default)")
     ap.add_argument("--eager", action="store_true", help="enqueue every call from Python instead of a graph")
+    ap.add_argument("--four-calls", dest="fused", action="store_false",
+                    help="run stages 2-4 as three calls instead of the fused select-attend call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)

@@ -180,9 +180,9 @@ skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int
  *               mapped pinned host memory and the copy crosses PCIe.  NULL
  *               sources build the lists only (the "no-IO" control).
  * Bad input seen on the device (a selection not strictly ascending, an id
- * outside [0, NB), a count outside [0, k_blocks], or a corrupt slot table
- * holding a block twice or an id outside [0, NB)) leaves the row untouched
- * and sets miss_count = -1 for it.
+ * outside [0, NB), a count outside [0, k_blocks], or a corrupt slot table:
+ * an id outside [-1, NB), or a selected block held by two slots) leaves the
+ * row untouched and sets miss_count = -1 for it.
  * Limits: 1 <= k_blocks <= capacity <= 1024.
  */
 skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
@@ -234,8 +234,38 @@ skv_status sparse_decode_attention(const skv_shape *shape, const void *q, void *
                                    const void *src_v, int32_t src_kind, float *out, float *lse, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
-/* Number of splits num_splits = 0 resolves to. */
+/*
+ * Stages 2-4 in one call: sparse_kv_topk, then sparse_kv_cache_update with
+ * NULL sources (lists only), then sparse_decode_attention with the given
+ * sources (fetch on attend) -- the same results bit for bit, with every
+ * argument as in those calls (the workspace is sized by
+ * sparse_decode_attention_workspace_bytes).  Each workgroup of a row
+ * recomputes the row's top-k and working-set plan in on-chip memory before
+ * attending its share, so the three stages cost one pass over the scores
+ * and slot table instead of three launches with global round trips in
+ * between; the plan is committed to the slot table, stamps and clock at the
+ * end of the call.  A row whose slot table is found corrupt gets
+ * miss_count = -1, an untouched table, out = 0 and lse = -inf.
+ * num_splits = 0 resolves to sparse_kv_select_attend_splits (fewer, larger
+ * parts than the attention call's default: the fused call prefers one
+ * resident workgroup per CU); results equal the separate calls' bit for bit
+ * when both use the same num_splits.  The workspace must hold
+ * sparse_decode_attention_workspace_bytes(shape, k_blocks, splits) bytes for
+ * the resolved split count.
+ * Limits: those of the three calls, and NB <= 8192.
+ */
+skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                                   int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t capacity,
+                                   int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block,
+                                   uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit,
+                                   int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count, const void *q,
+                                   void *pool_k, void *pool_v, const void *src_k, const void *src_v,
+                                   int32_t src_kind, float scale, int32_t num_splits, float *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Number of splits num_splits = 0 resolves to (attention / fused call). */
 int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k_blocks);
+int32_t sparse_kv_select_attend_splits(const skv_shape *shape, int32_t k_blocks);
 
 /* Workspace bytes sparse_decode_attention needs (0 on invalid arguments). */
 size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, int32_t k_blocks,

@@ -1,0 +1,71 @@
+"""The fused select -> update -> attend call equals the three separate calls
+(top-k, list-only working-set update, attention with fetch on attend) bit for
+bit, step after step, and equals the oracle through the step tests."""
+import numpy as np
+import pytest
+import torch
+
+from top_sparse_kv_block_amd import binding as B
+from top_sparse_kv_block_amd import synth
+from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig, decode_step
+from gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "clock", "sel_slot", "sel_hit",
+          "miss_block", "miss_slot", "miss_count", "pool_k", "pool_v")
+
+
+@pytest.mark.parametrize("name,kw,steps,splits", [
+    ("tiny", {}, 4, 0),
+    ("tiny", dict(capacity=8), 4, 0),
+    ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 6, 0),
+    ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 4, 5),
+    ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 3, 32),
+    ("llama8b_32k", dict(batch=3, ctx=2048 + 16 * 7, budget=256, capacity=40, ragged=True), 4, 0),
+    ("quest_128k", dict(batch=2, ctx=8192), 4, 0),
+    ("lookahead_1m", dict(ctx=16384), 3, 0),
+])
+def test_fused_equals_separate_calls(name, kw, steps, splits):
+    w = synth.WORKLOADS[name].scaled(steps=steps, **kw)
+    data = synth.gen_workload(w)
+    mode = B.SKV_SCORE_QUEST if w.scoring == "quest" else B.SKV_SCORE_BLOCKMAX
+    shape = B.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype)
+    # equal split counts on both paths (each call's own default differs)
+    splits = splits or B.sparse_kv_select_attend_splits(shape, w.k_blocks)
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
+                     mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent, num_splits=splits)
+    a, b = LayerBuffers(cfg), LayerBuffers(cfg)
+    K, V, lens = dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
+    keys = K
+    if mode == B.SKV_SCORE_QUEST:
+        keys = torch.empty(w.batch, w.n_kv_heads, w.nb_max, 2, w.head_dim, dtype=cfg.torch_dtype, device="cuda")
+        B.sparse_kv_quest_meta(cfg.shape, K, lens, keys)
+    for t in range(steps):
+        log("fused vs separate", name, kw, "step", t)
+        q, sq = dev(data["q"][t]), dev(data["score_q"][t])
+        decode_step(a, q, sq, keys, lens, K, V, fused=False)
+        decode_step(b, q, sq, keys, lens, K, V, fused=True)
+        torch.cuda.synchronize()
+        for f in FIELDS:
+            np.testing.assert_array_equal(host(getattr(b, f)), host(getattr(a, f)), err_msg=f"{f} at step {t}")
+
+
+def test_fused_flags_a_corrupt_table():
+    w = synth.WORKLOADS["tiny"].scaled(steps=1)
+    data = synth.gen_workload(w)
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity)
+    buf = LayerBuffers(cfg)
+    K, V, lens = dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
+    table = np.full((1, 2, w.capacity), -1, dtype=np.int32)
+    table[0, 0, :2] = [5, w.nb_max + 3]  # row 0 holds a block id past the end
+    buf.slot_block.copy_(dev(table))
+    log("fused corrupt table")
+    decode_step(buf, dev(data["q"][0]), dev(data["score_q"][0]), K, lens, K, V, fused=True)
+    torch.cuda.synchronize()
+    assert host(buf.miss_count)[0, 0] == -1 and host(buf.miss_count)[0, 1] == w.k_blocks
+    np.testing.assert_array_equal(host(buf.slot_block)[0, 0], table[0, 0])  # untouched
+    assert host(buf.clock).tolist() == [[0, 1]]
+    G = w.group
+    assert not host(buf.out)[0, :G].any() and np.all(np.isneginf(host(buf.lse)[0, :G]))
+    assert np.isfinite(host(buf.lse)[0, G:]).all()

@@ -43,7 +43,7 @@ def _forced_sets(w, lens):
     return out
 
 
-def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_on_attend=True):
+def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_on_attend=True, fused=False):
     """Run `steps` steps of workload `w`; check rows `rows` (None = all) of
     the scores and (b, h) pairs `heads` (None = all) of the attention."""
     steps = steps or w.steps
@@ -69,7 +69,8 @@ def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_
     total_miss = 0
     for t in range(steps):
         log(w.name, "step", t, (w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx))
-        decode_step(buf, dev(q[t]), dev(sq[t]), keys_or_meta, dlens, dK, dV, fetch_on_attend=fetch_on_attend)
+        decode_step(buf, dev(q[t]), dev(sq[t]), keys_or_meta, dlens, dK, dV, fetch_on_attend=fetch_on_attend,
+                    fused=fused)
         torch.cuda.synchronize()
         g_scores = host(buf.scores).astype(np.float64)
         g_sel, g_cnt = host(buf.sel_blocks), host(buf.sel_count)
@@ -169,9 +170,14 @@ def test_lookahead_drafts_reduced():
     run_workload(w, steps=3)
 
 
-def test_llama8b_full_size_sampled():
-    # full throughput workload (launch configuration of the benchmark); the
+@pytest.mark.parametrize("fused", [False, True])
+def test_llama8b_full_size_sampled(fused):
+    # full throughput workload (the benchmark runs the fused call); the
     # oracle checks sampled score rows and attention heads, and every row of
     # top-k (on the GPU's scores) and of the working set
     w = synth.WORKLOADS["llama8b_32k"]
-    run_workload(w, steps=3, rows=[0, 21, 63], heads=[(0, 0), (2, 13), (7, 31)])
+    run_workload(w, steps=3, rows=[0, 21, 63], heads=[(0, 0), (2, 13), (7, 31)], fused=fused)
+
+
+def test_tiny_workload_fused():
+    run_workload(synth.WORKLOADS["tiny"], fused=True)

@@ -30,7 +30,8 @@ STATUS = {
 EXPORTS = (
     "sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
     "sparse_decode_attention_splits", "sparse_decode_attention_workspace_bytes", "sparse_kv_quest_meta",
-    "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string",
+    "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
+    "sparse_kv_select_attend_splits",
 )
 
 
@@ -66,6 +67,10 @@ def load():
                                          _p]
     L.sparse_decode_attention.argtypes = [S, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _i32, _p, _p,
                                           _p, _sz, _p]
+    L.sparse_kv_select_attend.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                          _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _p, _sz, _p]
+    L.sparse_kv_select_attend_splits.argtypes = [S, _i32]
+    L.sparse_kv_select_attend_splits.restype = _i32
     L.sparse_decode_attention_splits.argtypes = [S, _i32]
     L.sparse_decode_attention_splits.restype = _i32
     L.sparse_decode_attention_workspace_bytes.argtypes = [S, _i32, _i32]
@@ -76,7 +81,7 @@ def load():
     L.sparse_kv_status_string.argtypes = [C.c_int]
     L.sparse_kv_status_string.restype = C.c_char_p
     for fn in ("sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
-               "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free"):
+               "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_select_attend"):
         getattr(L, fn).restype = C.c_int
     _lib = L
     return L
@@ -207,8 +212,43 @@ def sparse_decode_attention(shape, q, pool_k, pool_v, capacity, sel_blocks, sel_
     _check("sparse_decode_attention", rc)
 
 
+def sparse_kv_select_attend(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity, sel_blocks,
+                            sel_count, slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block, miss_slot,
+                            miss_count, q, pool_k, pool_v, src_k, src_v, src_kind, scale, num_splits, out, lse,
+                            workspace, stream=None):
+    """Top-k + working-set update + attention with fetch-on-attend in one call."""
+    dt = _torch_dtype(shape.dtype)
+    b, hq, d, t = shape.batch, shape.n_q_heads, shape.head_dim, shape.max_ctx
+    P = b * shape.n_kv_heads
+    pk, pc = P * k_blocks, P * capacity
+
+    def src(x, name):
+        if isinstance(x, int):
+            return x
+        return _ptr(x, dt, name, numel=P * t * d)
+
+    rc = load().sparse_kv_select_attend(
+        C.byref(shape), _ptr(scores, torch.float32, "scores", numel=P * (t // 16)),
+        _ptr(seq_lens, torch.int32, "seq_lens", numel=b), int(k_blocks), int(sink_tokens), int(recent_tokens),
+        int(capacity), _ptr(sel_blocks, torch.int32, "sel_blocks", numel=pk),
+        _ptr(sel_count, torch.int32, "sel_count", numel=P), _ptr(slot_block, torch.int32, "slot_block", numel=pc),
+        _ptr(slot_stamp, torch.int32, "slot_stamp", numel=pc), _ptr(clock, torch.int32, "clock", numel=P),
+        _ptr(sel_slot, torch.int32, "sel_slot", numel=pk), _ptr(sel_hit, torch.uint8, "sel_hit", numel=pk),
+        _ptr(miss_block, torch.int32, "miss_block", numel=pk), _ptr(miss_slot, torch.int32, "miss_slot", numel=pk),
+        _ptr(miss_count, torch.int32, "miss_count", numel=P), _ptr(q, dt, "q", numel=b * hq * d),
+        _ptr(pool_k, dt, "pool_k", numel=pc * 16 * d), _ptr(pool_v, dt, "pool_v", numel=pc * 16 * d),
+        src(src_k, "src_k"), src(src_v, "src_v"), int(src_kind), float(scale), int(num_splits),
+        _ptr(out, torch.float32, "out", numel=b * hq * d), _ptr(lse, torch.float32, "lse", allow_none=True, numel=b * hq),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("sparse_kv_select_attend", rc)
+
+
 def sparse_decode_attention_splits(shape, k_blocks) -> int:
     return int(load().sparse_decode_attention_splits(C.byref(shape), int(k_blocks)))
+
+
+def sparse_kv_select_attend_splits(shape, k_blocks) -> int:
+    return int(load().sparse_kv_select_attend_splits(C.byref(shape), int(k_blocks)))
 
 
 def sparse_decode_attention_workspace_bytes(shape, k_blocks, num_splits) -> int:

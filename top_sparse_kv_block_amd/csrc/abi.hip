@@ -122,6 +122,13 @@ SKV_API int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k
     return skv::attention_auto_splits(d.rows(), k_blocks);
 }
 
+SKV_API int32_t sparse_kv_select_attend_splits(const skv_shape *shape, int32_t k_blocks) {
+    Dims d;
+    if (check_shape(shape, d) != SKV_OK || k_blocks < 1)
+        return 0;
+    return skv::fused_auto_splits(d.rows(), k_blocks);
+}
+
 SKV_API size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits) {
     Dims d;
     if (check_shape(shape, d) != SKV_OK || k_blocks < 1 || num_splits < 0 || num_splits > k_blocks ||
@@ -161,6 +168,49 @@ SKV_API skv_status sparse_decode_attention(const skv_shape *shape, const void *q
                     seq_lens,  k_blocks, scale,      splits,   src_k,      src_v,    out,     lse,
                     workspace};
     return hip_status(skv::launch_attention(d, a, (hipStream_t)stream));
+}
+
+SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                                           int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens,
+                                           int32_t capacity, int32_t *sel_blocks, int32_t *sel_count,
+                                           int32_t *slot_block, uint32_t *slot_stamp, uint32_t *clock,
+                                           int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                                           int32_t *miss_slot, int32_t *miss_count, const void *q, void *pool_k,
+                                           void *pool_v, const void *src_k, const void *src_v, int32_t src_kind,
+                                           float scale, int32_t num_splits, float *out, float *lse, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!scores || !seq_lens || !sel_blocks || !sel_count || !slot_block || !slot_stamp || !clock || !sel_slot ||
+        !sel_hit || !miss_block || !miss_slot || !miss_count || !q || !pool_k || !pool_v || !src_k || !src_v || !out)
+        return SKV_ERR_NULL;
+    if (d.NB > skv::kMaxFusedBlocks)
+        return SKV_ERR_UNSUPPORTED;
+    if (k_blocks < 1 || k_blocks > d.NB || k_blocks > skv::kMaxK || sink_tokens < 0 || recent_tokens < 0 ||
+        capacity < 1 || num_splits < 0 || num_splits > k_blocks || num_splits > skv::kMaxSplits)
+        return SKV_ERR_SHAPE;
+    if (capacity < k_blocks)
+        return SKV_ERR_CAPACITY;
+    if (capacity > skv::kMaxCapacity || d.G() > skv::kMaxGroup)
+        return SKV_ERR_UNSUPPORTED;
+    if (sink_tokens > 0 || recent_tokens > 0) {
+        const long long forced_max = (long long)nb_blocks(sink_tokens) + nb_blocks(recent_tokens) + 1;
+        if (forced_max > k_blocks)
+            return SKV_ERR_CAPACITY;
+    }
+    if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
+        return SKV_ERR_SHAPE;
+    const int splits = num_splits == 0 ? skv::fused_auto_splits(d.rows(), k_blocks) : num_splits;
+    const size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return SKV_ERR_WORKSPACE;
+    skv::FusedArgs f{scores,   seq_lens,  k_blocks,  sink_tokens, recent_tokens, capacity,   sel_blocks,
+                     sel_count, slot_block, slot_stamp, clock,     sel_slot,      sel_hit,    miss_block,
+                     miss_slot, miss_count, q,          pool_k,    pool_v,        src_k,      src_v,
+                     scale,     splits,     out,        lse,       workspace};
+    return hip_status(skv::launch_select_attend(d, f, (hipStream_t)stream));
 }
 
 SKV_API skv_status sparse_kv_quest_meta(const skv_shape *shape, const void *keys, const int32_t *seq_lens, void *meta,

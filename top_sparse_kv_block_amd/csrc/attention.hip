@@ -1,35 +1,45 @@
 // Stage 4: GQA decode attention over the selected blocks, split-K with an
-// online-softmax merge, on gfx950.
+// online-softmax merge, on gfx950; and the fused select -> update -> attend
+// kernel that runs stages 2-4 of a row in one launch.
 //
 // Exact attention over the KV the step kept (OasisKV summary, key module 1)
 // read from the working set through the slot table (a block-table
 // indirection: KV-Cache 压缩技术的工程原理 §5.2), so the result does not
 // depend on which tier the blocks came from (HiSparse promo, insight 1).
 //
-// attn_kernel: grid (splits, rows), 8 waves.  The workgroup of split s owns
-// a contiguous share of the row's selection and each wave takes one block
-// of it at a time, so a workgroup has all of its blocks' K and V loads in
-// flight at once.  A wave loads the block's K and V (16 tokens) with the
-// coalesced 16-byte lane layout of the scoring kernel and uses them for all
-// G query heads of the kv group (each byte is read once per group).
-// Logits are kept in base-2 units (scale*log2(e)*q.k); the running max is
-// per head and wave-uniform; each lane accumulates its own tokens' share of
-// l and of the output, so per block the only cross-lane work is the
-// dot-product sums and one max per head.  Waves are combined in LDS; with
-// one split the workgroup writes the output directly, otherwise it writes
-// (max, sum, unnormalised output) per head to the workspace.
-// attn_merge_kernel: one workgroup per (b, h) loads every split's (max, sum)
-// in one round of independent loads, forms the weights exp2(m_s - m*) in
-// LDS, and each thread sums its output element over the splits.  (A merge
-// by the last workgroup of each row would need a device-scope release per
-// workgroup, which on this chip writes back the whole L2 each time.)
+// attn_body: one workgroup of 8 waves owns a contiguous share of a row's
+// selection and each wave takes one block of it at a time, so all of the
+// workgroup's K and V loads are in flight at once.  A wave loads the block's
+// K and V (16 tokens) with the coalesced 16-byte lane layout of the scoring
+// kernel and uses them for all G query heads of the kv group (each byte is
+// read once per group).  Logits are kept in base-2 units (scale*log2(e)*q.k);
+// the running max is per head and wave-uniform; each lane accumulates its
+// own tokens' share of l and of the output, so per block the only
+// cross-lane work is the dot-product sums and one max per head.  Waves are
+// combined in LDS; with one split the workgroup writes the output directly,
+// otherwise (max, sum, unnormalised output) per head go to the workspace.
 //
-// Fetch on attend (optional): when a source cache is given, a selected
-// block that was not resident (sel_hit == 0) is read from the source by
-// block id and also written into its pool slot, so the miss costs one read
-// and one write and no separate copy pass.
-#include "skv_device.h"
-#include "skv_launch.h"
+// Fetch on attend (optional): when a source cache is given, a selected block
+// that was not resident (hit == 0) is read from the source by block id and
+// also written into its pool slot, so a miss costs one read and one write
+// and no separate copy pass.
+//
+// select_attend_kernel: grid (splits, rows).  Every workgroup of a row first
+// recomputes the row's top-k and working-set plan in LDS (a few KB of scores
+// and slot state, identical code to the standalone kernels, so identical
+// results), then attends its share.  Split 0 also writes the selection and
+// the step's lists.  The slot table is only read here; merge_commit_kernel
+// applies the plan after every workgroup has read the old table.  This
+// replaces three launches and their global round trips with one: the
+// alternative, handing results between workgroups inside one launch, needs
+// a device-scope release per workgroup, which on this chip writes back the
+// whole L2 each time.
+//
+// merge_commit_kernel: one workgroup per row merges the splits' partials
+// (weights exp2(m_s - m*) formed once in LDS) and, when asked, commits the
+// working-set plan (new blocks and stamps for the selected slots, the
+// clock advanced by a device atomic).
+#include "skv_rowops.h"
 
 namespace skv {
 
@@ -39,15 +49,15 @@ template <> __device__ __forceinline__ float token_groups_max<8>(float v) {
     return rows_max(v);
 }
 template <> __device__ __forceinline__ float token_groups_max<16>(float v) { return rows_max(v); }
-template <> __device__ __forceinline__ float token_groups_max<32>(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+template <> __device__ __forceinline__ float token_groups_max<32>(float v) { return xor32_max(v); }
 
 template <int LPT> __device__ __forceinline__ float token_groups_sum(float v);
 template <> __device__ __forceinline__ float token_groups_sum<8>(float v) {
-    v += __shfl_xor(v, 8);
+    v += dpp<DPP_ROW_ROR8>(v);  // lanes i and i+8 of a row: the other 8-lane group
     return rows_sum(v);
 }
 template <> __device__ __forceinline__ float token_groups_sum<16>(float v) { return rows_sum(v); }
-template <> __device__ __forceinline__ float token_groups_sum<32>(float v) { return v + __shfl_xor(v, 32); }
+template <> __device__ __forceinline__ float token_groups_sum<32>(float v) { return xor32_sum(v); }
 
 template <typename E> __device__ __forceinline__ float elem(u32x4 v, int e) {
     if constexpr (E::bytes == 2)
@@ -60,40 +70,39 @@ constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr float kLn2 = 0.69314718055994531f;
 
-template <typename E, int D, int GMAX>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
-    const uint8_t *__restrict__ q, uint8_t *__restrict__ pool_k, uint8_t *__restrict__ pool_v, int C,
-    const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_slot, const uint8_t *__restrict__ sel_hit,
-    const int32_t *__restrict__ sel_count, const int32_t *__restrict__ seq_lens, int Hq, int Hkv, int T, int k,
-    int splits, int per_split, float scale_log2, const uint8_t *__restrict__ src_k, const uint8_t *__restrict__ src_v,
-    float *__restrict__ part, float *__restrict__ out, float *__restrict__ lse) {
+template <int D, int GMAX> struct AttnSmem {
+    float sm[kAttnWaves][GMAX][D + 2];
+    float shM[GMAX], shL[GMAX];
+};
+
+struct AttnRow {
+    const uint8_t *q;              // q of the group's first head, [G, D]
+    uint8_t *pool_k, *pool_v;      // the row's slots, [C, 16, D]
+    const uint8_t *src_k, *src_v;  // the row's source [T, D], or NULL
+    const int32_t *blk, *slot;
+    const uint8_t *hit;
+    int C, NB, G, len, i0, i1, splits;
+    float scale_log2;
+    float *part;  // this workgroup's partials [G, D + 2] (splits > 1)
+    float *out;   // the group's outputs [G, D] (splits == 1)
+    float *lse;   // [G] or NULL (splits == 1)
+};
+
+template <typename E, int D, int GMAX, int DEPTH>
+__device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S) {
     constexpr int LPT = D * E::bytes / 16;
     constexpr int TPL = 64 / LPT;
     constexpr int LPB = 16 / TPL;
     constexpr int EPL = E::EPL;
     constexpr size_t kBlockBytes = (size_t)16 * D * E::bytes;
-    __shared__ float sm[kAttnWaves][GMAX][D + 2];
-    __shared__ float shM[GMAX], shL[GMAX];
-
-    const int row = blockIdx.y, split = blockIdx.x;
-    const int b = row / Hkv, j = row - b * Hkv;
-    const int G = Hq / Hkv;
-    const int NB = T / 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane % LPT, tg = lane / LPT;
+    const int G = a.G;
 
     u32x4 qf[GMAX];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g)
-        qf[g] = g < G ? load16(q + (((size_t)b * Hq + (size_t)j * G + g) * D + sub * EPL) * E::bytes)
-                      : u32x4{0, 0, 0, 0};
-
-    const int len = max(seq_lens[b], 0);
-    const int n = min(max(sel_count[row], 0), k);
-    const int i0 = split * per_split;
-    const int i1 = min(i0 + per_split, n);
-    const int32_t *sblk = sel_blocks + (size_t)row * k;
-    const int32_t *sslot = sel_slot + (size_t)row * k;
+        qf[g] = g < G ? load16(a.q + ((size_t)g * D + sub * EPL) * E::bytes) : u32x4{0, 0, 0, 0};
 
     float m[GMAX], l[GMAX], acc[GMAX][EPL];
 #pragma unroll
@@ -105,28 +114,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
             acc[g][e] = 0.0f;
     }
 
-    for (int i = i0 + wave; i < i1; i += kAttnWaves) {
-        const int blk = sblk[i], s = sslot[i];
-        if (blk < 0 || s < 0 || s >= C)
-            continue;
-        const bool fetch = src_k != nullptr && blk < NB && sel_hit[(size_t)row * k + i] == 0;
-        const int nv = min(max(len - blk * 16, 0), 16);
-        if (nv == 0 && !fetch)
-            continue;
-        uint8_t *pk = pool_k + ((size_t)row * C + s) * kBlockBytes;
-        uint8_t *pv = pool_v + ((size_t)row * C + s) * kBlockBytes;
-        const uint8_t *rk = fetch ? src_k + ((size_t)row * T + (size_t)blk * 16) * D * E::bytes : pk;
-        const uint8_t *rv = fetch ? src_v + ((size_t)row * T + (size_t)blk * 16) * D * E::bytes : pv;
-        const size_t lo = ((size_t)tg * D + sub * EPL) * E::bytes;
-        constexpr size_t step = (size_t)TPL * D * E::bytes;
-        u32x4 kv[LPB], vv[LPB];
+    // one block of the selection: where to read it, whether to fetch it
+    auto describe = [&](int i, int &blk, int &s, int &nv, bool &fetch) -> bool {
+        if (i >= a.i1)
+            return false;
+        blk = a.blk[i];
+        s = a.slot[i];
+        if (blk < 0 || s < 0 || s >= a.C)
+            return false;
+        fetch = a.src_k != nullptr && blk < a.NB && a.hit[i] == 0;
+        nv = min(max(a.len - blk * 16, 0), 16);
+        return nv > 0 || fetch;
+    };
+    const size_t lo = ((size_t)tg * D + sub * EPL) * E::bytes;
+    constexpr size_t step = (size_t)TPL * D * E::bytes;
+    auto load_block = [&](int blk, int s, bool fetch, u32x4 *kv, u32x4 *vv) {
+        const uint8_t *rk = fetch ? a.src_k + (size_t)blk * kBlockBytes : a.pool_k + (size_t)s * kBlockBytes;
+        const uint8_t *rv = fetch ? a.src_v + (size_t)blk * kBlockBytes : a.pool_v + (size_t)s * kBlockBytes;
 #pragma unroll
         for (int li = 0; li < LPB; ++li)
             kv[li] = fetch ? load_nt(rk + lo + li * step) : load16(rk + lo + li * step);
 #pragma unroll
         for (int li = 0; li < LPB; ++li)
             vv[li] = fetch ? load_nt(rv + lo + li * step) : load16(rv + lo + li * step);
+    };
+    auto attend_block = [&](int s, int nv, bool fetch, const u32x4 *kv, const u32x4 *vv) {
         if (fetch) {
+            uint8_t *pk = a.pool_k + (size_t)s * kBlockBytes;
+            uint8_t *pv = a.pool_v + (size_t)s * kBlockBytes;
 #pragma unroll
             for (int li = 0; li < LPB; ++li) {
                 store16(pk + lo + li * step, kv[li]);
@@ -134,22 +149,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
             }
         }
         if (nv == 0)
-            continue;
-
+            return;
         float z[LPB][GMAX];
 #pragma unroll
         for (int li = 0; li < LPB; ++li) {
-            const bool valid = li * TPL + tg < nv;
 #pragma unroll
-            for (int g = 0; g < GMAX; ++g) {
-                float t = -__builtin_inff();
-                if (g < G) {
-                    t = group_sum<LPT>(dot_chunk<E>(kv[li], qf[g], 0.0f)) * scale_log2;
-                    if (!valid)
-                        t = -__builtin_inff();
+            for (int g = 0; g < GMAX; ++g)
+                z[li][g] = g < G ? group_sum<LPT>(dot_chunk<E>(kv[li], qf[g], 0.0f)) * a.scale_log2
+                                 : -__builtin_inff();
+        }
+        if (nv < 16) {  // partial last block: drop the tokens past the end
+#pragma unroll
+            for (int li = 0; li < LPB; ++li)
+                if (li * TPL + tg >= nv) {
+#pragma unroll
+                    for (int g = 0; g < GMAX; ++g)
+                        z[li][g] = -__builtin_inff();
                 }
-                z[li][g] = t;
-            }
         }
 #pragma unroll
         for (int g = 0; g < GMAX; ++g) {
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
                 bm = fmaxf(bm, z[li][g]);
             bm = token_groups_max<LPT>(bm);
             const float mn = fmaxf(m[g], bm);
-            const float alpha = exp2f(m[g] - mn);  // m = -inf -> 0
+            const float alpha = exp2_fast(m[g] - mn);  // m = -inf -> 0
             m[g] = mn;
             l[g] *= alpha;
 #pragma unroll
@@ -169,12 +185,54 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
                 acc[g][e] *= alpha;
 #pragma unroll
             for (int li = 0; li < LPB; ++li) {
-                const float p = exp2f(z[li][g] - mn);
+                const float p = exp2_fast(z[li][g] - mn);
                 l[g] += p;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e)
                     acc[g][e] = __builtin_fmaf(p, elem<E>(vv[li], e), acc[g][e]);
             }
+        }
+    };
+
+    // The wave's blocks are i0 + wave + 8*j.  DEPTH 1: one at a time.
+    // DEPTH 2: rolling, the next block's K and V loads are in flight while
+    // the current block is attended.  DEPTH > 2: taken DEPTH at a time, all
+    // their loads issued before any is used.
+    if constexpr (DEPTH == 2) {
+        int blk0, s0, nv0, blk1, s1, nv1;
+        bool f0, f1;
+        u32x4 k0[LPB], v0[LPB], k1[LPB], v1[LPB];
+        int i = a.i0 + wave;
+        bool h0 = describe(i, blk0, s0, nv0, f0);
+        if (h0)
+            load_block(blk0, s0, f0, k0, v0);
+        for (; i < a.i1; i += 2 * kAttnWaves) {
+            const bool h1 = describe(i + kAttnWaves, blk1, s1, nv1, f1);
+            if (h1)
+                load_block(blk1, s1, f1, k1, v1);
+            if (h0)
+                attend_block(s0, nv0, f0, k0, v0);
+            h0 = describe(i + 2 * kAttnWaves, blk0, s0, nv0, f0);
+            if (h0)
+                load_block(blk0, s0, f0, k0, v0);
+            if (h1)
+                attend_block(s1, nv1, f1, k1, v1);
+        }
+    } else {
+        for (int base = a.i0 + wave; base < a.i1; base += DEPTH * kAttnWaves) {
+            int blk[DEPTH], s[DEPTH], nv[DEPTH];
+            bool fetch[DEPTH], have[DEPTH];
+            u32x4 kv[DEPTH][LPB], vv[DEPTH][LPB];
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                have[d] = describe(base + d * kAttnWaves, blk[d], s[d], nv[d], fetch[d]);
+                if (have[d])
+                    load_block(blk[d], s[d], fetch[d], kv[d], vv[d]);
+            }
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d)
+                if (have[d])
+                    attend_block(s[d], nv[d], fetch[d], kv[d], vv[d]);
         }
     }
 
@@ -190,106 +248,246 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
         if (tg == 0) {
 #pragma unroll
             for (int e = 0; e < EPL; ++e)
-                sm[wave][g][sub * EPL + e] = acc[g][e];
+                S.sm[wave][g][sub * EPL + e] = acc[g][e];
             if (sub == 0) {
-                sm[wave][g][D] = m[g];
-                sm[wave][g][D + 1] = l[g];
+                S.sm[wave][g][D] = m[g];
+                S.sm[wave][g][D + 1] = l[g];
             }
         }
     }
     __syncthreads();
     // per head: max over waves, then sum and output rescaled to it
     const int W = G * (D + 2);
-    float *wpart = part + ((size_t)row * splits + split) * W;
     for (int idx = tid; idx < W; idx += kAttnThreads) {
         const int g = idx / (D + 2), c = idx - g * (D + 2);
         float M = -__builtin_inff();
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w)
-            M = fmaxf(M, sm[w][g][D]);
+            M = fmaxf(M, S.sm[w][g][D]);
         float r = M;
         if (c != D) {
             r = 0.0f;
             if (M != -__builtin_inff()) {
 #pragma unroll
                 for (int w = 0; w < kAttnWaves; ++w)
-                    r = __builtin_fmaf(exp2f(sm[w][g][D] - M), sm[w][g][c], r);
+                    r = __builtin_fmaf(exp2f(S.sm[w][g][D] - M), S.sm[w][g][c], r);
             }
         }
-        if (splits == 1) {
+        if (a.splits == 1) {
             if (c == D + 1)
-                shL[g] = r;
+                S.shL[g] = r;
             else if (c == D)
-                shM[g] = r;
+                S.shM[g] = r;
             else
-                sm[0][g][c] = r;  // only this thread reads sm[.][g][c] for this c < D
+                S.sm[0][g][c] = r;  // only this thread reads sm[.][g][c] for this c < D
         } else {
-            wpart[idx] = r;
+            a.part[idx] = r;
         }
     }
-    const size_t obase = ((size_t)b * Hq + (size_t)j * G) * D;
-    if (splits == 1) {
+    if (a.splits == 1) {
         __syncthreads();
         for (int idx = tid; idx < G * D; idx += kAttnThreads) {
             const int g = idx / D, d = idx - g * D;
-            const float L = shL[g];
-            out[obase + idx] = L > 0.0f ? sm[0][g][d] / L : 0.0f;
+            const float L = S.shL[g];
+            a.out[idx] = L > 0.0f ? S.sm[0][g][d] / L : 0.0f;
         }
-        if (lse && tid < G)
-            lse[(size_t)b * Hq + (size_t)j * G + tid] = shL[tid] > 0.0f ? shM[tid] * kLn2 + logf(shL[tid])
-                                                                          : -__builtin_inff();
-        return;
+        if (a.lse && tid < G)
+            a.lse[tid] = S.shL[tid] > 0.0f ? S.shM[tid] * kLn2 + logf(S.shL[tid]) : -__builtin_inff();
     }
 }
 
-// one workgroup per (b, h); thread d owns output element d
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int D,
-                                                         int splits, float *__restrict__ out,
-                                                         float *__restrict__ lse) {
-    __shared__ float sw[kMaxSplits];  // weight of split s: exp2(m_s - M)
-    __shared__ float sl[kMaxSplits];
-    __shared__ float shM, shL;
-    const int bh = blockIdx.x;
-    const int b = bh / Hq, h = bh - b * Hq;
+template <typename E, int D>
+__device__ __forceinline__ void init_row(AttnRow &a, const uint8_t *q, uint8_t *pool_k, uint8_t *pool_v,
+                                         const uint8_t *src_k, const uint8_t *src_v, int row, int b, int j, int Hq,
+                                         int G, int C, int T, int split, int splits, float scale_log2, float *part,
+                                         float *out, float *lse) {
+    const size_t kv_row = (size_t)16 * D * E::bytes;
+    a.q = q + ((size_t)b * Hq + (size_t)j * G) * D * E::bytes;
+    a.pool_k = pool_k + (size_t)row * C * kv_row;
+    a.pool_v = pool_v + (size_t)row * C * kv_row;
+    a.src_k = src_k ? src_k + (size_t)row * T * D * E::bytes : nullptr;
+    a.src_v = src_v ? src_v + (size_t)row * T * D * E::bytes : nullptr;
+    a.C = C;
+    a.NB = T / 16;
+    a.G = G;
+    a.splits = splits;
+    a.scale_log2 = scale_log2;
+    a.part = part + ((size_t)row * splits + split) * G * (D + 2);
+    a.out = out + ((size_t)b * Hq + (size_t)j * G) * D;
+    a.lse = lse ? lse + (size_t)b * Hq + (size_t)j * G : nullptr;
+}
+
+// Up to 4 heads per group: at least 4 waves per SIMD (<= 128 VGPRs), i.e.
+// two 8-wave workgroups per CU; larger groups need the registers.
+constexpr int attn_min_waves(int gmax) { return gmax <= 4 ? 4 : 2; }
+
+template <typename E, int D, int GMAX>
+__global__ __launch_bounds__(kAttnThreads, attn_min_waves(GMAX)) void attn_kernel(
+    const uint8_t *__restrict__ q, uint8_t *__restrict__ pool_k, uint8_t *__restrict__ pool_v, int C,
+    const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_slot, const uint8_t *__restrict__ sel_hit,
+    const int32_t *__restrict__ sel_count, const int32_t *__restrict__ seq_lens, int Hq, int Hkv, int T, int k,
+    int splits, int per_split, float scale_log2, const uint8_t *__restrict__ src_k, const uint8_t *__restrict__ src_v,
+    float *__restrict__ part, float *__restrict__ out, float *__restrict__ lse) {
+    __shared__ AttnSmem<D, GMAX> S;
+    const int row = blockIdx.y, split = blockIdx.x;
+    const int b = row / Hkv, j = row - b * Hkv;
+    const int n = min(max(sel_count[row], 0), k);
+    AttnRow a;
+    init_row<E, D>(a, q, pool_k, pool_v, src_k, src_v, row, b, j, Hq, Hq / Hkv, C, T, split, splits, scale_log2,
+                   part, out, lse);
+    a.blk = sel_blocks + (size_t)row * k;
+    a.slot = sel_slot + (size_t)row * k;
+    a.hit = sel_hit ? sel_hit + (size_t)row * k : nullptr;
+    a.len = max(seq_lens[b], 0);
+    a.i0 = split * per_split;
+    a.i1 = min(a.i0 + per_split, n);
+    attn_body<E, D, GMAX, 1>(a, S);
+}
+
+// Blocks of K and V a wave of the fused kernel holds at once (see
+// attn_body): two if they fit next to the per-head state in about 216 of
+// its 256 registers (2 waves per SIMD).
+template <typename E, int D, int GMAX> constexpr int fused_depth() {
+    constexpr int lpb = D * E::bytes / 64;  // 16-byte loads per lane per block, K or V
+    constexpr int fixed = GMAX * (4 + E::EPL + 2 + lpb);
+    return fixed + 2 * 8 * lpb <= 216 ? 2 : 1;
+}
+
+template <typename E, int D, int GMAX, int KPT>
+__global__ __launch_bounds__(kAttnThreads, 2) void select_attend_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int k, int sink, int recent, int C,
+    int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count, const int32_t *__restrict__ slot_block,
+    const uint32_t *__restrict__ slot_stamp, int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit,
+    int32_t *__restrict__ miss_block, int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count,
+    const uint8_t *__restrict__ q, uint8_t *__restrict__ pool_k, uint8_t *__restrict__ pool_v,
+    const uint8_t *__restrict__ src_k, const uint8_t *__restrict__ src_v, int Hq, int Hkv, int T, int splits,
+    int per_split, float scale_log2, float *__restrict__ part, float *__restrict__ out, float *__restrict__ lse) {
+    __shared__ TopkScratch tsc;
+    __shared__ int32_t sS[kMaxK];
+    __shared__ CacheScratch cs;
+    __shared__ AttnSmem<D, GMAX> S;
+    const int row = blockIdx.y, split = blockIdx.x;
+    const int b = row / Hkv, j = row - b * Hkv;
+    const int NB = T / 16;
+    const int len = min(max(seq_lens[b], 0), T);
+    SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
+    load_slots<kAttnThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
+
+    const int nn = topk_row<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, sS, tsc);
+    int bad;
+    const int nm = cache_plan_row<kAttnThreads>(sS, nn, C, NB, regs, cs, bad);
+    if (split == 0) {
+        for (int i = threadIdx.x; i < k; i += kAttnThreads)
+            sel_blocks[(size_t)row * k + i] = sS[i];
+        if (threadIdx.x == 0)
+            sel_count[row] = nn;
+        if (bad) {
+            if (threadIdx.x == 0)
+                miss_count[row] = -1;
+        } else {
+            write_lists<kAttnThreads>(sS, nn, nm, k, cs, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
+                                      miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);
+        }
+    }
+    AttnRow a;
+    init_row<E, D>(a, q, pool_k, pool_v, src_k, src_v, row, b, j, Hq, Hq / Hkv, C, T, split, splits, scale_log2,
+                   part, out, lse);
+    a.blk = sS;
+    a.slot = cs.slot_of;
+    a.hit = cs.hit;
+    a.len = len;
+    a.i0 = split * per_split;
+    a.i1 = bad ? a.i0 : min(a.i0 + per_split, nn);  // an invalid row attends nothing
+    attn_body<E, D, GMAX, fused_depth<E, D, GMAX>()>(a, S);
+}
+
+// One workgroup per row: merge the row's G heads over the splits (when
+// splits > 1), then commit the row's working-set plan (when commit is set):
+// every selected slot gets its block and the new stamp, the clock advances.
+__global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
+    const float *__restrict__ part, int Hq, int Hkv, int D, int splits, float *__restrict__ out,
+    float *__restrict__ lse, int commit, int k, int C, const int32_t *__restrict__ sel_blocks,
+    const int32_t *__restrict__ sel_count, const int32_t *__restrict__ sel_slot,
+    const int32_t *__restrict__ miss_count, int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp,
+    uint32_t *__restrict__ clock) {
+    __shared__ float sw[kMaxGroup][kMaxSplits];  // m_s, then the weight exp2(m_s - M)
+    __shared__ float sl[kMaxGroup][kMaxSplits];
+    __shared__ float shM[kMaxGroup], shL[kMaxGroup];
+    __shared__ uint32_t sNow;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
-    const int j = h / G, g = h - j * G;
     const size_t W = (size_t)G * (D + 2);
-    const float *p = part + (size_t)(b * Hkv + j) * splits * W + (size_t)g * (D + 2);
-    for (int s = threadIdx.x; s < splits; s += blockDim.x) {
-        sw[s] = p[s * W + D];
-        sl[s] = p[s * W + D + 1];
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float M = -__builtin_inff();
-        for (int s = 0; s < splits; ++s)
-            M = fmaxf(M, sw[s]);
-        float L = 0.0f;
-        if (M != -__builtin_inff())
+    const bool do_commit = commit && miss_count[row] >= 0;  // uniform over the workgroup
+    if (do_commit && tid == 0)
+        sNow = atomicAdd(&clock[row], 1u) + 1u;
+    if (splits > 1) {
+        const float *p = part + (size_t)row * splits * W;
+        for (int t = tid; t < splits * G; t += kAttnThreads) {
+            const int s = t / G, g = t - s * G;
+            sw[g][s] = p[s * W + g * (D + 2) + D];
+            sl[g][s] = p[s * W + g * (D + 2) + D + 1];
+        }
+        __syncthreads();
+        if (tid < G) {
+            float M = -__builtin_inff();
             for (int s = 0; s < splits; ++s)
-                L = __builtin_fmaf(exp2f(sw[s] - M), sl[s], L);
-        shM = M;
-        shL = L;
-    }
-    __syncthreads();
-    const float M = shM, L = shL;
-    for (int s = threadIdx.x; s < splits; s += blockDim.x)
-        sw[s] = L > 0.0f ? exp2f(sw[s] - M) : 0.0f;
-    __syncthreads();
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float a = 0.0f;
+                M = fmaxf(M, sw[tid][s]);
+            float L = 0.0f;
+            if (M != -__builtin_inff())
+                for (int s = 0; s < splits; ++s)
+                    L = __builtin_fmaf(exp2f(sw[tid][s] - M), sl[tid][s], L);
+            shM[tid] = M;
+            shL[tid] = L;
+        }
+        __syncthreads();
+        for (int t = tid; t < splits * G; t += kAttnThreads) {
+            const int s = t / G, g = t - s * G;
+            sw[g][s] = shL[g] > 0.0f ? exp2f(sw[g][s] - shM[g]) : 0.0f;
+        }
+        __syncthreads();
+        float *o = out + ((size_t)b * Hq + (size_t)j * G) * D;
+        for (int idx = tid; idx < G * D; idx += kAttnThreads) {
+            const int g = idx / D, d = idx - g * D;
+            const float L = shL[g];
+            float a = 0.0f;
 #pragma unroll 8
-        for (int s = 0; s < splits; ++s)
-            a = __builtin_fmaf(sw[s], p[s * W + d], a);
-        out[(size_t)bh * D + d] = L > 0.0f ? a / L : 0.0f;
+            for (int s = 0; s < splits; ++s)
+                a = __builtin_fmaf(sw[g][s], p[s * W + g * (D + 2) + d], a);
+            o[idx] = L > 0.0f ? a / L : 0.0f;
+        }
+        if (lse && tid < G)
+            lse[(size_t)b * Hq + (size_t)j * G + tid] =
+                shL[tid] > 0.0f ? shM[tid] * kLn2 + logf(shL[tid]) : -__builtin_inff();
     }
-    if (lse && threadIdx.x == 0)
-        lse[bh] = L > 0.0f ? M * kLn2 + logf(L) : -__builtin_inff();
+    if (do_commit) {
+        __syncthreads();
+        const uint32_t now = sNow;
+        const int n = min(max(sel_count[row], 0), k);
+        for (int i = tid; i < n; i += kAttnThreads) {
+            const int s = sel_slot[(size_t)row * k + i];
+            if (s >= 0 && s < C) {
+                slot_block[(size_t)row * C + s] = sel_blocks[(size_t)row * k + i];
+                slot_stamp[(size_t)row * C + s] = now;
+            }
+        }
+    }
 }
 
 int attention_auto_splits(int rows, int k) {
     (void)rows;
     int s = (k + kAttnWaves - 1) / kAttnWaves;  // one block per wave
+    return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+}
+
+// The fused call redoes the row's top-k and plan in every workgroup, so it
+// prefers about one workgroup per CU in total (all resident at once), each
+// wave streaming several blocks with the next one prefetched.
+int fused_auto_splits(int rows, int k) {
+    int s = (256 + rows - 1) / rows;
+    const int one_per_wave = (k + kAttnWaves - 1) / kAttnWaves;
+    if (s > one_per_wave)
+        s = one_per_wave;
     return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 
@@ -312,8 +510,9 @@ static hipError_t attn_t(const Dims &d, const AttnArgs &a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1)
         return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(d.B * d.Hq), dim3(128), 0, st, (const float *)part, d.Hq, d.Hkv, D,
-                       a.splits, a.out, a.lse);
+    hipLaunchKernelGGL(merge_commit_kernel, dim3(d.rows()), dim3(kAttnThreads), 0, st, (const float *)part, d.Hq,
+                       d.Hkv, d.D, a.splits, a.out, a.lse, 0, a.k, a.cap, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -331,6 +530,49 @@ hipError_t launch_attention(const Dims &d, const AttnArgs &a, hipStream_t st) {
     if (d.dtype == 1)
         return d.D == 128 ? attn_g<BF16, 128>(d, a, st) : attn_g<BF16, 64>(d, a, st);
     return d.D == 128 ? attn_g<F32, 128>(d, a, st) : attn_g<F32, 64>(d, a, st);
+}
+
+// ---------------------------------------------------------------- fused
+template <typename E, int D, int GMAX, int KPT>
+static hipError_t fused_t(const Dims &d, const FusedArgs &f, hipStream_t st) {
+    const int per = (f.k + f.splits - 1) / f.splits;
+    const float scale_log2 = f.scale * 1.4426950408889634f;
+    float *part = (float *)f.ws;
+    hipLaunchKernelGGL((select_attend_kernel<E, D, GMAX, KPT>), dim3(f.splits, d.rows()), dim3(kAttnThreads), 0, st,
+                       f.scores, f.seq_lens, f.k, f.sink, f.recent, f.cap, f.sel_blocks, f.sel_count, f.slot_block,
+                       f.slot_stamp, f.sel_slot, f.sel_hit, f.miss_block, f.miss_slot, f.miss_count,
+                       (const uint8_t *)f.q, (uint8_t *)f.pool_k, (uint8_t *)f.pool_v, (const uint8_t *)f.src_k,
+                       (const uint8_t *)f.src_v, d.Hq, d.Hkv, d.T, f.splits, per, scale_log2, part, f.out, f.lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(merge_commit_kernel, dim3(d.rows()), dim3(kAttnThreads), 0, st, (const float *)part, d.Hq,
+                       d.Hkv, d.D, f.splits, f.out, f.lse, 1, f.k, f.cap, f.sel_blocks, f.sel_count, f.sel_slot,
+                       f.miss_count, f.slot_block, f.slot_stamp, f.clock);
+    return hipGetLastError();
+}
+
+template <typename E, int D, int GMAX>
+static hipError_t fused_k(const Dims &d, const FusedArgs &f, hipStream_t st) {
+    if (d.NB <= kAttnThreads * 4)
+        return fused_t<E, D, GMAX, 4>(d, f, st);
+    return fused_t<E, D, GMAX, 16>(d, f, st);
+}
+
+template <typename E, int D>
+static hipError_t fused_g(const Dims &d, const FusedArgs &f, hipStream_t st) {
+    const int G = d.G();
+    if (G <= 4)
+        return fused_k<E, D, 4>(d, f, st);
+    if (G <= 8)
+        return fused_k<E, D, 8>(d, f, st);
+    return fused_k<E, D, 16>(d, f, st);
+}
+
+hipError_t launch_select_attend(const Dims &d, const FusedArgs &f, hipStream_t st) {
+    if (d.dtype == 1)
+        return d.D == 128 ? fused_g<BF16, 128>(d, f, st) : fused_g<BF16, 64>(d, f, st);
+    return d.D == 128 ? fused_g<F32, 128>(d, f, st) : fused_g<F32, 64>(d, f, st);
 }
 
 }  // namespace skv

@@ -33,201 +33,58 @@
 // gather_kernel: one wave per miss copies the block's K and V rows (16*D
 // elements each) from the source (HBM, or mapped pinned host memory read
 // over PCIe) into its slot with 16-byte loads and stores.
-#include "skv_device.h"
-#include "skv_launch.h"
+#include "skv_rowops.h"
 
 namespace skv {
 
 constexpr int kCacheThreads = 256;
-constexpr int kCacheWaves = kCacheThreads / 64;
-
-// inclusive-scan helper over the workgroup: returns the exclusive prefix of
-// v in thread order and the total
-__device__ __forceinline__ int wg_exclusive_scan(int v, int *wsum, int &total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off);
-        if (lane >= off)
-            x += y;
-    }
-    if (lane == 63)
-        wsum[wave] = x;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kCacheWaves; ++w) {
-        base += (w < wave) ? wsum[w] : 0;
-        tot += wsum[w];
-    }
-    __syncthreads();
-    total = tot;
-    return base + x - v;
-}
-
-__device__ __forceinline__ int find_sorted(const int32_t *S, int n, int32_t x) {
-    int lo = 0, hi = n - 1;
-    while (lo <= hi) {
-        const int mid = (lo + hi) >> 1;
-        const int32_t v = S[mid];
-        if (v == x)
-            return mid;
-        if (v < x)
-            lo = mid + 1;
-        else
-            hi = mid - 1;
-    }
-    return -1;
-}
 
 __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_count, int k, int C, int NB,
     int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp, uint32_t *__restrict__ clock,
     int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit, int32_t *__restrict__ miss_block,
     int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count) {
-    __shared__ int32_t sS[kMaxK];       // selection
-    __shared__ int32_t sSlotOf[kMaxK];  // slot of S[i]
-    __shared__ uint8_t sHit[kMaxK];
-    __shared__ int32_t sMissI[kMaxK];   // S index of miss m
-    __shared__ int32_t sBlk[kMaxCapacity];
-    __shared__ uint64_t sKey[kMaxCapacity];  // LRU key of a candidate slot, ~0 otherwise
-    __shared__ int wsum[kCacheWaves];
+    __shared__ int32_t sS[kMaxK];
+    __shared__ CacheScratch cs;
     __shared__ uint32_t sClock;
-
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t *S = sel_blocks + (size_t)row * k;
     int32_t *sb = slot_block + (size_t)row * C;
     uint32_t *ss = slot_stamp + (size_t)row * C;
 
-    // one round of independent global loads: count, selection, slot table
     const int n = sel_count[row];
-    for (int i = tid; i < k; i += kCacheThreads) {
+    SlotRegs<kCacheThreads> regs;
+    load_slots<kCacheThreads>(regs, C, sb, ss);
+    for (int i = tid; i < k; i += kCacheThreads)
         sS[i] = S[i];
-        sSlotOf[i] = -1;
-    }
-    uint32_t stamp_reg[(kMaxCapacity + kCacheThreads - 1) / kCacheThreads];
-#pragma unroll
-    for (int u = 0; u < (kMaxCapacity + kCacheThreads - 1) / kCacheThreads; ++u) {
-        const int s = tid + u * kCacheThreads;
-        if (s < C) {
-            sBlk[s] = sb[s];
-            stamp_reg[u] = ss[s];
-        }
-    }
-    __syncthreads();
-    const bool bad_count = n < 0 || n > k || n > C;
-    const int nn = bad_count ? 0 : n;
-    int bad = bad_count ? 1 : 0;
-    for (int i = tid; i < nn; i += kCacheThreads) {
-        const int32_t v = sS[i];
-        if (v < 0 || v >= NB || (i > 0 && v <= sS[i - 1]))
-            bad = 1;
-    }
-    for (int s = tid; s < C; s += kCacheThreads)
-        if (sBlk[s] < -1 || sBlk[s] >= NB)
-            bad = 1;
-    if (__syncthreads_or(bad)) {
+    const bool bad_count = n < 0 || n > k || n > C;  // uniform over the workgroup
+    if (bad_count) {
         if (tid == 0)
             miss_count[row] = -1;
         return;
     }
-    // hits: each occupied slot looks its block up in the ascending selection
-    int dup = 0;
-    for (int s = tid; s < C; s += kCacheThreads) {
-        const int32_t blk = sBlk[s];
-        const int i = blk >= 0 ? find_sorted(sS, nn, blk) : -1;
-        if (i >= 0 && atomicCAS(&sSlotOf[i], -1, s) != -1)
-            dup = 1;
-    }
-    if (__syncthreads_or(dup)) {  // a block resident twice: nothing written yet
+    __syncthreads();
+    int bad;
+    const int nm = cache_plan_row<kCacheThreads>(sS, n, C, NB, regs, cs, bad);
+    if (bad) {
         if (tid == 0)
             miss_count[row] = -1;
         return;
     }
-    // the row is valid: advance its clock now; the value is needed only at
-    // the end, so the atomic's latency overlaps the work below
-    uint32_t now = 0;
     if (tid == 0)
-        now = atomicAdd(&clock[row], 1u) + 1u;
-
-    // misses, compacted in ascending S order: thread t owns S indices
-    // [t*per, t*per+per)
-    const int per = (k + kCacheThreads - 1) / kCacheThreads;
-    int cnt = 0;
-    for (int u = 0; u < per; ++u) {
-        const int i = tid * per + u;
-        if (i < nn) {
-            const bool hit = sSlotOf[i] >= 0;
-            sHit[i] = hit ? 1 : 0;
-            cnt += hit ? 0 : 1;
-        }
-    }
-    int nm;
-    int pos = wg_exclusive_scan(cnt, wsum, nm);
-    for (int u = 0; u < per; ++u) {
-        const int i = tid * per + u;
-        if (i < nn && !sHit[i])
-            sMissI[pos++] = i;
-    }
-    // LRU keys of the candidate slots (empty, or occupied and not selected):
-    // empty slots first by slot index, then (stamp, block) ascending
-#pragma unroll
-    for (int u = 0; u < (kMaxCapacity + kCacheThreads - 1) / kCacheThreads; ++u) {
-        const int s = tid + u * kCacheThreads;
-        if (s < C) {
-            const int32_t blk = sBlk[s];
-            const bool taken = blk >= 0 && find_sorted(sS, nn, blk) >= 0;
-            sKey[s] = taken ? ~0ull
-                            : (blk < 0 ? (uint64_t)s
-                                       : ((1ull << 63) | ((uint64_t)stamp_reg[u] << 31) | (uint64_t)blk));
-        }
-    }
+        sClock = atomicAdd(&clock[row], 1u) + 1u;
     __syncthreads();
-
-    // victims: candidate rank r < #misses takes miss r.  Keys of a valid
-    // table are distinct; the slot index breaks ties of a corrupt one.
-    if (nm > 0) {
-        for (int s = tid; s < C; s += kCacheThreads) {
-            const uint64_t key = sKey[s];
-            if (key == ~0ull)
-                continue;
-            int rank = 0;
-#pragma unroll 8
-            for (int o = 0; o < C; ++o) {
-                const uint64_t ok = sKey[o];
-                rank += (ok < key || (ok == key && o < s)) ? 1 : 0;
-            }
-            if (rank < nm)
-                sSlotOf[sMissI[rank]] = s;
-        }
-    }
-    if (tid == 0)
-        sClock = now;
-    __syncthreads();
-    now = sClock;
-
-    int32_t *o_slot = sel_slot + (size_t)row * k;
-    uint8_t *o_hit = sel_hit + (size_t)row * k;
-    int32_t *o_mb = miss_block + (size_t)row * k;
-    int32_t *o_ms = miss_slot + (size_t)row * k;
-    for (int i = tid; i < k; i += kCacheThreads) {
-        const bool in = i < nn;
-        const int s = in ? sSlotOf[i] : -1;
-        o_slot[i] = s;
-        o_hit[i] = in ? sHit[i] : 0;
-        if (in && s >= 0 && s < C) {
+    const uint32_t now = sClock;
+    write_lists<kCacheThreads>(sS, n, nm, k, cs, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
+                               miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);
+    for (int i = tid; i < n; i += kCacheThreads) {
+        const int s = cs.slot_of[i];
+        if (s >= 0 && s < C) {
             sb[s] = sS[i];
             ss[s] = now;
         }
-        const bool mi = i < nm;
-        const int si = mi ? sMissI[i] : 0;
-        o_mb[i] = mi ? sS[si] : -1;
-        o_ms[i] = mi ? sSlotOf[si] : -1;
     }
-    if (tid == 0)
-        miss_count[row] = nm;
 }
 
 // One wave copies one missed block: K then V, 16*D elements each.

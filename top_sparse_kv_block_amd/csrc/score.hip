@@ -29,7 +29,7 @@ template <> __device__ __forceinline__ float groups_max<8>(float v) {
     return rows_max(v);
 }
 template <> __device__ __forceinline__ float groups_max<16>(float v) { return rows_max(v); }
-template <> __device__ __forceinline__ float groups_max<32>(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+template <> __device__ __forceinline__ float groups_max<32>(float v) { return xor32_max(v); }
 
 // 16 waves x 4 blocks per wave per workgroup (64 blocks = 256 KiB of bf16
 // keys at D=128): a launch-shape sweep on the 32K workload measured this

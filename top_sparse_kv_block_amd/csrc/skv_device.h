@@ -75,6 +75,25 @@ template <int CTRL> __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
+// Cross-row exchange in registers (gfx950 v_permlane16/32_swap): the pair
+// returned holds this lane's value and that of lane l^16 (resp. l^32).
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Sum over aligned groups of L lanes (L = 8, 16 or 32); every lane of the
 // group receives the group's total.  The order of the additions is fixed,
 // so the result is deterministic.
@@ -95,10 +114,11 @@ template <> __device__ __forceinline__ float group_sum<8>(float v) {
     return v;
 }
 
-template <> __device__ __forceinline__ float group_sum<32>(float v) {
-    v = group_sum<16>(v);
-    return v + __shfl_xor(v, 16);
-}
+template <> __device__ __forceinline__ float group_sum<32>(float v) { return xor16_sum(group_sum<16>(v)); }
+
+// max / sum across the lanes l, l^16, l^32, l^48 (the four rows of the wave)
+__device__ __forceinline__ float rows_max(float v) { return xor32_max(xor16_max(v)); }
+__device__ __forceinline__ float rows_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 // max over the whole wave (all lanes receive it)
 __device__ __forceinline__ float wave_max(float v) {
@@ -106,20 +126,27 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp<DPP_ROW_ROR4>(v));
     v = fmaxf(v, dpp<DPP_ROW_ROR2>(v));
     v = fmaxf(v, dpp<DPP_ROW_ROR1>(v));
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+    return rows_max(v);
 }
 
-// max across the lanes l, l^16, l^32, l^48 (the four rows of the wave)
-__device__ __forceinline__ float rows_max(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+template <int CTRL, int ROWMASK> __device__ __forceinline__ uint32_t dpp_zero(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += dpp_zero<0x111, 0xf>(v);  // row_shr:1
+    v += dpp_zero<0x112, 0xf>(v);  // row_shr:2
+    v += dpp_zero<0x114, 0xf>(v);  // row_shr:4
+    v += dpp_zero<0x118, 0xf>(v);  // row_shr:8
+    v += dpp_zero<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v += dpp_zero<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
 }
 
-__device__ __forceinline__ float rows_sum(float v) {
-    v += __shfl_xor(v, 16);
-    return v + __shfl_xor(v, 32);
-}
+// fast exp2 for arguments <= 0 (v_exp_f32; results below the smallest
+// normal flush to zero, which is what the softmax wants)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ int nb_of(int len) { return (len + 15) >> 4; }
 

@@ -46,6 +46,24 @@ struct AttnArgs {
     void *ws;
 };
 hipError_t launch_attention(const Dims &d, const AttnArgs &a, hipStream_t st);
+struct FusedArgs {
+    const float *scores;
+    const int32_t *seq_lens;
+    int k, sink, recent, cap;
+    int32_t *sel_blocks, *sel_count, *slot_block;
+    uint32_t *slot_stamp, *clock;
+    int32_t *sel_slot;
+    uint8_t *sel_hit;
+    int32_t *miss_block, *miss_slot, *miss_count;
+    const void *q;
+    void *pool_k, *pool_v;
+    const void *src_k, *src_v;
+    float scale;
+    int splits;
+    float *out, *lse;
+    void *ws;
+};
+hipError_t launch_select_attend(const Dims &d, const FusedArgs &f, hipStream_t st);
 
 // limits shared by validation and launch code
 constexpr int kMaxQueryRows = 32;  // G * n_queries for scoring
@@ -54,8 +72,10 @@ constexpr int kMaxK = 1024;
 constexpr int kMaxCapacity = 1024;
 constexpr int kMaxGroup = 16;  // G for attention
 constexpr int kMaxSplits = 128;
+constexpr int kMaxFusedBlocks = 8192;  // NB limit of the fused select -> attend call
 
 int attention_auto_splits(int rows, int k);
+int fused_auto_splits(int rows, int k);
 size_t attention_ws_bytes(int rows, int G, int D, int splits);
 
 }  // namespace skv

@@ -13,44 +13,11 @@
 // exactly that key still fit; one pass of two workgroup prefix sums then
 // emits the chosen ids in ascending order (ties at the threshold go to the
 // lowest ids because the equal-key rank is a prefix count in id order).
-#include "skv_device.h"
-#include "skv_launch.h"
+#include "skv_rowops.h"
 
 namespace skv {
 
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0 so equal floats give equal keys
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix sum over the 1024 threads in thread order; also returns
-// the total.  `wsum` is LDS scratch of kTopkWaves entries.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum, uint32_t &total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_up(x, off);
-        if (lane >= off)
-            x += y;
-    }
-    if (lane == 63)
-        wsum[wave] = x;
-    __syncthreads();
-    uint32_t base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkWaves; ++w) {
-        uint32_t s = wsum[w];
-        base += (w < wave) ? s : 0u;
-        tot += s;
-    }
-    __syncthreads();
-    total = tot;
-    return base + x - v;
-}
 
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ scores,
@@ -58,125 +25,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
                                                             int NB, int k, int sink, int recent,
                                                             int32_t *__restrict__ sel_blocks,
                                                             int32_t *__restrict__ sel_count) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t wsum[kTopkWaves];
-    __shared__ uint32_t sh_digit, sh_remaining;
-
+    __shared__ TopkScratch sc;
     const int row = blockIdx.x;
-    const int b = row / Hkv;
-    const int tid = threadIdx.x;
-    const int len = min(max(seq_lens[b], 0), T);
-    const int nvalid = min(nb_of(len), NB);
-    int32_t *out = sel_blocks + (size_t)row * k;
-
-    if (nvalid <= k) {
-        for (int i = tid; i < k; i += kTopkThreads)
-            out[i] = i < nvalid ? i : -1;
-        if (tid == 0)
-            sel_count[row] = nvalid;
-        return;
-    }
-    // forced ranges [0, fs) and [fr, nvalid)
-    const int fs = sink > 0 ? min(nb_of(min(sink, len)), nvalid) : 0;
-    const int fr = recent > 0 ? max(0, len - recent) / 16 : nvalid;
-    const int n_forced = fs + (nvalid - fr) - max(0, fs - fr);
-    const int need = k - n_forced;
-
-    const float *srow = scores + (size_t)row * NB;
-    uint32_t key[KPT];
-    uint64_t cand = 0, forced = 0;  // bit m: id tid*KPT+m is a candidate / forced
-#pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-        const int i = tid * KPT + m;
-        key[m] = 0;
-        if (i < nvalid) {
-            if (i < fs || i >= fr) {
-                forced |= 1ull << m;
-            } else {
-                cand |= 1ull << m;
-                key[m] = order_key(srow[i]);
-            }
-        }
-    }
-
-    uint32_t prefix = 0, mask = 0;
-    uint32_t remaining = (uint32_t)max(need, 0);
-    if (need > 0) {
-#pragma unroll 1
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            if (tid < 256)
-                hist[tid] = 0;
-            __syncthreads();
-#pragma unroll
-            for (int m = 0; m < KPT; ++m)
-                if (((cand >> m) & 1u) && (key[m] & mask) == prefix)
-                    atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
-            __syncthreads();
-            // find the digit holding the remaining-th largest key: an
-            // inclusive scan over the bins from the top digit down (waves
-            // 0-3 scan; every wave reaches both barriers)
-            uint32_t c = 0, x = 0;
-            if (tid < 256) {
-                const int lane = tid & 63;
-                c = hist[255 - tid];
-                x = c;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    uint32_t y = __shfl_up(x, off);
-                    if (lane >= off)
-                        x += y;
-                }
-                if (lane == 63)
-                    wsum[tid >> 6] = x;
-            }
-            __syncthreads();
-            if (tid < 256) {
-                uint32_t base = 0;
-                for (int w = 0; w < (tid >> 6); ++w)
-                    base += wsum[w];
-                const uint32_t incl = base + x, excl = incl - c;
-                if (excl < remaining && remaining <= incl) {
-                    sh_digit = 255u - (uint32_t)tid;
-                    sh_remaining = remaining - excl;
-                }
-            }
-            __syncthreads();
-            prefix |= sh_digit << shift;
-            mask |= 255u << shift;
-            remaining = sh_remaining;
-            __syncthreads();
-        }
-    }
-    const uint32_t tau = prefix;  // key of the last admitted block; `remaining` of that key are taken
-
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int m = 0; m < KPT; ++m)
-        n_eq += (need > 0 && ((cand >> m) & 1u) && key[m] == tau) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t eq_rank = block_exclusive_scan(n_eq, wsum, tot);
-    uint64_t take = 0;  // bit m: selected
-#pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-        const bool c = (cand >> m) & 1u;
-        bool s = ((forced >> m) & 1u) || (need > 0 && c && key[m] > tau);
-        if (need > 0 && c && key[m] == tau) {
-            s = eq_rank < remaining;
-            ++eq_rank;
-        }
-        take |= (uint64_t)s << m;
-    }
-    uint32_t pos = block_exclusive_scan((uint32_t)__builtin_popcountll(take), wsum, tot);
-#pragma unroll
-    for (int m = 0; m < KPT; ++m)
-        if (((take >> m) & 1u) && pos < (uint32_t)k)
-            out[pos++] = tid * KPT + m;
-    tot = min(tot, (uint32_t)k);
-    for (int i = (int)tot + tid; i < k; i += kTopkThreads)
-        out[i] = -1;
-    if (tid == 0)
-        sel_count[row] = (int)tot;
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    const int n = topk_row<kTopkThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent,
+                                              sel_blocks + (size_t)row * k, sc);
+    if (threadIdx.x == 0)
+        sel_count[row] = n;
 }
 
 template <int KPT>

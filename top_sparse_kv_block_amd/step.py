@@ -78,7 +78,9 @@ class LayerBuffers:
         self.out = torch.empty(b, hq, d, dtype=torch.float32, device=device)
         self.lse = torch.empty(b, hq, dtype=torch.float32, device=device)
         self.splits = cfg.num_splits or B.sparse_decode_attention_splits(self.shape, k)
-        ws = B.sparse_decode_attention_workspace_bytes(self.shape, k, self.splits)
+        self.fused_splits = cfg.num_splits or B.sparse_kv_select_attend_splits(self.shape, k)
+        ws = max(B.sparse_decode_attention_workspace_bytes(self.shape, k, self.splits),
+                 B.sparse_decode_attention_workspace_bytes(self.shape, k, self.fused_splits))
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
 
     def reset(self):
@@ -113,15 +115,29 @@ class LayerBuffers:
                                   src_k, src_v, src_kind, self.out, self.lse, self.workspace, stream)
 
 
+    def select_attend(self, q, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None):
+        """Top-k, working-set update and attention (fetching misses) in one call."""
+        c = self.cfg
+        B.sparse_kv_select_attend(self.shape, self.scores, seq_lens, c.k_blocks, c.sink, c.recent, c.capacity,
+                                  self.sel_blocks, self.sel_count, self.slot_block, self.slot_stamp, self.clock,
+                                  self.sel_slot, self.sel_hit, self.miss_block, self.miss_slot, self.miss_count, q,
+                                  self.pool_k, self.pool_v, src_k, src_v, src_kind, c.softmax_scale,
+                                  self.fused_splits, self.out, self.lse, self.workspace, stream)
+
+
 def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE,
-                stream=None, fetch_on_attend=True):
+                stream=None, fetch_on_attend=True, fused=False):
     """Enqueue one full step: score, top-k, cache update, attention.
 
     The misses are copied into the pool either by the attention kernel while
     it reads them (fetch_on_attend, the default: one read and one write per
-    missed block) or by the cache update's own copy pass.
+    missed block) or by the cache update's own copy pass.  fused=True runs
+    stages 2-4 as the single select-attend call (same results).
     """
     buf.score(score_q, keys_or_meta, seq_lens, stream)
+    if fused:
+        buf.select_attend(q, seq_lens, src_k, src_v, src_kind, stream)
+        return
     buf.topk(seq_lens, stream)
     if fetch_on_attend:
         buf.cache_update(None, None, src_kind, stream)
