@@ -18,8 +18,10 @@ algorithmic HBM GB/s for the whole step, the roofline of the dominant
 kernel (the block-scoring scan) and a per-call breakdown, both timed with
 HIP events on the stream the kernels run on during a second pass of the
 same steps right after the timed region (event markers inside the timed
-region would add queue gaps to it), and the oracle's throughput on the
-host cores on a bounded sample.
+region would add queue gaps to it), the host-tier miss fetch over PCIe
+(``host_fetch``: full K/V in pinned host memory, host->device GB/s of the
+misses beside a plain pinned copy; never part of ``value``), and the
+oracle's throughput on the host cores on a bounded sample.
 """
 
 from __future__ import annotations
@@ -138,6 +140,106 @@ def cpu_baseline(w, data, seconds: float):
                 gbps=round(step_bytes(w, misses / steps)["total"] * steps / el / 1e9, 3))
 
 
+# ---------------------------------------------------------------- host tier
+def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
+    """Miss fetch over PCIe at the host-tier row shape (16 x 8 rows, 131072
+    tokens, k = 128 of 256 slots, given selections with ~50% cross-layer and
+    ~80% cross-step overlap).  One layer's full K and V (2 x 4 GiB) sit in
+    pinned, device-mapped host memory and every layer reads it (each layer
+    has its own working set and selections, so the transfers are the same
+    as with distinct host layers).  Step 0 (cold) is not timed.  Reports the
+    host->device rate of the misses for the separate gather and for fetch on
+    attend, beside a plain pinned hipMemcpyAsync of 256 MiB."""
+    import torch
+
+    from top_sparse_kv_block_amd import binding as B
+    from top_sparse_kv_block_amd import synth
+    from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
+
+    w = synth.WORKLOADS["host_tier_32l"].scaled(layers=layers, steps=steps)
+    t0 = time.time()
+    sels = torch.from_numpy(synth.gen_layer_selections(w)).cuda()
+    n_elem = w.rows * w.ctx * w.head_dim
+    nbytes = n_elem * w.elem_bytes
+    hk, hv = B.HostBuffer(nbytes), B.HostBuffer(nbytes)
+    try:
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        chunk = torch.randn(1 << 25, generator=g, device="cuda").to(torch.bfloat16)  # 64 MiB
+        for hb in (hk, hv):
+            ht = torch.from_numpy(hb.numpy(np.int16, (n_elem,))).view(torch.bfloat16)
+            for off in range(0, n_elem, chunk.numel()):
+                n = min(chunk.numel(), n_elem - off)
+                ht[off:off + n].copy_(chunk[:n])
+        lens = torch.full((w.batch,), w.ctx, dtype=torch.int32, device="cuda")
+        q = torch.randn(w.batch, w.n_q_heads, w.head_dim, generator=g, device="cuda").to(torch.bfloat16)
+        cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity)
+        bufs = [LayerBuffers(cfg) for _ in range(layers)]
+        for b in bufs:
+            b.sel_count.fill_(w.k_blocks)
+        torch.cuda.synchronize()
+        setup_s = time.time() - t0
+        blk2 = 2 * 16 * w.head_dim * w.elem_bytes  # K + V bytes of one block
+
+        def run_mode(mode):
+            for b in bufs:
+                b.reset()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers * steps)]
+            misses = torch.zeros(steps, layers, dtype=torch.int64, device="cuda")
+            for s in range(steps):
+                for l, b in enumerate(bufs):
+                    b.sel_blocks.copy_(sels[s, l])
+                    e = ev[s * layers + l]
+                    if mode == "gather":
+                        e[0].record()
+                        b.cache_update(hk.device_ptr, hv.device_ptr, B.SKV_SRC_HOST_MAPPED)
+                        e[1].record()
+                        b.attention(q, lens)
+                    else:
+                        b.cache_update(None, None)
+                        e[0].record()
+                        b.attention(q, lens, hk.device_ptr, hv.device_ptr, B.SKV_SRC_HOST_MAPPED)
+                        e[1].record()
+                    misses[s, l] = b.miss_count.sum()
+            torch.cuda.synchronize()
+            us = sum(e[0].elapsed_time(e[1]) for e in ev[layers:]) * 1e3
+            m = int(misses[1:].sum().item())
+            return m, us
+
+        m_g, us_g = run_mode("gather")
+        m_f, us_f = run_mode("fetch_on_attend")
+        # plain pinned copy, 256 MiB, for scale
+        n_c = 128 << 20
+        src = torch.from_numpy(hk.numpy(np.int16, (n_c,)))
+        dst = torch.empty(n_c, dtype=torch.int16, device="cuda")
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(4):
+            dst.copy_(src, non_blocking=True)
+        c1.record()
+        torch.cuda.synchronize()
+        memcpy_gbps = 4 * n_c * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        timed = (steps - 1) * layers
+        return {
+            "workload": w.name,
+            "rows": w.rows, "ctx": w.ctx, "k_blocks": w.k_blocks, "capacity_slots": w.capacity,
+            "layers_run": layers, "timed_layer_steps": timed,
+            "host_source": "one layer's K and V (8 GiB) in pinned mapped host memory, read by every layer",
+            "miss_blocks_per_layer": round(m_g / timed, 1),
+            "gather_h2d_gbps": round(m_g * blk2 / (us_g * 1e-6) / 1e9, 2),
+            "gather_us_per_layer": round(us_g / timed, 1),
+            "fetch_on_attend_h2d_gbps": round(m_f * blk2 / (us_f * 1e-6) / 1e9, 2),
+            "attention_with_fetch_us_per_layer": round(us_f / timed, 1),
+            "pinned_memcpy_h2d_gbps": round(memcpy_gbps, 2),
+            "setup_s": round(setup_s, 1),
+        }
+    finally:
+        torch.cuda.synchronize()
+        hk.free()
+        hv.free()
+
+
 # ---------------------------------------------------------------- GPU leg
 def run(args):
     import torch
@@ -148,7 +250,7 @@ def run(args):
 
     w = synth.WORKLOADS[args.workload]
     if w.scoring == "given":
-        raise SystemExit("the host-tier workload has no scoring stage; use bench_host_tier")
+        raise SystemExit("the host-tier workload has no scoring stage; its PCIe fetch is the host_fetch leg")
     nsteps = args.warmup + args.steps
     wq = w.scaled(steps=max(nsteps, 1))
     t_gen = time.time()
@@ -309,6 +411,8 @@ def run(args):
                      "traffic": traffic, "avg_launch_us": round(score_avg_s * 1e6, 2),
                      "bytes_per_launch": sbytes},
     }
+    if not args.no_host_fetch:
+        res["host_fetch"] = host_fetch_leg()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, data, args.cpu_seconds)
     return res
@@ -325,6 +429,7 @@ def main(argv=None):
     ap.add_argument("--four-calls", dest="fused", action="store_false",
                     help="run stages 2-4 as three calls instead of the fused select-attend call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-host-fetch", action="store_true", help="skip the host-tier PCIe fetch measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
