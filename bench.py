@@ -140,6 +140,100 @@ def cpu_baseline(w, data, seconds: float):
                 gbps=round(step_bytes(w, misses / steps)["total"] * steps / el / 1e9, 3))
 
 
+# ---------------------------------------------------------------- counters
+COPY_MIB = 512  # calibration copy: 512 MiB read + 512 MiB written
+
+
+def pmc_pass(args):
+    """Run under ``rocprofv3 --pmc <counter>``: one plain device copy of
+    COPY_MIB MiB (the calibration kernel, known bytes), then `steps` launches
+    of the scoring kernel on the benchmark workload.  Prints one line."""
+    import torch
+
+    from top_sparse_kv_block_amd import binding as B
+    from top_sparse_kv_block_amd import synth
+    from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
+
+    w = synth.WORKLOADS[args.workload]
+    data = synth.gen_workload(w.scaled(steps=max(args.steps, 1)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda() \
+        if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sq, dK, dlens = dev(data["score_q"]), dev(data["K"]), dev(data["seq_lens"])
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
+                     n_queries=w.n_score_queries)
+    buf = LayerBuffers(cfg, pool=False)
+    n = COPY_MIB << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    for t in range(args.steps):
+        B.sparse_kv_score(cfg.shape, B.SKV_SCORE_BLOCKMAX, sq[t], cfg.n_queries, dK, dlens, cfg.softmax_scale,
+                          buf.scores)
+    torch.cuda.synchronize()
+    print(f"pmc pass done: copy {COPY_MIB} MiB, {args.steps} scoring launches on {w.name}", flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir, workload):
+    """Counter-derived HBM traffic of the scoring kernel from two rocprofv3
+    --pmc runs of ``--pmc-pass`` (FETCH_SIZE, then WRITE_SIZE, KiB per
+    dispatch), each scaled by the factor that makes the calibration copy
+    read (write) exactly COPY_MIB MiB.  Writes the JSON the benchmark reads
+    and a short markdown summary under profiles/."""
+    from top_sparse_kv_block_amd import synth
+
+    w = synth.WORKLOADS[workload]
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
+        copy = [float(r["Counter_Value"]) for r in rows if "copybuffer" in r["Kernel_Name"].lower()]
+        score = [float(r["Counter_Value"]) for r in rows if "score_blockmax_kernel" in r["Kernel_Name"]]
+        if not copy or not score:
+            raise SystemExit(f"{counter}: copy dispatches {len(copy)}, scoring dispatches {len(score)}")
+        factor = (COPY_MIB << 20) / (max(copy) * 1024.0)
+        out[counter] = dict(copy_kib=max(copy), factor=factor, score_kib_avg=float(np.mean(score)),
+                            score_bytes=float(np.mean(score)) * 1024.0 * factor, dispatches=len(score))
+    total = out["FETCH_SIZE"]["score_bytes"] + out["WRITE_SIZE"]["score_bytes"]
+    res = dict(workload=w.name, kernel="score_blockmax_kernel", source_sha=_sources_sha(),
+               bytes_per_launch=int(round(total)), algorithmic_bytes_per_launch=score_launch_bytes(w),
+               counters=out)
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(res, f, indent=1)
+    md = TRAFFIC_FILE.replace(".json", ".md")
+    with open(md, "w") as f:
+        f.write(f"# HBM traffic of score_blockmax_kernel, {w.name} workload\n\n"
+                "Two counter runs (one MI355X; `$REPO` is the repository root), then the summary:\n\n```\n"
+                "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o f -- "
+                f"python3 $REPO/bench.py --pmc-pass --steps 4 --workload {w.name}\n"
+                "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o w -- "
+                f"python3 $REPO/bench.py --pmc-pass --steps 4 --workload {w.name}\n"
+                "python3 bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write\n```\n\n"
+                f"Calibration: a plain device copy of {COPY_MIB} MiB; each counter is scaled so that the copy "
+                f"reads (writes) exactly {COPY_MIB} MiB.\n\n"
+                "| counter | copy KiB | scale factor | scoring KiB / launch | scaled bytes / launch |\n"
+                "|---|---:|---:|---:|---:|\n")
+        for c, v in out.items():
+            f.write(f"| {c} | {v['copy_kib']:.0f} | {v['factor']:.4f} | {v['score_kib_avg']:.0f} | "
+                    f"{v['score_bytes']:.0f} |\n")
+        f.write(f"\nTraffic per launch: {total:.0f} B; algorithmic bytes per launch: {score_launch_bytes(w)} B "
+                f"(ratio {total / score_launch_bytes(w):.4f}). Kernel source sha {res['source_sha']}.\n")
+    return res
+
+
 # ---------------------------------------------------------------- host tier
 def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
     """Miss fetch over PCIe at the host-tier row shape (16 x 8 rows, 131072
@@ -356,11 +450,22 @@ def run(args):
     #     events -> its average launch duration (the roofline point);
     # (b) the same steps again with each call bracketed by events -> a
     #     per-call breakdown (each bracket also holds one event marker).
+    def score_pass():
+        for i in range(args.steps):
+            B.sparse_kv_score(shape, mode, sq_all[args.warmup + i], cfg.n_queries, keys_or_meta, dlens, scale,
+                              buf.scores, st)
+
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for i in range(args.steps):
-        B.sparse_kv_score(shape, mode, sq_all[args.warmup + i], cfg.n_queries, keys_or_meta, dlens, scale,
-                          buf.scores, st)
+    if graph is not None:  # replayed as a graph too, so launch gaps stay small
+        sgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sgraph):
+            score_pass()
+        torch.cuda.synchronize()
+        s0.record()
+        sgraph.replay()
+    else:
+        s0.record()
+        score_pass()
     s1.record()
     torch.cuda.synchronize()
     score_avg_s = s0.elapsed_time(s1) / 1e3 / args.steps
@@ -431,12 +536,25 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-fetch", action="store_true", help="skip the host-tier PCIe fetch measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="calibration copy + scoring launches only, to run under rocprofv3 --pmc")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs of --pmc-pass into the traffic file under profiles/")
     args = ap.parse_args(argv)
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(*args.traffic_summary, args.workload)))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the step runs on a single MI355X and has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         return 2
+    if args.pmc_pass:
+        pmc_pass(args)
+        return 0
+    if args.pmc_pass:
+        pmc_pass(args)
+        return 0
     res = run(args)
     print(json.dumps(res), flush=True)
     return 0
