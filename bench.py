@@ -496,7 +496,8 @@ def run(args):
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "ctx": w.ctx, "block": 16, "budget_tokens": w.budget,
                    "k_blocks": w.k_blocks, "capacity_slots": w.capacity, "scoring": w.scoring,
-                   "n_score_queries": w.n_score_queries, "attn_splits": buf.fused_splits if args.fused else buf.splits,
+                   "n_score_queries": w.n_score_queries,
+                   "attn_splits": buf.fused_splits if args.fused else buf.splits,
                    "parallelism": "single-gpu"},
         "hbm_gbps": round(bytes_total / elapsed / 1e9, 1),
         "hbm_frac": round(bytes_total / elapsed / 1e9 / HBM_PEAK_GBPS, 4),

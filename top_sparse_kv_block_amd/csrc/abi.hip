@@ -126,7 +126,7 @@ SKV_API int32_t sparse_kv_select_attend_splits(const skv_shape *shape, int32_t k
     Dims d;
     if (check_shape(shape, d) != SKV_OK || k_blocks < 1)
         return 0;
-    return skv::fused_auto_splits(d.rows(), k_blocks);
+    return skv::fused_auto_splits(d, k_blocks);
 }
 
 SKV_API size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits) {
@@ -202,7 +202,7 @@ SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *
     }
     if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
         return SKV_ERR_SHAPE;
-    const int splits = num_splits == 0 ? skv::fused_auto_splits(d.rows(), k_blocks) : num_splits;
+    const int splits = num_splits == 0 ? skv::fused_auto_splits(d, k_blocks) : num_splits;
     const size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return SKV_ERR_WORKSPACE;

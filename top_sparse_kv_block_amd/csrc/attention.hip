@@ -88,8 +88,12 @@ struct AttnRow {
     float *lse;   // [G] or NULL (splits == 1)
 };
 
+template <int D, int GMAX> __device__ void combine_waves(const AttnRow &a, AttnSmem<D, GMAX> &S);
+
+// float32 storage: dot products and the value accumulation on the vector
+// ALU; every lane owns a 16-byte slice of the block's tokens.
 template <typename E, int D, int GMAX, int DEPTH>
-__device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+__device__ __forceinline__ void attn_body_valu(const AttnRow &a, AttnSmem<D, GMAX> &S) {
     constexpr int LPT = D * E::bytes / 16;
     constexpr int TPL = 64 / LPT;
     constexpr int LPB = 16 / TPL;
@@ -255,6 +259,14 @@ __device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S
             }
         }
     }
+    combine_waves<D, GMAX>(a, S);
+}
+
+// Waves' partials (S.sm[w][g] = unnormalised output, max, sum) -> the
+// workgroup's output (one split) or its partial for the merge.
+template <int D, int GMAX> __device__ void combine_waves(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+    const int tid = threadIdx.x;
+    const int G = a.G;
     __syncthreads();
     // per head: max over waves, then sum and output rescaled to it
     const int W = G * (D + 2);
@@ -294,6 +306,194 @@ __device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S
         if (a.lse && tid < G)
             a.lse[tid] = S.shL[tid] > 0.0f ? S.shM[tid] * kLn2 + logf(S.shL[tid]) : -__builtin_inff();
     }
+}
+
+// bf16 storage: q.k of a whole block on the matrix cores, the value
+// accumulation on the vector ALU.
+//
+// One v_mfma_f32_16x16x32_bf16 per 32 dims gives the block's 16 x 16 tile
+// S[token][head] (heads beyond G are zero columns): the block's keys are the
+// A operand (lane l holds token l%16, dims 32c + 8(l/16) .. +8, i.e. 16
+// contiguous bytes) and the group's q the B operand (head l%16, same dims).
+// Lane l then holds S for tokens 4(l/16) .. +4 of head l%16, so per block
+// the max over tokens is 3 max + one cross-row max and each lane does 4
+// exponentials for all heads at once.  V is read as rows: lane l holds
+// dims (l%16)*D/16 .. of tokens 4(l/16) .. +4, and p[token][head g] reaches
+// it by a row broadcast of lane g.  The lane's output is summed over its
+// row's tokens; the 4 rows are added at the end.
+template <int D, int GMAX, int DEPTH>
+__device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+    constexpr int KCH = D / 32;   // 32-dim chunks of the contraction
+    constexpr int VB = D / 8;     // bytes of a token's V per lane
+    constexpr int EPLV = D / 16;  // V elements per lane per token
+    constexpr int TB = D * 2;     // bytes of one token
+    constexpr size_t kBlockBytes = (size_t)16 * TB;
+    using VT = typename std::conditional<VB == 16, u32x4, u32x2>::type;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, rsub = lane >> 4;
+    const int G = a.G;
+
+    u32x4 qf[KCH];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+        qf[c] = col < G ? load16(a.q + ((size_t)col * D + c * 32 + rsub * 8) * 2) : u32x4{0, 0, 0, 0};
+    const size_t k_off = (size_t)col * TB + rsub * 16;       // + 64 c
+    const size_t v_off = (size_t)(4 * rsub) * TB + col * VB;  // + TB i
+
+    float m = -__builtin_inff(), lsum = 0.0f, acc[GMAX][EPLV];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+        for (int e = 0; e < EPLV; ++e)
+            acc[g][e] = 0.0f;
+
+    auto describe = [&](int i, int &blk, int &s, int &nv, bool &fetch) -> bool {
+        if (i >= a.i1)
+            return false;
+        blk = a.blk[i];
+        s = a.slot[i];
+        if (blk < 0 || s < 0 || s >= a.C)
+            return false;
+        fetch = a.src_k != nullptr && blk < a.NB && a.hit[i] == 0;
+        nv = min(max(a.len - blk * 16, 0), 16);
+        return nv > 0 || fetch;
+    };
+    auto load_block = [&](int blk, int s, bool fetch, u32x4 *kf, VT *vf) {
+        const uint8_t *rk = fetch ? a.src_k + (size_t)blk * kBlockBytes : a.pool_k + (size_t)s * kBlockBytes;
+        const uint8_t *rv = fetch ? a.src_v + (size_t)blk * kBlockBytes : a.pool_v + (size_t)s * kBlockBytes;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            kf[c] = fetch ? load_nt(rk + k_off + c * 64) : load16(rk + k_off + c * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const VT *pv = reinterpret_cast<const VT *>(rv + v_off + i * TB);
+            vf[i] = fetch ? __builtin_nontemporal_load(pv) : *pv;
+        }
+    };
+    auto attend_block = [&](int s, int nv, bool fetch, const u32x4 *kf, const VT *vf) {
+        if (fetch) {
+            uint8_t *pk = a.pool_k + (size_t)s * kBlockBytes;
+            uint8_t *pv = a.pool_v + (size_t)s * kBlockBytes;
+#pragma unroll
+            for (int c = 0; c < KCH; ++c)
+                store16(pk + k_off + c * 64, kf[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<VT *>(pv + v_off + i * TB) = vf[i];
+        }
+        if (nv == 0)
+            return;
+        f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[c]),
+                                                          __builtin_bit_cast(bf16x8, qf[c]), st, 0, 0, 0);
+        float z[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            z[i] = st[i] * a.scale_log2;
+        if (nv < 16) {  // partial last block: drop the tokens past the end
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * rsub + i >= nv)
+                    z[i] = -__builtin_inff();
+        }
+        const float bm = rows_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+        const float mn = fmaxf(m, bm);  // finite: token 0 of the block is valid
+        const float alpha = exp2_fast(m - mn);
+        m = mn;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            p[i] = exp2_fast(z[i] - mn);
+        lsum = __builtin_fmaf(lsum, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+        float v[4][EPLV];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < EPLV; ++e)
+                v[i][e] = (e & 1) ? bf16_hi(vf[i][e >> 1]) : bf16_lo(vf[i][e >> 1]);
+        StaticFor<0, GMAX>::run([&](auto gc) {
+            constexpr int g = decltype(gc)::value;
+            const float ag = row_bcast<g>(alpha);
+#pragma unroll
+            for (int e = 0; e < EPLV; ++e)
+                acc[g][e] *= ag;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pg = row_bcast<g>(p[i]);
+#pragma unroll
+                for (int e = 0; e < EPLV; ++e)
+                    acc[g][e] = __builtin_fmaf(pg, v[i][e], acc[g][e]);
+            }
+        });
+    };
+
+    if constexpr (DEPTH == 2) {
+        int blk0, s0, nv0, blk1, s1, nv1;
+        bool f0, f1;
+        u32x4 k0[KCH], k1[KCH];
+        VT v0[4], v1[4];
+        int i = a.i0 + wave;
+        bool h0 = describe(i, blk0, s0, nv0, f0);
+        if (h0)
+            load_block(blk0, s0, f0, k0, v0);
+        for (; i < a.i1; i += 2 * kAttnWaves) {
+            const bool h1 = describe(i + kAttnWaves, blk1, s1, nv1, f1);
+            if (h1)
+                load_block(blk1, s1, f1, k1, v1);
+            if (h0)
+                attend_block(s0, nv0, f0, k0, v0);
+            h0 = describe(i + 2 * kAttnWaves, blk0, s0, nv0, f0);
+            if (h0)
+                load_block(blk0, s0, f0, k0, v0);
+            if (h1)
+                attend_block(s1, nv1, f1, k1, v1);
+        }
+    } else {
+        static_assert(DEPTH == 1, "one or two blocks in flight");
+        for (int i = a.i0 + wave; i < a.i1; i += kAttnWaves) {
+            int blk, s, nv;
+            bool f;
+            u32x4 kf[KCH];
+            VT vf[4];
+            if (describe(i, blk, s, nv, f)) {
+                load_block(blk, s, f, kf, vf);
+                attend_block(s, nv, f, kf, vf);
+            }
+        }
+    }
+
+    // the wave's totals: add the 4 rows (token groups); m is per column
+    lsum = rows_sum(lsum);
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+        for (int e = 0; e < EPLV; ++e)
+            acc[g][e] = rows_sum(acc[g][e]);
+    if (rsub == 0) {
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+            if (g >= G)
+                continue;
+#pragma unroll
+            for (int e = 0; e < EPLV; ++e)
+                S.sm[wave][g][col * EPLV + e] = acc[g][e];
+        }
+        if (col < G) {
+            S.sm[wave][col][D] = m;
+            S.sm[wave][col][D + 1] = lsum;
+        }
+    }
+    combine_waves<D, GMAX>(a, S);
+}
+
+template <typename E, int D, int GMAX, int DEPTH>
+__device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+    if constexpr (E::bytes == 2)
+        attn_body_mfma<D, GMAX, DEPTH>(a, S);
+    else
+        attn_body_valu<E, D, GMAX, DEPTH>(a, S);
 }
 
 template <typename E, int D>
@@ -344,17 +544,29 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_waves(GMAX)) void attn_kerne
     attn_body<E, D, GMAX, 1>(a, S);
 }
 
+// Waves per SIMD of the fused kernel: 4 (two workgroups per CU, <= 128
+// registers) where the top-k keys and the head state are small enough,
+// else 2.  The host side (fused_waves_per_simd) applies the same rule.
+template <typename E, int D, int GMAX, int KPT> constexpr int fused_min_waves() {
+    return (E::bytes == 2 && GMAX <= 4 && KPT <= 4) ? 4 : 2;
+}
+
 // Blocks of K and V a wave of the fused kernel holds at once (see
-// attn_body): two if they fit next to the per-head state in about 216 of
-// its 256 registers (2 waves per SIMD).
+// attn_body): at 4 waves per SIMD one; else two if they fit next to the
+// per-head state in about 216 of its 256 registers.
 template <typename E, int D, int GMAX> constexpr int fused_depth() {
-    constexpr int lpb = D * E::bytes / 64;  // 16-byte loads per lane per block, K or V
-    constexpr int fixed = GMAX * (4 + E::EPL + 2 + lpb);
-    return fixed + 2 * 8 * lpb <= 216 ? 2 : 1;
+    if constexpr (E::bytes == 2) {  // matrix-core body: q, accumulators, K + V of a block
+        constexpr int fixed = D / 8 + GMAX * D / 16 + 24;
+        return fixed + 2 * (D / 4) <= 216 ? 2 : 1;
+    } else {
+        constexpr int lpb = D * E::bytes / 64;  // 16-byte loads per lane per block, K or V
+        constexpr int fixed = GMAX * (4 + E::EPL + 2 + lpb);
+        return fixed + 2 * 8 * lpb <= 216 ? 2 : 1;
+    }
 }
 
 template <typename E, int D, int GMAX, int KPT>
-__global__ __launch_bounds__(kAttnThreads, 2) void select_attend_kernel(
+__global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>())) void select_attend_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int k, int sink, int recent, int C,
     int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count, const int32_t *__restrict__ slot_block,
     const uint32_t *__restrict__ slot_stamp, int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit,
@@ -398,7 +610,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void select_attend_kernel(
     a.len = len;
     a.i0 = split * per_split;
     a.i1 = bad ? a.i0 : min(a.i0 + per_split, nn);  // an invalid row attends nothing
-    attn_body<E, D, GMAX, fused_depth<E, D, GMAX>()>(a, S);
+    constexpr int depth = fused_min_waves<E, D, GMAX, KPT>() == 4 ? 1 : fused_depth<E, D, GMAX>();
+    attn_body<E, D, GMAX, depth>(a, S);
 }
 
 // One workgroup per row: merge the row's G heads over the splits (when
@@ -481,10 +694,16 @@ int attention_auto_splits(int rows, int k) {
 }
 
 // The fused call redoes the row's top-k and plan in every workgroup, so it
-// prefers about one workgroup per CU in total (all resident at once), each
-// wave streaming several blocks with the next one prefetched.
-int fused_auto_splits(int rows, int k) {
-    int s = (256 + rows - 1) / rows;
+// prefers as many workgroups as are resident at once (one or two per CU,
+// see fused_min_waves), each wave streaming several blocks.
+int fused_waves_per_simd(const Dims &d) {
+    return (d.dtype == 1 && d.G() <= 4 && d.NB <= kAttnThreads * 4) ? 4 : 2;
+}
+
+int fused_auto_splits(const Dims &d, int k) {
+    const int rows = d.rows();
+    const int resident = 256 * fused_waves_per_simd(d) / 2;  // workgroups resident on 256 CUs
+    int s = (resident + rows - 1) / rows;
     const int one_per_wave = (k + kAttnWaves - 1) / kAttnWaves;
     if (s > one_per_wave)
         s = one_per_wave;

@@ -6,9 +6,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace skv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -143,6 +147,25 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     v += dpp_zero<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
     return v;
 }
+
+// Every lane of a 16-lane row gets lane N of that row (DPP row_newbcast).
+template <int N> __device__ __forceinline__ float row_bcast(float v) {
+    static_assert(N >= 0 && N < 16, "lane within a row");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf,
+                                                                 false));
+}
+
+// Calls f(std::integral_constant<int, i>) for i = I .. N-1 (compile-time lane
+// or head indices for DPP controls).
+template <int I, int N> struct StaticFor {
+    template <typename F> __device__ __forceinline__ static void run(F &&f) {
+        f(std::integral_constant<int, I>{});
+        StaticFor<I + 1, N>::run(f);
+    }
+};
+template <int N> struct StaticFor<N, N> {
+    template <typename F> __device__ __forceinline__ static void run(F &&) {}
+};
 
 // fast exp2 for arguments <= 0 (v_exp_f32; results below the smallest
 // normal flush to zero, which is what the softmax wants)

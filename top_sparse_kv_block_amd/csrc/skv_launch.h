@@ -75,7 +75,7 @@ constexpr int kMaxSplits = 128;
 constexpr int kMaxFusedBlocks = 8192;  // NB limit of the fused select -> attend call
 
 int attention_auto_splits(int rows, int k);
-int fused_auto_splits(int rows, int k);
+int fused_auto_splits(const Dims &d, int k);
 size_t attention_ws_bytes(int rows, int G, int D, int splits);
 
 }  // namespace skv

@@ -145,3 +145,4 @@ def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, sr
     else:
         buf.cache_update(src_k, src_v, src_kind, stream)
         buf.attention(q, seq_lens, stream=stream)
+
