@@ -83,6 +83,11 @@ def score_launch_bytes(w) -> int:
         w.batch * w.n_score_queries * w.n_q_heads * w.head_dim * w.elem_bytes
 
 
+def _score_kernel_name(w) -> str:
+    """The exact-scoring kernel the library runs for this workload's dtype."""
+    return "score_blockmax_mfma_kernel" if w.dtype == "bf16" else "score_blockmax_kernel"
+
+
 def _sources_sha() -> str:
     h = hashlib.sha256()
     for p in SCORE_SOURCES:
@@ -200,14 +205,14 @@ def traffic_summary(fetch_dir, write_dir, workload):
     for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
         copy = [float(r["Counter_Value"]) for r in rows if "copybuffer" in r["Kernel_Name"].lower()]
-        score = [float(r["Counter_Value"]) for r in rows if "score_blockmax_kernel" in r["Kernel_Name"]]
+        score = [float(r["Counter_Value"]) for r in rows if "score_blockmax" in r["Kernel_Name"]]
         if not copy or not score:
             raise SystemExit(f"{counter}: copy dispatches {len(copy)}, scoring dispatches {len(score)}")
         factor = (COPY_MIB << 20) / (max(copy) * 1024.0)
         out[counter] = dict(copy_kib=max(copy), factor=factor, score_kib_avg=float(np.mean(score)),
                             score_bytes=float(np.mean(score)) * 1024.0 * factor, dispatches=len(score))
     total = out["FETCH_SIZE"]["score_bytes"] + out["WRITE_SIZE"]["score_bytes"]
-    res = dict(workload=w.name, kernel="score_blockmax_kernel", source_sha=_sources_sha(),
+    res = dict(workload=w.name, kernel=_score_kernel_name(w), source_sha=_sources_sha(),
                bytes_per_launch=int(round(total)), algorithmic_bytes_per_launch=score_launch_bytes(w),
                counters=out)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -215,7 +220,7 @@ def traffic_summary(fetch_dir, write_dir, workload):
         json.dump(res, f, indent=1)
     md = TRAFFIC_FILE.replace(".json", ".md")
     with open(md, "w") as f:
-        f.write(f"# HBM traffic of score_blockmax_kernel, {w.name} workload\n\n"
+        f.write(f"# HBM traffic of {_score_kernel_name(w)}, {w.name} workload\n\n"
                 "Two counter runs (one MI355X; `$REPO` is the repository root), then the summary:\n\n```\n"
                 "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o f -- "
                 f"python3 $REPO/bench.py --pmc-pass --steps 4 --workload {w.name}\n"
@@ -510,7 +515,7 @@ def run(args):
                       "select_update_attend": round(float(stage[:, 1].mean()), 2)} if args.fused else
                      {name: round(float(v), 2) for name, v in
                       zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))}),
-        "roofline": {"bound": "hbm", "kernel": "score_blockmax_kernel" if mode == B.SKV_SCORE_BLOCKMAX
+        "roofline": {"bound": "hbm", "kernel": _score_kernel_name(w) if mode == B.SKV_SCORE_BLOCKMAX
                      else "score_quest_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -617,12 +617,19 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
 // One workgroup per row: merge the row's G heads over the splits (when
 // splits > 1), then commit the row's working-set plan (when commit is set):
 // every selected slot gets its block and the new stamp, the clock advances.
+// The kernel is a chain of dependent steps, so every global read it needs
+// (commit operands, the clock advance, and the row's partials, staged in
+// LDS when they fit) is issued before the first barrier.
+constexpr int kMergeStage = 12288;  // floats of partials staged in LDS (48 KiB)
+constexpr int kCommitPerThread = kMaxK / kAttnThreads;
+
 __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
     const float *__restrict__ part, int Hq, int Hkv, int D, int splits, float *__restrict__ out,
     float *__restrict__ lse, int commit, int k, int C, const int32_t *__restrict__ sel_blocks,
     const int32_t *__restrict__ sel_count, const int32_t *__restrict__ sel_slot,
     const int32_t *__restrict__ miss_count, int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp,
     uint32_t *__restrict__ clock) {
+    __shared__ float stage[kMergeStage];
     __shared__ float sw[kMaxGroup][kMaxSplits];  // m_s, then the weight exp2(m_s - M)
     __shared__ float sl[kMaxGroup][kMaxSplits];
     __shared__ float shM[kMaxGroup], shL[kMaxGroup];
@@ -630,16 +637,35 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
     const int row = blockIdx.x, tid = threadIdx.x;
     const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
-    const size_t W = (size_t)G * (D + 2);
+    const int W = G * (D + 2);
+    const float *p = part + (size_t)row * splits * W;
+    const bool staged = splits > 1 && splits * W <= kMergeStage;
+
     const bool do_commit = commit && miss_count[row] >= 0;  // uniform over the workgroup
-    if (do_commit && tid == 0)
-        sNow = atomicAdd(&clock[row], 1u) + 1u;
+    int n = 0, c_slot[kCommitPerThread], c_blk[kCommitPerThread];
+    if (do_commit) {
+        n = min(max(sel_count[row], 0), k);
+#pragma unroll
+        for (int u = 0; u < kCommitPerThread; ++u) {
+            const int i = tid + u * kAttnThreads;
+            c_slot[u] = i < n ? sel_slot[(size_t)row * k + i] : -1;
+            c_blk[u] = i < n ? sel_blocks[(size_t)row * k + i] : -1;
+        }
+        if (tid == 0)
+            sNow = atomicAdd(&clock[row], 1u) + 1u;
+    }
+    if (staged) {
+#pragma unroll 8
+        for (int t = tid; t < splits * W; t += kAttnThreads)
+            stage[t] = p[t];
+    }
+    const float *src = staged ? stage : p;  // LDS or global, same layout [splits][G][D + 2]
     if (splits > 1) {
-        const float *p = part + (size_t)row * splits * W;
+        __syncthreads();
         for (int t = tid; t < splits * G; t += kAttnThreads) {
             const int s = t / G, g = t - s * G;
-            sw[g][s] = p[s * W + g * (D + 2) + D];
-            sl[g][s] = p[s * W + g * (D + 2) + D + 1];
+            sw[g][s] = src[s * W + g * (D + 2) + D];
+            sl[g][s] = src[s * W + g * (D + 2) + D + 1];
         }
         __syncthreads();
         if (tid < G) {
@@ -666,7 +692,7 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
             float a = 0.0f;
 #pragma unroll 8
             for (int s = 0; s < splits; ++s)
-                a = __builtin_fmaf(sw[g][s], p[s * W + g * (D + 2) + d], a);
+                a = __builtin_fmaf(sw[g][s], src[s * W + g * (D + 2) + d], a);
             o[idx] = L > 0.0f ? a / L : 0.0f;
         }
         if (lse && tid < G)
@@ -676,11 +702,11 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
     if (do_commit) {
         __syncthreads();
         const uint32_t now = sNow;
-        const int n = min(max(sel_count[row], 0), k);
-        for (int i = tid; i < n; i += kAttnThreads) {
-            const int s = sel_slot[(size_t)row * k + i];
+#pragma unroll
+        for (int u = 0; u < kCommitPerThread; ++u) {
+            const int s = c_slot[u];
             if (s >= 0 && s < C) {
-                slot_block[(size_t)row * C + s] = sel_blocks[(size_t)row * k + i];
+                slot_block[(size_t)row * C + s] = c_blk[u];
                 slot_stamp[(size_t)row * C + s] = now;
             }
         }

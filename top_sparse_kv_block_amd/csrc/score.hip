@@ -9,7 +9,9 @@
 //
 // Layout on the chip.  A (b, kv-head) row of keys is T*D contiguous
 // elements; one 16-token block is 16*D*e contiguous bytes (4 KiB for bf16,
-// D=128).  A wave reads a block with fully coalesced 16-byte lane loads:
+// D=128).  bf16 keys are scored on the matrix cores (see the MFMA kernel
+// below); float32 keys on the vector ALU as follows.
+// A wave reads a block with fully coalesced 16-byte lane loads:
 // LPT = D*e/16 lanes share a token (each holds EPL consecutive elements),
 // TPL = 64/LPT tokens per wave load, 16/TPL loads per block.  Each lane
 // keeps the matching 16-byte slice of every query row in registers, forms
@@ -95,6 +97,98 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uin
                 m = fmaxf(m, best);
         }
         m = groups_max<LPT>(m);
+        if (lane == 0)
+            srow[n] = m * scale;
+    }
+}
+
+// bf16 block max on the matrix cores, for many query rows (lookahead
+// drafts x GQA heads).  One v_mfma_f32_16x16x32_bf16 per 32 dims and per
+// tile of 16 query rows gives S[token][query] for a whole block.  The MFMA
+// wants each lane to hold 16 contiguous bytes of token l%16 (the A operand:
+// dims 32c + 8(l/16) .. +8), which as a global load would read only 64
+// contiguous bytes per token per instruction; so the wave reads the block
+// with the fully coalesced lane layout of the vector kernel (4 tokens x
+// 256 bytes per instruction), writes it to its own LDS tile (rows padded by
+// 16 bytes, so both access patterns are free of bank conflicts) and reads
+// the A operand back from there.  The query rows are the B operand (row
+// 16t + l%16, same dims).  Lane l then holds S for tokens 4(l/16) .. +4 of
+// query row 16t + l%16; the block's score is the max over the valid tokens
+// and real query rows, one wave reduction.
+template <int D, int NT>
+__global__ __launch_bounds__(kScoreThreads) void score_blockmax_mfma_kernel(const uint8_t *__restrict__ q,
+                                                                  const uint8_t *__restrict__ keys,
+                                                                  const int32_t *__restrict__ seq_lens,
+                                                                  float *__restrict__ scores, int Hq, int Hkv,
+                                                                  int NQ, int T, int NB, float scale) {
+    constexpr int KCH = D / 32;
+    constexpr int TB = D * 2;          // bytes of one token
+    constexpr int ROW = TB + 16;       // padded LDS row
+    constexpr int LPT = TB / 16;       // lanes per token in the coalesced layout
+    constexpr int TPL = 64 / LPT;      // tokens per load instruction
+    constexpr int LPB = 16 / TPL;      // load instructions per block
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kScoreWaves][16 * ROW];
+    const int row = blockIdx.y;
+    const int b = row / Hkv, j = row - b * Hkv;
+    const int G = Hq / Hkv;
+    const int R = NQ * G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, rsub = lane >> 4;
+    const int sub = lane % LPT, tg = lane / LPT;
+    uint8_t *my = tile[wave];
+
+    u32x4 qf[NT][KCH];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int r = 16 * t + col;
+        const int rq = r / G, g = r - rq * G;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            qf[t][c] = r < R ? load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + c * 32 + rsub * 8) * 2)
+                             : u32x4{0, 0, 0, 0};
+    }
+    const int len = min(max(seq_lens[b], 0), T);
+    const int nvalid = nb_of(len);
+    const uint8_t *krow = keys + (size_t)row * T * TB;
+    float *srow = scores + (size_t)row * NB;
+    const int n0 = blockIdx.x * (kScoreWaves * kScoreBlocksPerWave);
+    const int n1 = min(n0 + kScoreWaves * kScoreBlocksPerWave, NB);
+
+    for (int n = n0 + wave; n < n1; n += kScoreWaves) {
+        if (n >= nvalid) {
+            if (lane == 0)
+                srow[n] = -__builtin_inff();
+            continue;
+        }
+        u32x4 kv[LPB];
+#pragma unroll
+        for (int i = 0; i < LPB; ++i)
+            kv[i] = load_nt(krow + (size_t)(n * 16 + i * TPL + tg) * TB + sub * 16);
+#pragma unroll
+        for (int i = 0; i < LPB; ++i)
+            *reinterpret_cast<u32x4 *>(my + (i * TPL + tg) * ROW + sub * 16) = kv[i];
+        __builtin_amdgcn_wave_barrier();
+        u32x4 kf[KCH];
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            kf[c] = *reinterpret_cast<const u32x4 *>(my + col * ROW + c * 64 + rsub * 16);
+        __builtin_amdgcn_wave_barrier();  // the tile is rewritten by the next block
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int c = 0; c < KCH; ++c)
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[c]),
+                                                              __builtin_bit_cast(bf16x8, qf[t][c]), st, 0, 0, 0);
+            if (16 * t + col < R) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n * 16 + 4 * rsub + i < len)
+                        m = fmaxf(m, st[i]);
+            }
+        }
+        m = wave_max(m);
         if (lane == 0)
             srow[n] = m * scale;
     }
@@ -261,17 +355,36 @@ static hipError_t blockmax_t(const Dims &d, const void *q, int nq, const void *k
     return hipGetLastError();
 }
 
+template <int D, int NT>
+static hipError_t blockmax_mfma_t(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
+                                  float scale, float *scores, hipStream_t st) {
+    const int per_wg = kScoreWaves * kScoreBlocksPerWave;
+    dim3 grid((d.NB + per_wg - 1) / per_wg, d.rows());
+    hipLaunchKernelGGL((score_blockmax_mfma_kernel<D, NT>), grid, dim3(kScoreThreads), 0, st, (const uint8_t *)q,
+                       (const uint8_t *)keys, lens, scores, d.Hq, d.Hkv, nq, d.T, d.NB, scale);
+    return hipGetLastError();
+}
+
+// bf16 keys always take the matrix-core kernel: measured on the 32K
+// workload (4 query rows) it streams faster than the vector kernel (77 us
+// against 81 us per launch), and with 32 query rows (1M context, 4 drafts)
+// the vector kernel is ALU-bound (512 us against 336 us).
 template <typename E, int D>
 static hipError_t blockmax_r(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
                              float scale, float *scores, hipStream_t st) {
     const int R = nq * d.G();
-    if (R <= 4)
-        return blockmax_t<E, D, 4>(d, q, nq, keys, lens, scale, scores, st);
-    if (R <= 8)
-        return blockmax_t<E, D, 8>(d, q, nq, keys, lens, scale, scores, st);
-    if (R <= 16)
-        return blockmax_t<E, D, 16>(d, q, nq, keys, lens, scale, scores, st);
-    return blockmax_t<E, D, 32>(d, q, nq, keys, lens, scale, scores, st);
+    if constexpr (E::bytes == 2) {
+        return R <= 16 ? blockmax_mfma_t<D, 1>(d, q, nq, keys, lens, scale, scores, st)
+                       : blockmax_mfma_t<D, 2>(d, q, nq, keys, lens, scale, scores, st);
+    } else {
+        if (R <= 4)
+            return blockmax_t<E, D, 4>(d, q, nq, keys, lens, scale, scores, st);
+        if (R <= 8)
+            return blockmax_t<E, D, 8>(d, q, nq, keys, lens, scale, scores, st);
+        if (R <= 16)
+            return blockmax_t<E, D, 16>(d, q, nq, keys, lens, scale, scores, st);
+        return blockmax_t<E, D, 32>(d, q, nq, keys, lens, scale, scores, st);
+    }
 }
 
 hipError_t launch_score_blockmax(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,

@@ -39,10 +39,33 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 struct TopkScratch {
-    uint32_t hist[256];
+    uint32_t hist[2][256];  // passes alternate buffers, so clearing needs no barrier of its own
     uint32_t wsum[16];
-    uint32_t digit, remaining;
+    uint32_t digit, remaining, n_tau;
 };
+
+// Wave 0 finds the digit bin holding the `remaining`-th largest key of the
+// pass: lane l scans bins 255-4l .. 252-4l, a DPP scan adds the lanes.
+// Writes the digit, the rank left inside its bin and the bin's count.
+__device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remaining, TopkScratch &sc) {
+    const int lane = threadIdx.x & 63;
+    uint32_t c[4], t = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        c[u] = hist[255 - 4 * lane - u];
+        t += c[u];
+    }
+    uint32_t run = wave_incl_scan(t) - t;  // keys in higher bins
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        if (run < remaining && remaining <= run + c[u]) {
+            sc.digit = 255u - (uint32_t)(4 * lane + u);
+            sc.remaining = remaining - run;
+            sc.n_tau = c[u];
+        }
+        run += c[u];
+    }
+}
 
 // Per-row selection under the budget (sink + recent blocks forced, the rest
 // by (score desc, id asc)); writes the ascending ids to out[0, count) and -1
@@ -82,14 +105,15 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
         }
     }
     uint32_t prefix = 0, mask = 0;
-    uint32_t remaining = (uint32_t)max(need, 0);
+    uint32_t remaining = (uint32_t)max(need, 0), n_tau = 0;
     if (need > 0) {
+        if (tid < 256)
+            sc.hist[0][tid] = 0;
+        __syncthreads();
 #pragma unroll 1
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-            if (tid < 256)
-                sc.hist[tid] = 0;
-            __syncthreads();
+            uint32_t *hist = sc.hist[pass & 1];
             if (pass == 0) {
                 // the leading byte (sign and high exponent bits) is shared by
                 // nearly every score of a row: count each distinct digit of
@@ -106,7 +130,7 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
                         const bool same = pending && dg == dl;
                         const uint64_t grp = __builtin_amdgcn_ballot_w64(same);
                         if (lane == leader)
-                            atomicAdd(&sc.hist[dl], (uint32_t)__builtin_popcountll(grp));
+                            atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(grp));
                         pending = pending && !same;
                         act &= ~grp;
                     }
@@ -115,53 +139,49 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
 #pragma unroll
                 for (int m = 0; m < KPT; ++m)
                     if (((cand >> m) & 1u) && (key[m] & mask) == prefix)
-                        atomicAdd(&sc.hist[(key[m] >> shift) & 255u], 1u);
+                        atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
             }
+            if (tid < 256)
+                sc.hist[(pass + 1) & 1][tid] = 0;  // last read by the previous pass's pick
             __syncthreads();
-            // inclusive scan over the bins from the top digit down (waves 0-3)
-            uint32_t c = 0, x = 0;
-            if (tid < 256) {
-                c = sc.hist[255 - tid];
-                x = wave_incl_scan(c);
-                if ((tid & 63) == 63)
-                    sc.wsum[tid >> 6] = x;
-            }
-            __syncthreads();
-            if (tid < 256) {
-                uint32_t base = 0;
-                for (int w = 0; w < (tid >> 6); ++w)
-                    base += sc.wsum[w];
-                const uint32_t incl = base + x, excl = incl - c;
-                if (excl < remaining && remaining <= incl) {
-                    sc.digit = 255u - (uint32_t)tid;
-                    sc.remaining = remaining - excl;
-                }
-            }
+            if (tid < 64)
+                pick_digit(hist, remaining, sc);
             __syncthreads();
             prefix |= sc.digit << shift;
             mask |= 255u << shift;
             remaining = sc.remaining;
-            __syncthreads();
+            n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
         }
     }
     const uint32_t tau = prefix;
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int m = 0; m < KPT; ++m)
-        n_eq += (need > 0 && ((cand >> m) & 1u) && key[m] == tau) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t eq_rank = wg_exclusive_scan<THREADS, uint32_t>(n_eq, sc.wsum, tot);
     uint64_t take = 0;
+    if (need > 0 && n_tau > remaining) {
+        // exact ties at the threshold: the lowest ids among them are taken
+        uint32_t n_eq = 0;
 #pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-        const bool c = (cand >> m) & 1u;
-        bool s = ((forced >> m) & 1u) || (need > 0 && c && key[m] > tau);
-        if (need > 0 && c && key[m] == tau) {
-            s = eq_rank < remaining;
-            ++eq_rank;
+        for (int m = 0; m < KPT; ++m)
+            n_eq += (((cand >> m) & 1u) && key[m] == tau) ? 1u : 0u;
+        uint32_t tot;
+        uint32_t eq_rank = wg_exclusive_scan<THREADS, uint32_t>(n_eq, sc.wsum, tot);
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+            const bool c = (cand >> m) & 1u;
+            bool s = ((forced >> m) & 1u) || (c && key[m] > tau);
+            if (c && key[m] == tau) {
+                s = eq_rank < remaining;
+                ++eq_rank;
+            }
+            take |= (uint64_t)s << m;
         }
-        take |= (uint64_t)s << m;
+    } else {
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+            const bool c = (cand >> m) & 1u;
+            const bool s = ((forced >> m) & 1u) || (need > 0 && c && key[m] >= tau);
+            take |= (uint64_t)s << m;
+        }
     }
+    uint32_t tot;
     uint32_t pos = wg_exclusive_scan<THREADS, uint32_t>((uint32_t)__builtin_popcountll(take), sc.wsum, tot);
 #pragma unroll
     for (int m = 0; m < KPT; ++m)
@@ -239,28 +259,30 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
     for (int i = tid; i < nn; i += THREADS)
         cs.slot_of[i] = -1;
     __syncthreads();
+    // validation and hits in one round: the selection must be ascending and
+    // in range and the table's ids in [-1, NB); each occupied slot looks its
+    // block up in the selection (a binary search that ends whatever S holds)
+    // and claims the entry, so a block held by two slots is caught too.  If
+    // anything is wrong the claims are discarded with the whole plan.
     int bad = 0;
     for (int i = tid; i < nn; i += THREADS) {
         const int32_t v = S[i];
         if (v < 0 || v >= NB || (i > 0 && v <= S[i - 1]))
             bad = 1;
     }
-    for (int s = tid; s < C; s += THREADS)
-        if (cs.blk[s] < -1 || cs.blk[s] >= NB)
-            bad = 1;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int s = tid + u * THREADS;
+        if (s < C) {
+            const int32_t blk = r.blk[u];
+            if (blk < -1 || blk >= NB)
+                bad = 1;
+            const int i = blk >= 0 ? find_sorted(S, nn, blk) : -1;
+            if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
+                bad = 1;
+        }
+    }
     if (__syncthreads_or(bad)) {
-        bad_out = 1;
-        return -1;
-    }
-    // hits: each occupied slot looks its block up in the ascending selection
-    int dup = 0;
-    for (int s = tid; s < C; s += THREADS) {
-        const int32_t blk = cs.blk[s];
-        const int i = blk >= 0 ? find_sorted(S, nn, blk) : -1;
-        if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
-            dup = 1;
-    }
-    if (__syncthreads_or(dup)) {
         bad_out = 1;
         return -1;
     }
