@@ -199,7 +199,6 @@ struct CacheScratch {
     int32_t slot_of[kMaxK];  // slot of S[i]
     uint8_t hit[kMaxK];
     int32_t miss_i[kMaxK];   // S index of miss m
-    int32_t blk[kMaxCapacity];
     uint64_t key[kMaxCapacity];  // LRU key of a candidate slot, ~0 otherwise
     int wsum[16];
 };
@@ -250,12 +249,6 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
                               int &bad_out) {
     const int tid = threadIdx.x;
     constexpr int SPT = SlotRegs<THREADS>::SPT;
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-        const int s = tid + u * THREADS;
-        if (s < C)
-            cs.blk[s] = r.blk[u];
-    }
     for (int i = tid; i < nn; i += THREADS)
         cs.slot_of[i] = -1;
     __syncthreads();
@@ -270,6 +263,8 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
         if (v < 0 || v >= NB || (i > 0 && v <= S[i - 1]))
             bad = 1;
     }
+    // the same pass also stores each slot's LRU key: ~0 for a selected
+    // (taken) slot, else empty slots first by index, then (stamp, block)
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
         const int s = tid + u * THREADS;
@@ -280,6 +275,9 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
             const int i = blk >= 0 ? find_sorted(S, nn, blk) : -1;
             if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
                 bad = 1;
+            cs.key[s] = i >= 0 ? ~0ull
+                               : (blk < 0 ? (uint64_t)s
+                                          : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk));
         }
     }
     if (__syncthreads_or(bad)) {
@@ -304,26 +302,14 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
         if (i < nn && !cs.hit[i])
             cs.miss_i[pos++] = i;
     }
-    // LRU keys of the candidate slots (empty, or occupied and not selected)
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-        const int s = tid + u * THREADS;
-        if (s < C) {
-            const int32_t blk = cs.blk[s];
-            const bool taken = blk >= 0 && find_sorted(S, nn, blk) >= 0;
-            cs.key[s] = taken ? ~0ull
-                              : (blk < 0 ? (uint64_t)s
-                                         : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk));
-        }
-    }
-    __syncthreads();
     // victims: candidate rank r < #misses takes miss r (keys of a valid table
     // are distinct; the slot index breaks ties of a corrupt one).  Q lanes
-    // share a candidate, each counting over a slice of the slots, so the
-    // loads of one thread stay few and independent.
+    // share a candidate, each counting over every Q-th slot (the Q lanes
+    // then read Q neighbouring keys: different LDS banks), so the loads of
+    // one thread stay few and independent.  (The keys were written before
+    // the barrier of the miss scan.)
     if (nm > 0) {
         constexpr int Q = THREADS >= 1024 ? 8 : (THREADS >= 512 ? 4 : 1);
-        const int per_c = (C + Q - 1) / Q;
         for (int base = 0; base < C * Q; base += THREADS) {
             const int t = base + tid;
             const int s = t / Q, part = t % Q;
@@ -331,9 +317,8 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
             const uint64_t key = on ? cs.key[s] : ~0ull;
             int rank = 0;
             if (on && key != ~0ull) {
-                const int o0 = part * per_c, o1 = min(o0 + per_c, C);
 #pragma unroll 8
-                for (int o = o0; o < o1; ++o) {
+                for (int o = part; o < C; o += Q) {
                     const uint64_t ok = cs.key[o];
                     rank += (ok < key || (ok == key && o < s)) ? 1 : 0;
                 }
