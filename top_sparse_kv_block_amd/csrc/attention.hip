@@ -529,7 +529,8 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_waves(GMAX)) void attn_kerne
     int splits, int per_split, float scale_log2, const uint8_t *__restrict__ src_k, const uint8_t *__restrict__ src_v,
     float *__restrict__ part, float *__restrict__ out, float *__restrict__ lse) {
     __shared__ AttnSmem<D, GMAX> S;
-    const int row = blockIdx.y, split = blockIdx.x;
+    int row, split;
+    xcd_row_part(row, split);
     const int b = row / Hkv, j = row - b * Hkv;
     const int n = min(max(sel_count[row], 0), k);
     AttnRow a;
@@ -578,7 +579,8 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     __shared__ int32_t sS[kMaxK];
     __shared__ CacheScratch cs;
     __shared__ AttnSmem<D, GMAX> S;
-    const int row = blockIdx.y, split = blockIdx.x;
+    int row, split;
+    xcd_row_part(row, split);
     const int b = row / Hkv, j = row - b * Hkv;
     const int NB = T / 16;
     const int len = min(max(seq_lens[b], 0), T);

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uin
     constexpr int LPT = D * E::bytes / 16;
     constexpr int TPL = 64 / LPT;
     constexpr int LPB = 16 / TPL;
-    const int row = blockIdx.y;
+    int row, wgp;
+    xcd_row_part(row, wgp);
     const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
     const int R = NQ * G;
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uin
     const int nvalid = nb_of(len);
     const uint8_t *krow = keys + (size_t)row * T * D * E::bytes;
     float *srow = scores + (size_t)row * NB;
-    const int n0 = blockIdx.x * (kScoreWaves * kScoreBlocksPerWave);
+    const int n0 = wgp * (kScoreWaves * kScoreBlocksPerWave);
     const int n1 = min(n0 + kScoreWaves * kScoreBlocksPerWave, NB);
 
     for (int n = n0 + wave; n < n1; n += kScoreWaves) {
@@ -128,7 +129,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_mfma_kernel(cons
     constexpr int TPL = 64 / LPT;      // tokens per load instruction
     constexpr int LPB = 16 / TPL;      // load instructions per block
     __shared__ __attribute__((aligned(16))) uint8_t tile[kScoreWaves][16 * ROW];
-    const int row = blockIdx.y;
+    int row, wgp;
+    xcd_row_part(row, wgp);
     const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
     const int R = NQ * G;
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_mfma_kernel(cons
     const int nvalid = nb_of(len);
     const uint8_t *krow = keys + (size_t)row * T * TB;
     float *srow = scores + (size_t)row * NB;
-    const int n0 = blockIdx.x * (kScoreWaves * kScoreBlocksPerWave);
+    const int n0 = wgp * (kScoreWaves * kScoreBlocksPerWave);
     const int n1 = min(n0 + kScoreWaves * kScoreBlocksPerWave, NB);
 
     for (int n = n0 + wave; n < n1; n += kScoreWaves) {
@@ -213,7 +215,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_quest_kernel(const uint8_
                                                           int NB, float scale) {
     constexpr int LPT = D * E::bytes / 16;  // lanes covering one D-vector
     constexpr int BPL = 64 / LPT;           // blocks per wave iteration
-    const int row = blockIdx.y;
+    int row, wgp;
+    xcd_row_part(row, wgp);
     const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
     const int R = NQ * G;
@@ -239,7 +242,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_quest_kernel(const uint8_
     const uint8_t *mrow = meta + (size_t)row * NB * 2 * vec_bytes;
     float *srow = scores + (size_t)row * NB;
     const int per_wg = kScoreWaves * BPL * kScoreBlocksPerWave;
-    const int n0 = blockIdx.x * per_wg;
+    const int n0 = wgp * per_wg;
     const int n1 = min(n0 + per_wg, NB);
 
     for (int nb = n0 + wave * BPL; nb < n1; nb += kScoreWaves * BPL) {

@@ -173,4 +173,24 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int nb_of(int len) { return (len + 15) >> 4; }
 
+// (row, part) handled by this workgroup of a (parts x rows) grid.  The
+// dispatcher deals workgroups to the 8 XCDs in turn, so with rows % 8 == 0
+// the parts of one row are laid out 8 apart in dispatch order: they run on
+// one XCD and share its L2 (the row's scores, slot state and partials
+// written by one kernel are then read from that L2 by the next, whose
+// workgroups follow the same rule).  Any other row count is row-major.
+// Only the placement depends on this; every mapping is a bijection.
+__device__ __forceinline__ void xcd_row_part(int &row, int &part) {
+    const int parts = gridDim.x, rows = gridDim.y;
+    const int L = blockIdx.y * parts + blockIdx.x;  // dispatch order
+    if ((rows & 7) == 0) {
+        const int x = L & 7, r8 = L >> 3;
+        row = 8 * (r8 / parts) + x;
+        part = r8 - (r8 / parts) * parts;
+    } else {
+        row = blockIdx.y;
+        part = blockIdx.x;
+    }
+}
+
 }  // namespace skv
