@@ -643,24 +643,26 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
     const float *p = part + (size_t)row * splits * W;
     const bool staged = splits > 1 && splits * W <= kMergeStage;
 
-    const bool do_commit = commit && miss_count[row] >= 0;  // uniform over the workgroup
-    int n = 0, c_slot[kCommitPerThread], c_blk[kCommitPerThread];
-    if (do_commit) {
-        n = min(max(sel_count[row], 0), k);
+    int mc = -1, n = 0, c_slot[kCommitPerThread], c_blk[kCommitPerThread];
+    if (commit) {  // reads first, decisions after: none of these addresses depends on another read
+        mc = miss_count[row];
+        n = sel_count[row];
 #pragma unroll
         for (int u = 0; u < kCommitPerThread; ++u) {
             const int i = tid + u * kAttnThreads;
-            c_slot[u] = i < n ? sel_slot[(size_t)row * k + i] : -1;
-            c_blk[u] = i < n ? sel_blocks[(size_t)row * k + i] : -1;
+            c_slot[u] = i < k ? sel_slot[(size_t)row * k + i] : -1;
+            c_blk[u] = i < k ? sel_blocks[(size_t)row * k + i] : -1;
         }
-        if (tid == 0)
-            sNow = atomicAdd(&clock[row], 1u) + 1u;
     }
     if (staged) {
 #pragma unroll 8
         for (int t = tid; t < splits * W; t += kAttnThreads)
             stage[t] = p[t];
     }
+    const bool do_commit = commit && mc >= 0;  // uniform over the workgroup
+    if (do_commit && tid == 0)
+        sNow = atomicAdd(&clock[row], 1u) + 1u;
+    n = min(max(n, 0), k);
     const float *src = staged ? stage : p;  // LDS or global, same layout [splits][G][D + 2]
     if (splits > 1) {
         __syncthreads();
@@ -707,7 +709,7 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
 #pragma unroll
         for (int u = 0; u < kCommitPerThread; ++u) {
             const int s = c_slot[u];
-            if (s >= 0 && s < C) {
+            if (tid + u * kAttnThreads < n && s >= 0 && s < C) {
                 slot_block[(size_t)row * C + s] = c_blk[u];
                 slot_stamp[(size_t)row * C + s] = now;
             }
