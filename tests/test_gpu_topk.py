@@ -66,3 +66,41 @@ def test_topk_rejects_too_many_forced_blocks():
         B.sparse_kv_topk(shape, t(1, 1, 64), t(1, dtype=torch.int32), 4, 16, 64, t(1, 1, 4, dtype=torch.int32),
                          t(1, 1, dtype=torch.int32))
     assert e.value.status == 4
+
+
+# Rows longer than 16384 blocks take the long-row path (thread maxima bound
+# the threshold, exact select over the keys that reach it, bitmap emit) and
+# fall back to the register path when too many keys reach the bound.
+@pytest.mark.parametrize("nb,k", [(16385, 64), (32768, 1024), (65536, 128), (65536, 1)])
+def test_topk_long_rows(nb, k):
+    r = np.random.default_rng(nb * 7 + k)
+    s = r.standard_normal((1, 3, nb)).astype(np.float32)
+    s[0, 2, 100:5000] += 6.0  # a dense cluster of high scores in one row
+    _run(s, [nb * 16], k)
+
+
+def test_topk_long_rows_ties_and_fallback():
+    r = np.random.default_rng(11)
+    nb = 65536
+    s = (np.round(r.standard_normal((1, 4, nb)) * 64) / 64).astype(np.float32)  # ties near the threshold
+    s[0, 1, :] = 2.0  # all equal: every key reaches the bound -> fallback, lowest ids win
+    s[0, 2, :] = (np.arange(nb) % 3).astype(np.float32)  # a third of the row ties at the top
+    _run(s, [nb * 16], 128)
+
+
+def test_topk_long_rows_ragged_sink_recent():
+    r = np.random.default_rng(12)
+    nb = 40000
+    s = r.standard_normal((4, 2, nb)).astype(np.float32)
+    s[:, :, 0] = -50
+    _run(s, [nb * 16, nb * 16 - 7, 16 * 129 + 3, 16 * 40], 128, sink=4, recent=128)
+
+
+def test_topk_long_rows_short_valid_lengths():
+    # long allocated rows whose valid part is short: the sampled bound must
+    # not be used when the sample holds fewer candidates than the budget
+    r = np.random.default_rng(13)
+    nb = 65536
+    s = r.standard_normal((6, 1, nb)).astype(np.float32)
+    _run(s, [16 * 130, 16 * 129 + 5, 16 * 300, 16 * 1000 + 1, 16 * 4100, 16 * 128 + 16], 128, sink=4, recent=128)
+    _run(s, [16 * 130, 16 * 129 + 5, 16 * 300, 16 * 1000 + 1, 16 * 4100, 16 * 128 + 16], 120)

@@ -32,6 +32,13 @@ __device__ __forceinline__ T wg_exclusive_scan(T v, T *wsum, T &total) {
     return base + x - v;
 }
 
+// Sum of v over the workgroup (every thread gets it).
+template <int THREADS> __device__ __forceinline__ uint32_t wg_reduce_sum(uint32_t v, uint32_t *wsum) {
+    uint32_t tot;
+    (void)wg_exclusive_scan<THREADS, uint32_t>(v, wsum, tot);
+    return tot;
+}
+
 // ------------------------------------------------------------ top-k
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0 so equal floats give equal keys
@@ -65,6 +72,68 @@ __device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remain
         }
         run += c[u];
     }
+}
+
+// Radix select: the key of the `need`-th largest of the keys flagged in
+// `cand` (KPT per thread; need >= 1 and at most the number of flagged keys).
+// Four 8-bit passes over an LDS histogram; each pass needs two barriers (the
+// histogram buffers alternate, so clearing the next one needs none).
+// Returns the key; `remaining` = how many keys equal to it are admitted,
+// `n_tau` = how many flagged keys equal it.
+template <int THREADS, int KPT>
+__device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uint64_t cand, uint32_t need,
+                                                 TopkScratch &sc, uint32_t &remaining_out, uint32_t &n_tau_out) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0, mask = 0;
+    uint32_t remaining = need, n_tau = 0;
+    if (tid < 256)
+        sc.hist[0][tid] = 0;
+    __syncthreads();
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        uint32_t *hist = sc.hist[pass & 1];
+        if (pass == 0) {
+            // the leading byte (sign and high exponent bits) is shared by
+            // nearly every score of a row: count each distinct digit of
+            // the wave once (ballot) instead of one contended atomic per key
+            const int lane = tid & 63;
+#pragma unroll
+            for (int m = 0; m < KPT; ++m) {
+                const uint32_t dg = key[m] >> 24;
+                bool pending = (cand >> m) & 1u;
+                uint64_t act = __builtin_amdgcn_ballot_w64(pending);
+                while (act) {
+                    const int leader = __builtin_ctzll(act);
+                    const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)dg, leader);
+                    const bool same = pending && dg == dl;
+                    const uint64_t grp = __builtin_amdgcn_ballot_w64(same);
+                    if (lane == leader)
+                        atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(grp));
+                    pending = pending && !same;
+                    act &= ~grp;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < KPT; ++m)
+                if (((cand >> m) & 1u) && (key[m] & mask) == prefix)
+                    atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
+        }
+        if (tid < 256)
+            sc.hist[(pass + 1) & 1][tid] = 0;  // last read by the previous pass's pick
+        __syncthreads();
+        if (tid < 64)
+            pick_digit(hist, remaining, sc);
+        __syncthreads();
+        prefix |= sc.digit << shift;
+        mask |= 255u << shift;
+        remaining = sc.remaining;
+        n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
+    }
+    remaining_out = remaining;
+    n_tau_out = n_tau;
+    return prefix;
 }
 
 // Per-row selection under the budget (sink + recent blocks forced, the rest
@@ -104,56 +173,8 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
             }
         }
     }
-    uint32_t prefix = 0, mask = 0;
-    uint32_t remaining = (uint32_t)max(need, 0), n_tau = 0;
-    if (need > 0) {
-        if (tid < 256)
-            sc.hist[0][tid] = 0;
-        __syncthreads();
-#pragma unroll 1
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            uint32_t *hist = sc.hist[pass & 1];
-            if (pass == 0) {
-                // the leading byte (sign and high exponent bits) is shared by
-                // nearly every score of a row: count each distinct digit of
-                // the wave once (ballot) instead of one contended atomic per key
-                const int lane = tid & 63;
-#pragma unroll
-                for (int m = 0; m < KPT; ++m) {
-                    const uint32_t dg = key[m] >> 24;
-                    bool pending = (cand >> m) & 1u;
-                    uint64_t act = __builtin_amdgcn_ballot_w64(pending);
-                    while (act) {
-                        const int leader = __builtin_ctzll(act);
-                        const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)dg, leader);
-                        const bool same = pending && dg == dl;
-                        const uint64_t grp = __builtin_amdgcn_ballot_w64(same);
-                        if (lane == leader)
-                            atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(grp));
-                        pending = pending && !same;
-                        act &= ~grp;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < KPT; ++m)
-                    if (((cand >> m) & 1u) && (key[m] & mask) == prefix)
-                        atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
-            }
-            if (tid < 256)
-                sc.hist[(pass + 1) & 1][tid] = 0;  // last read by the previous pass's pick
-            __syncthreads();
-            if (tid < 64)
-                pick_digit(hist, remaining, sc);
-            __syncthreads();
-            prefix |= sc.digit << shift;
-            mask |= 255u << shift;
-            remaining = sc.remaining;
-            n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
-        }
-    }
-    const uint32_t tau = prefix;
+    uint32_t remaining = 0, n_tau = 0;
+    const uint32_t tau = need > 0 ? radix_select<THREADS, KPT>(key, cand, (uint32_t)need, sc, remaining, n_tau) : 0u;
     uint64_t take = 0;
     if (need > 0 && n_tau > remaining) {
         // exact ties at the threshold: the lowest ids among them are taken
@@ -192,6 +213,242 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
         out[i] = -1;
     __syncthreads();
     return (int)tot;
+}
+
+// ------------------------------------------------------------ long rows
+// Top-k for long rows (up to 65536 blocks with 1024 threads); same result as
+// topk_row, without holding the row in registers:
+//  1. a lower bound of the threshold: the need-th largest of the per-thread
+//     maxima, since at least `need` keys reach it.  One more pass over the
+//     row puts the keys that reach it (typically not many more than need)
+//     with their ids into LDS, and a
+//     radix select over those gives the threshold key, how many keys equal
+//     it and how many of those are admitted.  If more than kLongRowCand keys
+//     reach the bound (many equal scores) the radix passes stream the row.
+//  2. the choice goes into a bitmap of the row: forced ids and keys above the
+//     threshold; keys equal to it go to a second bitmap whose prefix
+//     popcounts rank them by id (the lowest ids are admitted);
+//  3. one prefix sum over the bitmap words emits the ids in ascending order.
+constexpr int kLongRowCand = 4096;
+
+struct TopkLongScratch {
+    TopkScratch sc;
+    uint32_t n_cand;
+    uint32_t cand_key[kLongRowCand];
+    int32_t cand_id[kLongRowCand];
+    uint32_t bits[kMaxTopkBlocks / 32];
+    uint32_t eq[kMaxTopkBlocks / 32];
+};
+
+// Adds `digit` to hist for every lane with `on` set, one atomic per distinct
+// digit of the wave (lanes must be converged).
+__device__ __forceinline__ void wave_hist_add(uint32_t *hist, uint32_t digit, bool on) {
+    const int lane = threadIdx.x & 63;
+    uint64_t act = __builtin_amdgcn_ballot_w64(on);
+    while (act) {
+        const int leader = __builtin_ctzll(act);
+        const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)digit, leader);
+        const bool same = on && digit == dl;
+        const uint64_t grp = __builtin_amdgcn_ballot_w64(same);
+        if (lane == leader)
+            atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(grp));
+        on = on && !same;
+        act &= ~grp;
+    }
+}
+
+template <int THREADS>
+__device__ int topk_long_row(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
+                             int32_t *out, TopkLongScratch &ls) {
+    static_assert(THREADS * 4 >= kLongRowCand && THREADS * 2 * 32 >= kMaxTopkBlocks, "coverage");
+    constexpr int BATCH = 8;
+    const int tid = threadIdx.x;
+    const int nvalid = min(nb_of(len), NB);
+    if (nvalid <= k) {
+        for (int i = tid; i < k; i += THREADS)
+            out[i] = i < nvalid ? i : -1;
+        __syncthreads();
+        return nvalid;
+    }
+    const int fs = sink > 0 ? min(nb_of(min(sink, len)), nvalid) : 0;
+    const int fr = recent > 0 ? max(0, len - recent) / 16 : nvalid;
+    const int n_forced = fs + (nvalid - fr) - max(0, fs - fr);
+    const int need = k - n_forced;
+    const int nwords = (nvalid + 31) >> 5;
+    for (int w = tid; w < nwords; w += THREADS) {
+        ls.bits[w] = 0;
+        ls.eq[w] = 0;
+    }
+    // f(id, key, is_candidate) for this thread's ids, every lane of a wave
+    // calling f together (keys of non-candidates are 0).  Thread t reads the
+    // 4-id groups t, t + THREADS, ... with 16-byte loads when the row is
+    // 16-byte aligned (BATCH groups in flight), else single floats.
+    const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+    auto stream = [&](auto &&f) {
+        const int ngroups = (nvalid + 3) >> 2;
+        for (int g0 = tid; g0 < ngroups; g0 += BATCH * THREADS) {
+            float v[BATCH][4];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int g = g0 + u * THREADS;
+                if (vec && 4 * g + 3 < nvalid) {
+                    const u32x4 w = load16(srow + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[u][e] = __uint_as_float(w[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[u][e] = 4 * g + e < nvalid ? srow[4 * g + e] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * (g0 + u * THREADS) + e;
+                    const bool c = i < nvalid && i >= fs && i < fr;
+                    f(i, c ? order_key(v[u][e]) : 0u, c);
+                }
+            }
+        }
+    };
+    __syncthreads();  // bitmaps cleared
+    uint32_t remaining = 0, n_tau = 0, tau = 0;
+    if (need > 0) {
+        // 1a. a lower bound of the threshold: the need-th largest of the
+        //     per-thread maxima (at least `need` keys reach it).  (A sampled
+        //     subset of the row reads less but its radix select, over a few
+        //     thousand keys, measured slower than this one over 1024.)
+        uint32_t bound = 1u;
+        {
+            uint32_t tmax[1] = {0u}, r1, n1;
+            stream([&](int, uint32_t kk, bool) { tmax[0] = max(tmax[0], kk); });
+            if (__syncthreads_count(tmax[0] != 0u) >= need)
+                bound = radix_select<THREADS, 1>(tmax, tmax[0] != 0u ? 1ull : 0ull, (uint32_t)need, ls.sc, r1, n1);
+        }
+        // 1b. the keys that reach the bound, with their ids, into LDS (in
+        //     any order: neither the select nor the marking needs one)
+        if (tid == 0)
+            ls.n_cand = 0;
+        __syncthreads();
+        stream([&](int i, uint32_t kk, bool c) {
+            if (c && kk >= bound) {
+                const uint32_t p = atomicAdd(&ls.n_cand, 1u);
+                if (p < (uint32_t)kLongRowCand) {
+                    ls.cand_key[p] = kk;
+                    ls.cand_id[p] = i;
+                }
+            }
+        });
+        __syncthreads();
+        const uint32_t total = ls.n_cand;
+        if (total <= (uint32_t)kLongRowCand) {  // uniform
+            uint32_t ck[4];
+            uint64_t cm = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t p = (uint32_t)(tid + THREADS * u);
+                ck[u] = p < total ? ls.cand_key[p] : 0u;
+                cm |= (uint64_t)(p < total) << u;
+            }
+            tau = radix_select<THREADS, 4>(ck, cm, (uint32_t)need, ls.sc, remaining, n_tau);
+            // 2. mark from the candidate list (every key >= tau is in it)
+            const bool all_eq = n_tau == remaining;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t p = (uint32_t)(tid + THREADS * u);
+                if (p < total && ck[u] >= tau) {
+                    const int i = ls.cand_id[p];
+                    if (ck[u] > tau || all_eq)
+                        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
+                    else
+                        atomicOr(&ls.eq[i >> 5], 1u << (i & 31));
+                }
+            }
+        } else {
+            // many keys reach the bound (many equal scores): radix passes that
+            // stream the row (wave-aggregated histogram adds), then marking
+            uint32_t prefix = 0, mask = 0;
+            remaining = (uint32_t)need;
+            if (tid < 256)
+                ls.sc.hist[0][tid] = 0;
+            __syncthreads();
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                uint32_t *hist = ls.sc.hist[pass & 1];
+                stream([&](int, uint32_t kk, bool c) {
+                    wave_hist_add(hist, (kk >> shift) & 255u, c && (kk & mask) == prefix);
+                });
+                if (tid < 256)
+                    ls.sc.hist[(pass + 1) & 1][tid] = 0;
+                __syncthreads();
+                if (tid < 64)
+                    pick_digit(hist, remaining, ls.sc);
+                __syncthreads();
+                prefix |= ls.sc.digit << shift;
+                mask |= 255u << shift;
+                remaining = ls.sc.remaining;
+                n_tau = ls.sc.n_tau;
+            }
+            tau = prefix;
+            const bool all_eq = n_tau == remaining;
+            stream([&](int i, uint32_t kk, bool c) {
+                if (c && kk >= tau) {
+                    if (kk > tau || all_eq)
+                        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
+                    else
+                        atomicOr(&ls.eq[i >> 5], 1u << (i & 31));
+                }
+            });
+        }
+    }
+    // forced blocks: the id ranges [0, fs) and [fr, nvalid)
+    for (int i = tid; i < fs; i += THREADS)
+        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
+    for (int i = fr + tid; i < nvalid; i += THREADS)
+        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
+    __syncthreads();
+    // thread t owns words 2t, 2t + 1
+    const int w0i = 2 * tid, w1i = 2 * tid + 1;
+    uint32_t w0 = w0i < nwords ? ls.bits[w0i] : 0u, w1 = w1i < nwords ? ls.bits[w1i] : 0u;
+    if (need > 0 && n_tau > remaining) {  // uniform: exact ties, the lowest ids among them
+        const uint32_t e0 = w0i < nwords ? ls.eq[w0i] : 0u, e1 = w1i < nwords ? ls.eq[w1i] : 0u;
+        uint32_t n_eq;
+        const uint32_t r0 = wg_exclusive_scan<THREADS, uint32_t>(
+            (uint32_t)(__builtin_popcount(e0) + __builtin_popcount(e1)), ls.sc.wsum, n_eq);
+        const uint32_t r1 = r0 + (uint32_t)__builtin_popcount(e0);
+        auto keep = [&](uint32_t e, uint32_t r) -> uint32_t {  // the first remaining - r set bits
+            uint32_t kept = 0;
+            while (e && r < remaining) {
+                kept |= e & (0u - e);
+                e &= e - 1;
+                ++r;
+            }
+            return kept;
+        };
+        w0 |= keep(e0, r0);
+        w1 |= keep(e1, r1);
+    }
+    uint32_t n_out;
+    uint32_t o = wg_exclusive_scan<THREADS, uint32_t>((uint32_t)(__builtin_popcount(w0) + __builtin_popcount(w1)),
+                                                      ls.sc.wsum, n_out);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t w = h ? w1 : w0;
+        while (w) {
+            const int bit = __builtin_ctz(w);
+            w &= w - 1;
+            if (o < (uint32_t)k)
+                out[o] = (2 * tid + h) * 32 + bit;
+            ++o;
+        }
+    }
+    n_out = min(n_out, (uint32_t)k);
+    for (int i = (int)n_out + tid; i < k; i += THREADS)
+        out[i] = -1;
+    __syncthreads();
+    return (int)n_out;
 }
 
 // ------------------------------------------------------------ working set

@@ -34,6 +34,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restr
         sel_count[row] = n;
 }
 
+// Rows longer than 16384 blocks: the long-row path (thread maxima bound the
+// threshold, the exact select runs over the few keys that reach it).
+__global__ __launch_bounds__(kTopkThreads) void topk_long_kernel(const float *__restrict__ scores,
+                                                                 const int32_t *__restrict__ seq_lens, int Hkv, int T,
+                                                                 int NB, int k, int sink, int recent,
+                                                                 int32_t *__restrict__ sel_blocks,
+                                                                 int32_t *__restrict__ sel_count) {
+    __shared__ TopkLongScratch ls;
+    const int row = blockIdx.x;
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    const float *srow = scores + (size_t)row * NB;
+    int32_t *out = sel_blocks + (size_t)row * k;
+    const int n = topk_long_row<kTopkThreads>(srow, len, NB, k, sink, recent, out, ls);
+    if (threadIdx.x == 0)
+        sel_count[row] = n;
+}
+
 template <int KPT>
 static hipError_t topk_t(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
                          int32_t *sel, int32_t *cnt, hipStream_t st) {
@@ -55,9 +72,9 @@ hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *lens, 
         return topk_t<8>(d, scores, lens, k, sink, recent, sel, cnt, st);
     if (kpt <= 16)
         return topk_t<16>(d, scores, lens, k, sink, recent, sel, cnt, st);
-    if (kpt <= 32)
-        return topk_t<32>(d, scores, lens, k, sink, recent, sel, cnt, st);
-    return topk_t<64>(d, scores, lens, k, sink, recent, sel, cnt, st);
+    hipLaunchKernelGGL(topk_long_kernel, dim3(d.rows()), dim3(kTopkThreads), 0, st, scores, lens, d.Hkv, d.T, d.NB, k,
+                       sink, recent, sel, cnt);
+    return hipGetLastError();
 }
 
 }  // namespace skv
