@@ -181,3 +181,23 @@ def test_llama8b_full_size_sampled(fused):
 
 def test_tiny_workload_fused():
     run_workload(synth.WORKLOADS["tiny"], fused=True)
+
+
+@pytest.mark.timeout(400)
+def test_quest_full_size_sampled():
+    # Quest-scored 128K-context workload at full size (4 x 8 rows, 8192
+    # blocks per row, 512-token budget with 4 sink and 128 recent tokens
+    # forced): sampled score rows and attention heads, every row of top-k and
+    # of the working set
+    w = synth.WORKLOADS["quest_128k"]
+    run_workload(w, steps=2, rows=[0, 31], heads=[(0, 0), (3, 31)], fused=True)
+
+
+@pytest.mark.timeout(400)
+def test_lookahead_1m_full_size_sampled():
+    # 1M-context workload with 4 lookahead drafts (8 rows of 65536 blocks, 32
+    # scoring query rows per kv head, matrix-core scoring, long-row top-k):
+    # one sampled score row, two attention heads, every row of top-k and of
+    # the working set
+    w = synth.WORKLOADS["lookahead_1m"]
+    run_workload(w, steps=2, rows=[5], heads=[(0, 0), (0, 47)])
