@@ -63,6 +63,7 @@ def _declare(L):
     L.oracle_lru_order.argtypes = [_p, _p]
     L.oracle_lru_step.argtypes = [_p, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_gather.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
+    L.oracle_capped_step.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_attention.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _d, _p, _p]
     L.oracle_attention_pool.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _d, _p, _p]
 
@@ -189,6 +190,30 @@ class LRU:
         lib().oracle_lru_step(self._h, k, int(nb_limit), _ptr(sel), _ptr(cnt), _ptr(ss), _ptr(sh), _ptr(mb),
                               _ptr(ms), _ptr(mc))
         return dict(sel_slot=ss, sel_hit=sh, miss_block=mb, miss_slot=ms, miss_count=mc)
+
+
+def capped_step(slot_block, sel, sel_count, scores, nb_limit):
+    """Importance-capped eviction step (OasisKV summary, key module 3): hits
+    keep their slot; misses (ascending) take the empty slots by index, then
+    the unselected resident slots with the lowest current score (ties: lower
+    block id).  ``slot_block`` [rows, cap] int32 is updated in place; scores
+    [rows, nb_max] are the step's block scores (float64).  Returns the lists
+    like ``LRU.step``; a row with invalid input gets miss_count = -1 and is
+    left untouched."""
+    assert slot_block.dtype == np.int32 and slot_block.flags.c_contiguous
+    rows, cap = slot_block.shape
+    sel = _c(sel, np.int32).reshape(rows, -1)
+    cnt = _c(sel_count, np.int32).reshape(rows)
+    sc = _c(scores, np.float64).reshape(rows, -1)
+    k = sel.shape[1]
+    ss = np.full((rows, k), -1, dtype=np.int32)
+    sh = np.zeros((rows, k), dtype=np.uint8)
+    mb = np.full((rows, k), -1, dtype=np.int32)
+    ms = np.full((rows, k), -1, dtype=np.int32)
+    mc = np.zeros(rows, dtype=np.int32)
+    lib().oracle_capped_step(rows, cap, k, int(nb_limit), sc.shape[1], _ptr(sel), _ptr(cnt), _ptr(sc),
+                             _ptr(slot_block), _ptr(ss), _ptr(sh), _ptr(mb), _ptr(ms), _ptr(mc))
+    return dict(sel_slot=ss, sel_hit=sh, miss_block=mb, miss_slot=ms, miss_count=mc)
 
 
 def gather(miss_block, miss_slot, miss_count, src_k, src_v, pool_k, pool_v, block=16):

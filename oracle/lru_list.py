@@ -17,6 +17,7 @@ LRU, hit detection + replacement + fetch in one pass; "KV Cache å¡žä¸è¿› HBM äº
 
 from __future__ import annotations
 
+import heapq
 from collections import OrderedDict
 
 
@@ -61,6 +62,38 @@ class ListLRU:
         for s in sel_slot:  # ascending block order
             self.lru.pop(s, None)
             self.lru[s] = None
+        return sel_slot, sel_hit, out_misses
+
+
+class HeapCapped:
+    """Importance-capped working set with a priority queue (OasisKV summary,
+    key module 3: when the capped cache has no room, the least important
+    blocks go).  Victims: empty slots by index (a heap of slot numbers), then
+    resident unselected blocks by (current score, block id) from a heap."""
+
+    def __init__(self, cap: int):
+        self.cap = cap
+        self.slot_block = [-1] * cap
+
+    def step(self, S, scores):
+        """scores: mapping block -> current score.  Returns (sel_slot, sel_hit, misses[(block, slot)])."""
+        S = list(S)
+        where = {b: s for s, b in enumerate(self.slot_block) if b >= 0}
+        chosen = set(S)
+        sel_slot = [where.get(b, -1) for b in S]
+        sel_hit = [int(s >= 0) for s in sel_slot]
+        empty = [s for s in range(self.cap) if self.slot_block[s] < 0]
+        heapq.heapify(empty)
+        resident = [(scores[b], b, s) for s, b in enumerate(self.slot_block) if b >= 0 and b not in chosen]
+        heapq.heapify(resident)
+        out_misses = []
+        for i, b in enumerate(S):
+            if sel_slot[i] >= 0:
+                continue
+            v = heapq.heappop(empty) if empty else heapq.heappop(resident)[2]
+            self.slot_block[v] = b
+            sel_slot[i] = v
+            out_misses.append((b, v))
         return sel_slot, sel_hit, out_misses
 
 

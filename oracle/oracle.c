@@ -480,6 +480,112 @@ int oracle_lru_step(oracle_lru *h, int k_max, int nb_limit, const int32_t *sel, 
 }
 
 /*
+ * Importance-capped eviction (OasisKV summary, key module 3: the important
+ * blocks are compared with the resident ones, only the delta moves, and
+ * when the capped HBM cache has no room the least important blocks are
+ * evicted).  Reading: a block's importance is its score of the current step.
+ * Hits and misses as for the LRU form; the victims are the empty slots in
+ * ascending slot order, then the occupied slots whose block is not
+ * selected, least important first: score ascending, then block id
+ * ascending.  Miss i goes to victim i.
+ *
+ * The slot table [rows, cap] is the caller's and is updated in place.  An
+ * invalid row (count outside [0, min(k, cap)], a selection not strictly
+ * ascending or out of [0, nb_limit), a table id outside [-1, nb_limit), or a
+ * block resident twice) is left untouched with miss_count = -1.
+ */
+typedef struct {
+    double score;
+    int32_t blk, slot;
+} orc_cand;
+
+static int by_score_then_block(const void *a, const void *b)
+{
+    const orc_cand *x = (const orc_cand *)a, *y = (const orc_cand *)b;
+    if (x->score != y->score)
+        return x->score < y->score ? -1 : 1;
+    return (x->blk > y->blk) - (x->blk < y->blk);
+}
+
+int oracle_capped_step(int rows, int cap, int k_max, int nb_limit, int nb_max, const int32_t *sel,
+                       const int32_t *sel_count, const double *scores, int32_t *slot_block, int32_t *sel_slot,
+                       uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count)
+{
+    const int C = cap;
+#pragma omp parallel for schedule(dynamic)
+    for (int r = 0; r < rows; ++r) {
+        const int32_t *S = sel + (size_t)r * k_max;
+        int32_t *sb = slot_block + (size_t)r * C;
+        int n = sel_count[r];
+        int ok = n >= 0 && n <= k_max && n <= C;
+        for (int i = 0; ok && i < n; ++i)
+            if (S[i] < 0 || S[i] >= nb_limit || (i > 0 && S[i] <= S[i - 1]))
+                ok = 0;
+        for (int s = 0; ok && s < C; ++s) {
+            if (sb[s] < -1 || sb[s] >= nb_limit)
+                ok = 0;
+            for (int t = 0; ok && t < s; ++t)
+                if (sb[s] >= 0 && sb[t] == sb[s])
+                    ok = 0;
+        }
+        if (!ok) {
+            miss_count[r] = -1;
+            continue;
+        }
+        int32_t *ss = sel_slot + (size_t)r * k_max;
+        uint8_t *sh = sel_hit + (size_t)r * k_max;
+        int32_t *mb = miss_block + (size_t)r * k_max, *ms = miss_slot + (size_t)r * k_max;
+        orc_cand *cand = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(C > 0 ? C : 1));
+        int32_t *victim = (int32_t *)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
+        int nm = 0;
+        for (int i = 0; i < n; ++i) {
+            int found = -1;
+            for (int s = 0; s < C; ++s)
+                if (sb[s] == S[i]) {
+                    found = s;
+                    break;
+                }
+            ss[i] = found;
+            sh[i] = (uint8_t)(found >= 0);
+            if (found < 0)
+                mb[nm++] = S[i];
+        }
+        int nv = 0, nc = 0;
+        for (int s = 0; s < C; ++s)
+            if (sb[s] < 0)
+                victim[nv++] = s;
+        for (int s = 0; s < C; ++s)
+            if (sb[s] >= 0 && !in_sorted(S, n, sb[s])) {
+                cand[nc].score = scores[(size_t)r * nb_max + sb[s]];
+                cand[nc].blk = sb[s];
+                cand[nc].slot = s;
+                ++nc;
+            }
+        qsort(cand, (size_t)nc, sizeof(orc_cand), by_score_then_block);
+        for (int c = 0; c < nc; ++c)
+            victim[nv++] = cand[c].slot;
+        for (int i = 0, m = 0; i < n; ++i)
+            if (!sh[i]) {
+                int v = victim[m];
+                sb[v] = S[i];
+                ss[i] = v;
+                ms[m] = v;
+                ++m;
+            }
+        for (int i = n; i < k_max; ++i) {
+            ss[i] = -1;
+            sh[i] = 0;
+        }
+        for (int i = nm; i < k_max; ++i)
+            mb[i] = ms[i] = -1;
+        miss_count[r] = nm;
+        free(cand);
+        free(victim);
+    }
+    return ORC_OK;
+}
+
+/*
  * Fetch: copy the rows of every missed block from the source cache into its
  * slot (hit detection, replacement and fetch are one pass in HiSparse;
  * "to_load" blocks are what moves in "KV Cache 塞不进 HBM 了" §3 step 1).
