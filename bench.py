@@ -388,9 +388,16 @@ def run(args):
         if ev is not None:
             ev[2].record()
         # list-only cache update; the attention kernel fetches the misses
-        B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count, buf.slot_block,
-                                 buf.slot_stamp, buf.clock, buf.sel_slot, buf.sel_hit, buf.miss_block, buf.miss_slot,
-                                 miss_log[t], None, None, B.SKV_SRC_DEVICE, buf.pool_k, buf.pool_v, st)
+        if args.eviction == "importance":
+            B.sparse_kv_cache_update_importance(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count,
+                                                buf.scores, buf.slot_block, buf.slot_stamp, buf.clock, buf.sel_slot,
+                                                buf.sel_hit, buf.miss_block, buf.miss_slot, miss_log[t], None, None,
+                                                B.SKV_SRC_DEVICE, buf.pool_k, buf.pool_v, st)
+        else:
+            B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count,
+                                     buf.slot_block, buf.slot_stamp, buf.clock, buf.sel_slot, buf.sel_hit,
+                                     buf.miss_block, buf.miss_slot, miss_log[t], None, None, B.SKV_SRC_DEVICE,
+                                     buf.pool_k, buf.pool_v, st)
         if ev is not None:
             ev[3].record()
         B.sparse_decode_attention(shape, q_all[t], buf.pool_k, buf.pool_v, cfg.capacity, buf.sel_blocks,
@@ -511,6 +518,7 @@ def run(args):
         "mode": "hip-graph replay" if graph is not None else "eager",
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "path": "score + fused select/update/attend" if args.fused else "four calls",
+        "eviction": args.eviction,
         "stage_us": ({"score": round(float(stage[:, 0].mean()), 2),
                       "select_update_attend": round(float(stage[:, 1].mean()), 2)} if args.fused else
                      {name: round(float(v), 2) for name, v in
@@ -539,6 +547,8 @@ def main(argv=None):
     ap.add_argument("--eager", action="store_true", help="enqueue every call from Python instead of a graph")
     ap.add_argument("--four-calls", dest="fused", action="store_false",
                     help="run stages 2-4 as three calls instead of the fused select-attend call")
+    ap.add_argument("--eviction", choices=("lru", "importance"), default="lru",
+                    help="working-set eviction; importance (by this step's scores) runs the four calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-fetch", action="store_true", help="skip the host-tier PCIe fetch measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -547,6 +557,8 @@ def main(argv=None):
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc outputs of --pmc-pass into the traffic file under profiles/")
     args = ap.parse_args(argv)
+    if args.eviction == "importance":
+        args.fused = False  # the fused call evicts LRU only
     if args.traffic_summary:
         print(json.dumps(traffic_summary(*args.traffic_summary, args.workload)))
         return 0

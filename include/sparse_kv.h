@@ -194,6 +194,25 @@ skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int3
                                   void *stream);
 
 /*
+ * Stage 3 with importance-capped eviction instead of LRU (OasisKV summary,
+ * key module 3: only the delta moves, and when the capped cache has no room
+ * the least important blocks are evicted).  Everything as in
+ * sparse_kv_cache_update except the order of the victims after the empty
+ * slots: occupied slots whose block is not in S, least important first,
+ * ordered by (scores[b,j,block], block id), where scores [B,Hkv,NB] float32
+ * are this step's block scores (from sparse_kv_score; not modified).  Stamps
+ * and the clock are still advanced, so a row may switch policies between
+ * steps.  scores == NULL returns SKV_ERR_NULL.
+ */
+skv_status sparse_kv_cache_update_importance(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
+                                             const int32_t *sel_blocks, const int32_t *sel_count,
+                                             const float *scores, int32_t *slot_block, uint32_t *slot_stamp,
+                                             uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit,
+                                             int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
+                                             const void *src_k, const void *src_v, int32_t src_kind, void *pool_k,
+                                             void *pool_v, void *stream);
+
+/*
  * Stage 4: GQA decode attention over the selected blocks.
  *
  * For query head h (kv head j = h / G) and the valid tokens t of the

@@ -492,7 +492,7 @@ int oracle_lru_step(oracle_lru *h, int k_max, int nb_limit, const int32_t *sel, 
  * The slot table [rows, cap] is the caller's and is updated in place.  An
  * invalid row (count outside [0, min(k, cap)], a selection not strictly
  * ascending or out of [0, nb_limit), a table id outside [-1, nb_limit), or a
- * block resident twice) is left untouched with miss_count = -1.
+ * selected block held by two slots) is left untouched with miss_count = -1.
  */
 typedef struct {
     double score;
@@ -525,7 +525,7 @@ int oracle_capped_step(int rows, int cap, int k_max, int nb_limit, int nb_max, c
             if (sb[s] < -1 || sb[s] >= nb_limit)
                 ok = 0;
             for (int t = 0; ok && t < s; ++t)
-                if (sb[s] >= 0 && sb[t] == sb[s])
+                if (sb[s] >= 0 && sb[t] == sb[s] && in_sorted(S, n, sb[s]))
                     ok = 0;
         }
         if (!ok) {

@@ -169,3 +169,75 @@ def test_flush_refetches_everything():
     torch.cuda.synchronize()
     assert host(buf.miss_count).tolist() == [[8, 8]]
     assert host(buf.sel_slot)[0, 0].tolist() == list(range(8))
+
+
+@pytest.mark.parametrize("Bsz,Hkv,cap,k,nb,retain,partial,ties", [
+    (1, 2, 16, 8, 64, 0.8, 0.0, False),
+    (2, 4, 128, 128, 2048, 0.8, 0.0, False),   # throughput workload row shape
+    (2, 8, 256, 128, 8192, 0.8, 0.2, True),    # host-tier row shape, partial selections, tied scores
+    (1, 3, 37, 20, 100, 0.5, 0.3, True),
+])
+def test_importance_capped_eviction_matches_oracle(Bsz, Hkv, cap, k, nb, retain, partial, ties):
+    # importance-capped eviction (OasisKV summary, key module 3): the same
+    # hits and misses, victims by (this step's score, block id); bit-exact
+    # against the oracle's capped step given the same selections and scores
+    r = np.random.default_rng(cap * 11 + k)
+    rows, T, D = Bsz * Hkv, nb * 16, 64
+    cfg = StepConfig(Bsz, Hkv, Hkv, D, T, "f32", k, cap)
+    buf = LayerBuffers(cfg)
+    src_k = r.standard_normal((Bsz, Hkv, T, D)).astype(np.float32)
+    src_v = r.standard_normal((Bsz, Hkv, T, D)).astype(np.float32)
+    dk, dv = dev(src_k), dev(src_v)
+    pool_k = np.zeros((Bsz, Hkv, cap, 16, D), dtype=np.float32)
+    pool_v = np.zeros_like(pool_k)
+    table = np.full((rows, cap), -1, dtype=np.int32)
+    chains = _chains(r, rows, nb, k, 8, retain, partial)
+    for t in range(8):
+        sel, cnt = _pack(chains, t, k)
+        scores = r.standard_normal((rows, nb)).astype(np.float32)
+        if ties:
+            scores = np.round(scores * 2) / 2
+        scores[:, ::17] = -np.inf  # blocks past a row's end score -inf
+        buf.sel_blocks.copy_(dev(sel).view(Bsz, Hkv, k))
+        buf.sel_count.copy_(dev(cnt).view(Bsz, Hkv))
+        buf.scores.copy_(dev(scores).view(Bsz, Hkv, nb))
+        log("cache_update importance", (Bsz, Hkv, cap, k, nb), "step", t)
+        buf.cache_update(dk, dv, importance=True)
+        torch.cuda.synchronize()
+        out = oracle.capped_step(table, sel, cnt, scores.astype(np.float64), nb)
+        oracle.gather(out["miss_block"], out["miss_slot"], out["miss_count"], src_k, src_v, pool_k, pool_v)
+        _compare(buf, out, rows, k)
+        np.testing.assert_array_equal(host(buf.slot_block).reshape(rows, cap), table)
+        np.testing.assert_array_equal(host(buf.pool_k), pool_k)
+        np.testing.assert_array_equal(host(buf.pool_v), pool_v)
+    assert np.all(host(buf.clock) == 8)
+
+
+def test_switching_between_lru_and_importance_eviction():
+    # a row can change policy between steps: the state is the same slot table
+    r = np.random.default_rng(21)
+    Bsz, Hkv, cap, k, nb = 1, 4, 24, 16, 200
+    rows = Bsz * Hkv
+    cfg = StepConfig(Bsz, Hkv, Hkv, 64, nb * 16, "f32", k, cap)
+    buf = LayerBuffers(cfg, pool=False)
+    table = np.full((rows, cap), -1, dtype=np.int32)
+    chains = _chains(r, rows, nb, k, 6, 0.6)
+    replaced = False
+    for t in range(6):
+        sel, cnt = _pack(chains, t, k)
+        scores = r.standard_normal((rows, nb)).astype(np.float32)
+        buf.sel_blocks.copy_(dev(sel).view(Bsz, Hkv, k))
+        buf.sel_count.copy_(dev(cnt).view(Bsz, Hkv))
+        buf.scores.copy_(dev(scores).view(Bsz, Hkv, nb))
+        log("policy switch step", t)
+        buf.cache_update(None, None, importance=(t % 2 == 1))
+        torch.cuda.synchronize()
+        if t % 2 == 1:
+            before = table.copy()
+            out = oracle.capped_step(table, sel, cnt, scores.astype(np.float64), nb)
+            _compare(buf, out, rows, k)
+            np.testing.assert_array_equal(host(buf.slot_block).reshape(rows, cap), table)
+            replaced |= not np.array_equal(table, before)  # the capped steps did evict
+        else:  # an LRU step: carry its table into the next capped step
+            table = host(buf.slot_block).reshape(rows, cap).copy()
+    assert replaced

@@ -82,12 +82,12 @@ SKV_API skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, c
                                        sel_count, (hipStream_t)stream));
 }
 
-SKV_API skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
-                                          const int32_t *sel_blocks, const int32_t *sel_count, int32_t *slot_block,
-                                          uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot,
-                                          uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot,
-                                          int32_t *miss_count, const void *src_k, const void *src_v,
-                                          int32_t src_kind, void *pool_k, void *pool_v, void *stream) {
+static skv_status cache_update_impl(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
+                                    const int32_t *sel_blocks, const int32_t *sel_count, const float *scores,
+                                    int32_t *slot_block, uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot,
+                                    uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
+                                    const void *src_k, const void *src_v, int32_t src_kind, void *pool_k,
+                                    void *pool_v, void *stream) {
     Dims d;
     skv_status st = check_shape(shape, d);
     if (st != SKV_OK)
@@ -108,11 +108,36 @@ SKV_API skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_bloc
         return SKV_ERR_NULL;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = skv::launch_cache_update(d, k_blocks, capacity, sel_blocks, sel_count, slot_block, slot_stamp,
-                                            clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, s);
+                                            clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, scores, s);
     if (e != hipSuccess || !fetch)
         return hip_status(e);
     return hip_status(
         skv::launch_gather(d, k_blocks, capacity, miss_block, miss_slot, miss_count, src_k, src_v, pool_k, pool_v, s));
+}
+
+SKV_API skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
+                                          const int32_t *sel_blocks, const int32_t *sel_count, int32_t *slot_block,
+                                          uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot,
+                                          uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot,
+                                          int32_t *miss_count, const void *src_k, const void *src_v,
+                                          int32_t src_kind, void *pool_k, void *pool_v, void *stream) {
+    return cache_update_impl(shape, k_blocks, capacity, sel_blocks, sel_count, nullptr, slot_block, slot_stamp,
+                             clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, src_k, src_v, src_kind,
+                             pool_k, pool_v, stream);
+}
+
+SKV_API skv_status sparse_kv_cache_update_importance(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
+                                                     const int32_t *sel_blocks, const int32_t *sel_count,
+                                                     const float *scores, int32_t *slot_block, uint32_t *slot_stamp,
+                                                     uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit,
+                                                     int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
+                                                     const void *src_k, const void *src_v, int32_t src_kind,
+                                                     void *pool_k, void *pool_v, void *stream) {
+    if (!scores)
+        return SKV_ERR_NULL;
+    return cache_update_impl(shape, k_blocks, capacity, sel_blocks, sel_count, scores, slot_block, slot_stamp, clock,
+                             sel_slot, sel_hit, miss_block, miss_slot, miss_count, src_k, src_v, src_kind, pool_k,
+                             pool_v, stream);
 }
 
 SKV_API int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k_blocks) {

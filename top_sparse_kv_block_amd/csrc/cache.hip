@@ -11,6 +11,11 @@
 // insight 2).  Evicted slots are overwritten in place (KV-Cache 压缩技术的工程
 // 原理 §4.3).
 //
+// Importance-capped eviction (OasisKV summary, key module 3: when the capped
+// cache has no room the least important blocks go) is the same kernel with
+// the row's scores of this step: occupied unselected slots are then ranked
+// by (score, block id) instead of (stamp, block id).
+//
 // LRU as stamps.  Every slot of S gets the row's new clock value, and the
 // least recently used slot is the smallest (stamp, block id).  Because a
 // step touches its blocks in ascending id order, ordering by (stamp, id) is
@@ -43,7 +48,7 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_count, int k, int C, int NB,
     int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp, uint32_t *__restrict__ clock,
     int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit, int32_t *__restrict__ miss_block,
-    int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count) {
+    int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count, const float *__restrict__ scores) {
     __shared__ int32_t sS[kMaxK];
     __shared__ CacheScratch cs;
     __shared__ uint32_t sClock;
@@ -66,7 +71,8 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     }
     __syncthreads();
     int bad;
-    const int nm = cache_plan_row<kCacheThreads>(sS, n, C, NB, regs, cs, bad);
+    const int nm = cache_plan_row<kCacheThreads>(sS, n, C, NB, regs, cs, bad,
+                                                 scores ? scores + (size_t)row * NB : nullptr);
     if (bad) {
         if (tid == 0)
             miss_count[row] = -1;
@@ -124,10 +130,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const int32_t *__restrict__
 hipError_t launch_cache_update(const Dims &d, int k, int cap, const int32_t *sel_blocks, const int32_t *sel_count,
                                int32_t *slot_block, uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot,
                                uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
-                               hipStream_t st) {
+                               const float *scores, hipStream_t st) {
     hipLaunchKernelGGL(cache_update_kernel, dim3(d.rows()), dim3(kCacheThreads), 0, st, sel_blocks, sel_count, k,
                        cap, d.NB, slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block, miss_slot,
-                       miss_count);
+                       miss_count, scores);
     return hipGetLastError();
 }
 

@@ -503,7 +503,7 @@ __device__ __forceinline__ void load_slots(SlotRegs<THREADS> &r, int C, const in
 // global memory.  THREADS >= 256.
 template <int THREADS>
 __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const SlotRegs<THREADS> &r, CacheScratch &cs,
-                              int &bad_out) {
+                              int &bad_out, const float *__restrict__ importance = nullptr) {
     const int tid = threadIdx.x;
     constexpr int SPT = SlotRegs<THREADS>::SPT;
     for (int i = tid; i < nn; i += THREADS)
@@ -520,8 +520,10 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
         if (v < 0 || v >= NB || (i > 0 && v <= S[i - 1]))
             bad = 1;
     }
-    // the same pass also stores each slot's LRU key: ~0 for a selected
-    // (taken) slot, else empty slots first by index, then (stamp, block)
+    // the same pass also stores each slot's eviction key: ~0 for a selected
+    // (taken) slot, else empty slots first by index, then occupied slots by
+    // (stamp, block) for LRU or, with `importance` (the row's scores of this
+    // step), by (score, block): the least important block goes first
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
         const int s = tid + u * THREADS;
@@ -532,9 +534,10 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
             const int i = blk >= 0 ? find_sorted(S, nn, blk) : -1;
             if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
                 bad = 1;
+            const uint32_t order = importance && blk >= 0 && blk < NB ? order_key(importance[blk]) : r.stamp[u];
             cs.key[s] = i >= 0 ? ~0ull
                                : (blk < 0 ? (uint64_t)s
-                                          : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk));
+                                          : ((1ull << 63) | ((uint64_t)order << 31) | (uint64_t)blk));
         }
     }
     if (__syncthreads_or(bad)) {

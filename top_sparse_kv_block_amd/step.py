@@ -100,8 +100,16 @@ class LayerBuffers:
         B.sparse_kv_topk(self.shape, self.scores, seq_lens, c.k_blocks, c.sink, c.recent, self.sel_blocks,
                          self.sel_count, stream)
 
-    def cache_update(self, src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None):
+    def cache_update(self, src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None, importance=False):
+        """importance=True evicts by this step's scores (in self.scores) instead of LRU."""
         c = self.cfg
+        if importance:
+            B.sparse_kv_cache_update_importance(self.shape, c.k_blocks, c.capacity, self.sel_blocks, self.sel_count,
+                                                self.scores, self.slot_block, self.slot_stamp, self.clock,
+                                                self.sel_slot, self.sel_hit, self.miss_block, self.miss_slot,
+                                                self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
+                                                stream)
+            return
         B.sparse_kv_cache_update(self.shape, c.k_blocks, c.capacity, self.sel_blocks, self.sel_count, self.slot_block,
                                  self.slot_stamp, self.clock, self.sel_slot, self.sel_hit, self.miss_block,
                                  self.miss_slot, self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
