@@ -64,6 +64,7 @@ def _declare(L):
     L.oracle_lru_step.argtypes = [_p, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_gather.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_capped_step.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
+    L.oracle_append.argtypes = [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p]
     L.oracle_attention.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _d, _p, _p]
     L.oracle_attention_pool.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _d, _p, _p]
 
@@ -214,6 +215,25 @@ def capped_step(slot_block, sel, sel_count, scores, nb_limit):
     lib().oracle_capped_step(rows, cap, k, int(nb_limit), sc.shape[1], _ptr(sel), _ptr(cnt), _ptr(sc),
                              _ptr(slot_block), _ptr(ss), _ptr(sh), _ptr(mb), _ptr(ms), _ptr(mc))
     return dict(sel_slot=ss, sel_hit=sh, miss_block=mb, miss_slot=ms, miss_count=mc)
+
+
+def append(new_k, new_v, seq_lens, k, v, slot_block=None, pool_k=None, pool_v=None, block=16):
+    """Store one new token per sequence at seq_lens[b] (in place on k, v, the
+    pools of resident blocks and seq_lens, which grows by one; full sequences
+    are left alone).  new_k/new_v [B,Hkv,D]; k, v [B,Hkv,T,D]; slot_block
+    [B*Hkv, cap] or None; pools [B,Hkv,cap,16,D]."""
+    B, Hkv, T, D = k.shape
+    assert k.flags.c_contiguous and v.flags.c_contiguous and seq_lens.dtype == np.int32
+    nk, nv = _c(new_k, k.dtype), _c(new_v, v.dtype)
+    if slot_block is None:
+        sb, cap, pk, pv = None, 0, None, None
+    else:
+        sb = _c(slot_block, np.int32)
+        cap = sb.shape[-1]
+        assert pool_k.flags.c_contiguous and pool_v.flags.c_contiguous
+        pk, pv = _ptr(pool_k), _ptr(pool_v)
+    lib().oracle_append(B, Hkv, D, T, block, k.itemsize, _ptr(nk), _ptr(nv), _ptr(seq_lens), _ptr(k), _ptr(v),
+                        None if sb is None else _ptr(sb), cap, pk, pv)
 
 
 def gather(miss_block, miss_slot, miss_count, src_k, src_v, pool_k, pool_v, block=16):

@@ -586,6 +586,43 @@ int oracle_capped_step(int rows, int cap, int k_max, int nb_limit, int nb_max, c
 }
 
 /*
+ * Decode-time append (the gains of the method concentrate where the KV grows
+ * during decoding: "KV Cache 塞不进 HBM 了", intro and §1).  For every
+ * sequence b with seq_lens[b] < T_max, the new key and value rows of each kv
+ * head are stored at token seq_lens[b]; if the block holding that token is
+ * resident in a slot of the row's working set (slot_block may be NULL), the
+ * row is also stored in that slot, so every resident slot keeps the bytes of
+ * its block.  Then seq_lens[b] grows by one.  A full sequence (seq_lens[b]
+ * >= T_max) is left as it is.  Plain byte copies.
+ */
+int oracle_append(int B, int Hkv, int D, int T_max, int block, int elem_bytes, const void *new_k,
+                  const void *new_v, int32_t *seq_lens, void *k, void *v, const int32_t *slot_block, int cap,
+                  void *pool_k, void *pool_v)
+{
+    const size_t rowb = (size_t)D * elem_bytes;
+    for (int b = 0; b < B; ++b) {
+        const int len = seq_lens[b];
+        if (len < 0 || len >= T_max)
+            continue;
+        for (int j = 0; j < Hkv; ++j) {
+            const size_t r = (size_t)b * Hkv + j;
+            memcpy((char *)k + (r * T_max + len) * rowb, (const char *)new_k + r * rowb, rowb);
+            memcpy((char *)v + (r * T_max + len) * rowb, (const char *)new_v + r * rowb, rowb);
+            if (!slot_block)
+                continue;
+            for (int s = 0; s < cap; ++s)
+                if (slot_block[r * cap + s] == len / block) {
+                    const size_t po = ((r * cap + s) * block + len % block) * rowb;
+                    memcpy((char *)pool_k + po, (const char *)new_k + r * rowb, rowb);
+                    memcpy((char *)pool_v + po, (const char *)new_v + r * rowb, rowb);
+                }
+        }
+        seq_lens[b] = len + 1;
+    }
+    return ORC_OK;
+}
+
+/*
  * Fetch: copy the rows of every missed block from the source cache into its
  * slot (hit detection, replacement and fetch are one pass in HiSparse;
  * "to_load" blocks are what moves in "KV Cache 塞不进 HBM 了" §3 step 1).
