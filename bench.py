@@ -360,14 +360,31 @@ def run(args):
     dev = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
                      if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a))).cuda()
     q_all, sq_all = dev(data["q"]), dev(data["score_q"])
-    dK, dV, dlens = dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
+    T = w.ctx
+    if args.grow:
+        # room for one appended token per step (warm-up, timed steps and the
+        # per-call timing pass); the appended rows are seeded random values
+        T = w.ctx + 16 * ((args.warmup + 2 * args.steps + 15) // 16)
+        kv_shape = (w.batch, w.n_kv_heads, T, w.head_dim)
+        dK = torch.zeros(kv_shape, dtype=q_all.dtype, device="cuda")
+        dV = torch.zeros_like(dK)
+        dK[:, :, :w.ctx] = dev(data["K"])
+        dV[:, :, :w.ctx] = dev(data["V"])
+        g = torch.Generator(device="cuda").manual_seed(w.seed + 100)
+        new_rows = torch.randn(2, nsteps + args.steps, w.batch, w.n_kv_heads, w.head_dim, generator=g,
+                               device="cuda").to(q_all.dtype)
+    else:
+        dK, dV = dev(data["K"]), dev(data["V"])
+    dlens = dev(data["seq_lens"])
     mode = B.SKV_SCORE_QUEST if w.scoring == "quest" else B.SKV_SCORE_BLOCKMAX
-    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, T, w.dtype, w.k_blocks, w.capacity,
                      mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent, num_splits=args.splits)
     buf = LayerBuffers(cfg)
+    if args.fused and cfg.nb > 8192:
+        args.fused = False  # rows over 8192 blocks exceed the fused call: the four calls run
     keys_or_meta = dK
     if mode == B.SKV_SCORE_QUEST:
-        keys_or_meta = torch.empty(w.batch, w.n_kv_heads, w.nb_max, 2, w.head_dim, dtype=cfg.torch_dtype,
+        keys_or_meta = torch.empty(w.batch, w.n_kv_heads, cfg.nb, 2, w.head_dim, dtype=cfg.torch_dtype,
                                    device="cuda")
         B.sparse_kv_quest_meta(cfg.shape, dK, dlens, keys_or_meta)
     miss_log = torch.zeros(nsteps, w.batch, w.n_kv_heads, dtype=torch.int32, device="cuda")
@@ -378,6 +395,8 @@ def run(args):
         if args.fused:
             return step_fused(t, ev)
         # ev: optional list of 5 events bracketing the four calls (profiling pass only)
+        if args.grow:
+            grow()
         if ev is not None:
             ev[0].record()
         B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
@@ -406,9 +425,21 @@ def run(args):
         if ev is not None:
             ev[4].record()
 
+    appended = [0]
+
+    def grow():
+        # one new token per sequence before the step (lengths grow on the device)
+        i = appended[0]
+        appended[0] += 1
+        B.sparse_kv_append(shape, new_rows[0, i], new_rows[1, i], dlens, dK, dV,
+                           keys_or_meta if mode == B.SKV_SCORE_QUEST else None, buf.slot_block, cfg.capacity,
+                           buf.pool_k, buf.pool_v, st)
+
     def step_fused(t, ev=None):
         # score, then top-k + working-set update + attention (fetching the
         # misses) as the single fused call; ev brackets the two calls
+        if args.grow:
+            grow()
         if ev is not None:
             ev[0].record()
         B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
@@ -519,6 +550,7 @@ def run(args):
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "path": "score + fused select/update/attend" if args.fused else "four calls",
         "eviction": args.eviction,
+        "grow": bool(args.grow),
         "stage_us": ({"score": round(float(stage[:, 0].mean()), 2),
                       "select_update_attend": round(float(stage[:, 1].mean()), 2)} if args.fused else
                      {name: round(float(v), 2) for name, v in
@@ -549,6 +581,8 @@ def main(argv=None):
                     help="run stages 2-4 as three calls instead of the fused select-attend call")
     ap.add_argument("--eviction", choices=("lru", "importance"), default="lru",
                     help="working-set eviction; importance (by this step's scores) runs the four calls")
+    ap.add_argument("--grow", action="store_true",
+                    help="append one token per sequence before every step (decode-time growth; Quest boxes kept)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-fetch", action="store_true", help="skip the host-tier PCIe fetch measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -559,6 +593,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.eviction == "importance":
         args.fused = False  # the fused call evicts LRU only
+    if args.grow:
+        args.no_cpu_baseline = True  # the oracle leg replays the fixed-length workload
     if args.traffic_summary:
         print(json.dumps(traffic_summary(*args.traffic_summary, args.workload)))
         return 0

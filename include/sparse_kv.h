@@ -213,6 +213,26 @@ skv_status sparse_kv_cache_update_importance(const skv_shape *shape, int32_t k_b
                                              void *pool_v, void *stream);
 
 /*
+ * Decode-time append (the method's gains come where the KV grows during
+ * decoding: "KV Cache 塞不进 HBM 了", intro and §1).  For every sequence b
+ * with 0 <= seq_lens[b] < T, the new rows new_k[b,j,:], new_v[b,j,:] of each
+ * kv head j are stored at token seq_lens[b] of keys/values [B,Hkv,T,D], and
+ * seq_lens[b] grows by one (device-side; a full sequence is left as it is).
+ *   meta (nullable) [B,Hkv,NB,2,D]: the Quest box of the token's block is
+ *     kept exact: a token that opens a block sets min = max = its row, else
+ *     min/max take the element-wise minimum/maximum with it (the result
+ *     equals sparse_kv_quest_meta over the grown cache);
+ *   slot_block (nullable) [B,Hkv,capacity]: if the token's block is resident
+ *     in a slot, the rows are also stored in pool_k/pool_v [B,Hkv,capacity,
+ *     16,D], so every resident slot keeps its block's bytes.
+ * new_k, new_v [B,Hkv,D] in shape->dtype.  Call it between steps on the
+ * step's stream; every later call sees the grown length.
+ */
+skv_status sparse_kv_append(const skv_shape *shape, const void *new_k, const void *new_v, int32_t *seq_lens,
+                            void *keys, void *values, void *meta, const int32_t *slot_block, int32_t capacity,
+                            void *pool_k, void *pool_v, void *stream);
+
+/*
  * Stage 4: GQA decode attention over the selected blocks.
  *
  * For query head h (kv head j = h / G) and the valid tokens t of the

@@ -24,6 +24,9 @@ FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "
     ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 3, 32),
     ("llama8b_32k", dict(batch=3, ctx=2048 + 16 * 7, budget=256, capacity=40, ragged=True), 4, 0),
     ("quest_128k", dict(batch=2, ctx=8192), 4, 0),
+    # rows just past 2048 and 4096 blocks: the 8- and 16-keys-per-thread variants
+    ("llama8b_32k", dict(batch=1, ctx=32768 + 16 * 5, budget=2048), 3, 0),
+    ("quest_128k", dict(batch=1, ctx=65536 + 16 * 3), 3, 0),
     ("lookahead_1m", dict(ctx=16384), 3, 0),
 ])
 def test_fused_equals_separate_calls(name, kw, steps, splits):

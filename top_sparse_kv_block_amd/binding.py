@@ -31,7 +31,7 @@ EXPORTS = (
     "sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
     "sparse_decode_attention_splits", "sparse_decode_attention_workspace_bytes", "sparse_kv_quest_meta",
     "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
-    "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance",
+    "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append",
 )
 
 
@@ -67,6 +67,7 @@ def load():
                                          _p]
     L.sparse_kv_cache_update_importance.argtypes = [S, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                                     _p, _i32, _p, _p, _p]
+    L.sparse_kv_append.argtypes = [S, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p]
     L.sparse_decode_attention.argtypes = [S, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _i32, _p, _p,
                                           _p, _sz, _p]
     L.sparse_kv_select_attend.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -84,7 +85,7 @@ def load():
     L.sparse_kv_status_string.restype = C.c_char_p
     for fn in ("sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
                "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_select_attend",
-               "sparse_kv_cache_update_importance"):
+               "sparse_kv_cache_update_importance", "sparse_kv_append"):
         getattr(L, fn).restype = C.c_int
     _lib = L
     return L
@@ -216,6 +217,24 @@ def sparse_kv_cache_update_importance(shape, k_blocks, capacity, sel_blocks, sel
         int(src_kind), _ptr(pool_k, dt, "pool_k", allow_none=True, numel=pc * 16 * d),
         _ptr(pool_v, dt, "pool_v", allow_none=True, numel=pc * 16 * d), _stream(stream))
     _check("sparse_kv_cache_update_importance", rc)
+
+
+def sparse_kv_append(shape, new_k, new_v, seq_lens, keys, values, meta=None, slot_block=None, capacity=0,
+                     pool_k=None, pool_v=None, stream=None):
+    """Store one new token per sequence at seq_lens[b] (which grows by one on
+    the device), keep the Quest boxes exact and refresh resident pool slots."""
+    dt = _torch_dtype(shape.dtype)
+    b, hkv, d, t = shape.batch, shape.n_kv_heads, shape.head_dim, shape.max_ctx
+    P = b * hkv
+    rc = load().sparse_kv_append(
+        C.byref(shape), _ptr(new_k, dt, "new_k", numel=P * d), _ptr(new_v, dt, "new_v", numel=P * d),
+        _ptr(seq_lens, torch.int32, "seq_lens", numel=b), _ptr(keys, dt, "keys", numel=P * t * d),
+        _ptr(values, dt, "values", numel=P * t * d),
+        _ptr(meta, dt, "meta", allow_none=True, numel=P * (t // 16) * 2 * d),
+        _ptr(slot_block, torch.int32, "slot_block", allow_none=True, numel=P * int(capacity)), int(capacity),
+        _ptr(pool_k, dt, "pool_k", allow_none=True, numel=P * int(capacity) * 16 * d),
+        _ptr(pool_v, dt, "pool_v", allow_none=True, numel=P * int(capacity) * 16 * d), _stream(stream))
+    _check("sparse_kv_append", rc)
 
 
 def sparse_decode_attention(shape, q, pool_k, pool_v, capacity, sel_blocks, sel_slot, sel_hit, sel_count, seq_lens,

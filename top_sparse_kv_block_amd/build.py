@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsparse_kv.so")
-SOURCES = ["abi.hip", "score.hip", "topk.hip", "cache.hip", "attention.hip"]
+SOURCES = ["abi.hip", "score.hip", "topk.hip", "cache.hip", "attention.hip", "append.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

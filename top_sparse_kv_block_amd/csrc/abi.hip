@@ -140,6 +140,27 @@ SKV_API skv_status sparse_kv_cache_update_importance(const skv_shape *shape, int
                              pool_v, stream);
 }
 
+SKV_API skv_status sparse_kv_append(const skv_shape *shape, const void *new_k, const void *new_v, int32_t *seq_lens,
+                                    void *keys, void *values, void *meta, const int32_t *slot_block, int32_t capacity,
+                                    void *pool_k, void *pool_v, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!new_k || !new_v || !seq_lens || !keys || !values)
+        return SKV_ERR_NULL;
+    if (slot_block) {
+        if (!pool_k || !pool_v)
+            return SKV_ERR_NULL;
+        if (capacity < 1)
+            return SKV_ERR_SHAPE;
+        if (capacity > skv::kMaxCapacity)
+            return SKV_ERR_UNSUPPORTED;
+    }
+    return hip_status(skv::launch_append(d, new_k, new_v, seq_lens, keys, values, meta, slot_block,
+                                         slot_block ? capacity : 0, pool_k, pool_v, (hipStream_t)stream));
+}
+
 SKV_API int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k_blocks) {
     Dims d;
     if (check_shape(shape, d) != SKV_OK || k_blocks < 1)

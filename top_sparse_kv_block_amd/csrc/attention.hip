@@ -549,7 +549,7 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_waves(GMAX)) void attn_kerne
 // registers) where the top-k keys and the head state are small enough,
 // else 2.  The host side (fused_waves_per_simd) applies the same rule.
 template <typename E, int D, int GMAX, int KPT> constexpr int fused_min_waves() {
-    return (E::bytes == 2 && GMAX <= 4 && KPT <= 4) ? 4 : 2;
+    return (E::bytes == 2 && GMAX <= 4 && KPT <= 8) ? 4 : 2;
 }
 
 // Blocks of K and V a wave of the fused kernel holds at once (see
@@ -727,7 +727,7 @@ int attention_auto_splits(int rows, int k) {
 // prefers as many workgroups as are resident at once (one or two per CU,
 // see fused_min_waves), each wave streaming several blocks.
 int fused_waves_per_simd(const Dims &d) {
-    return (d.dtype == 1 && d.G() <= 4 && d.NB <= kAttnThreads * 4) ? 4 : 2;
+    return (d.dtype == 1 && d.G() <= 4 && d.NB <= kAttnThreads * 8) ? 4 : 2;
 }
 
 int fused_auto_splits(const Dims &d, int k) {
@@ -805,6 +805,8 @@ template <typename E, int D, int GMAX>
 static hipError_t fused_k(const Dims &d, const FusedArgs &f, hipStream_t st) {
     if (d.NB <= kAttnThreads * 4)
         return fused_t<E, D, GMAX, 4>(d, f, st);
+    if (d.NB <= kAttnThreads * 8)
+        return fused_t<E, D, GMAX, 8>(d, f, st);
     return fused_t<E, D, GMAX, 16>(d, f, st);
 }
 

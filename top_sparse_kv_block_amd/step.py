@@ -115,6 +115,15 @@ class LayerBuffers:
                                  self.miss_slot, self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
                                  stream)
 
+    def append(self, new_k, new_v, seq_lens, keys, values, meta=None, stream=None):
+        """Append one token per sequence (seq_lens grows on the device); the
+        pool copies of resident blocks stay current."""
+        c = self.cfg
+        with_pool = self.pool_k is not None
+        B.sparse_kv_append(self.shape, new_k, new_v, seq_lens, keys, values, meta,
+                           self.slot_block if with_pool else None, c.capacity if with_pool else 0, self.pool_k,
+                           self.pool_v, stream)
+
     def attention(self, q, seq_lens, src_k=None, src_v=None, src_kind=B.SKV_SRC_DEVICE, stream=None):
         """With src_k/src_v the misses are fetched here (fetch on attend)."""
         c = self.cfg
