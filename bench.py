@@ -248,12 +248,18 @@ def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
     has its own working set and selections, so the transfers are the same
     as with distinct host layers).  Step 0 (cold) is not timed.  Reports the
     host->device rate of the misses for the separate gather and for fetch on
-    attend, beside a plain pinned hipMemcpyAsync of 256 MiB."""
+    attend, beside a plain pinned hipMemcpyAsync of 256 MiB, and the layer
+    loop with the cross-layer prefetch (layer l+1's working set takes layer
+    l's picks on a second stream while layer l attends): the misses left on
+    each layer's critical path, the blocks prefetched, and the time of each
+    layer's own update (the stall once its selection is known) with and
+    without it.  Layer 0 of each step has no earlier layer and is left out
+    of these per-layer figures."""
     import torch
 
     from top_sparse_kv_block_amd import binding as B
     from top_sparse_kv_block_amd import synth
-    from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
+    from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig, layer_sweep
 
     w = synth.WORKLOADS["host_tier_32l"].scaled(layers=layers, steps=steps)
     t0 = time.time()
@@ -279,7 +285,43 @@ def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
         setup_s = time.time() - t0
         blk2 = 2 * 16 * w.head_dim * w.elem_bytes  # K + V bytes of one block
 
-        def run_mode(mode):
+        srcs = [(hk.device_ptr, hv.device_ptr)] * layers
+        side = torch.cuda.Stream()
+
+        def run_sweep(prefetch):
+            # the layer loop of one decode step (layer_sweep); with prefetch,
+            # layer l+1's working set takes layer l's picks on a second stream
+            for b in bufs:
+                b.reset()
+            evs, walls = [], []
+            misses = torch.zeros(steps, layers, 2, dtype=torch.int64, device="cuda")
+            for s in range(steps):
+                for l, b in enumerate(bufs):
+                    b.sel_blocks.copy_(sels[s, l])
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+                rec = []
+                layer_sweep(bufs, q, lens, srcs, B.SKV_SRC_HOST_MAPPED, prefetch=prefetch, side_stream=side,
+                            events=rec)
+                e[1].record()
+                for l, b in enumerate(bufs):
+                    misses[s, l, 0] = b.miss_count.sum()
+                    if prefetch and l > 0:
+                        misses[s, l, 1] = b.pf_miss_count.sum()
+                evs.append(rec)
+                walls.append(e)
+            torch.cuda.synchronize()
+            # steps after the cold one; layers after the first (the first has no earlier layer)
+            upd = sum(r[l]["update"][0].elapsed_time(r[l]["update"][1]) for r in evs[1:] for l in range(1, layers))
+            pf = sum(r[l]["prefetch"][0].elapsed_time(r[l]["prefetch"][1]) for r in evs[1:]
+                     for l in range(layers - 1)) if prefetch else 0.0
+            wall = sum(a.elapsed_time(b) for a, b in walls[1:])
+            m = misses[1:, 1:].sum(dim=(0, 1)).tolist()
+            n = (steps - 1) * (layers - 1)
+            return dict(crit=m[0] / n, pf=m[1] / n, update_us=upd * 1e3 / n, prefetch_us=pf * 1e3 / n,
+                        wall_us_per_layer=wall * 1e3 / ((steps - 1) * layers), m_total=m[0], upd_ms=upd)
+
+        def run_fetch_on_attend():
             for b in bufs:
                 b.reset()
             ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers * steps)]
@@ -288,24 +330,19 @@ def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
                 for l, b in enumerate(bufs):
                     b.sel_blocks.copy_(sels[s, l])
                     e = ev[s * layers + l]
-                    if mode == "gather":
-                        e[0].record()
-                        b.cache_update(hk.device_ptr, hv.device_ptr, B.SKV_SRC_HOST_MAPPED)
-                        e[1].record()
-                        b.attention(q, lens)
-                    else:
-                        b.cache_update(None, None)
-                        e[0].record()
-                        b.attention(q, lens, hk.device_ptr, hv.device_ptr, B.SKV_SRC_HOST_MAPPED)
-                        e[1].record()
+                    b.cache_update(None, None)
+                    e[0].record()
+                    b.attention(q, lens, hk.device_ptr, hv.device_ptr, B.SKV_SRC_HOST_MAPPED)
+                    e[1].record()
                     misses[s, l] = b.miss_count.sum()
             torch.cuda.synchronize()
             us = sum(e[0].elapsed_time(e[1]) for e in ev[layers:]) * 1e3
             m = int(misses[1:].sum().item())
             return m, us
 
-        m_g, us_g = run_mode("gather")
-        m_f, us_f = run_mode("fetch_on_attend")
+        plain = run_sweep(False)
+        cross = run_sweep(True)
+        m_f, us_f = run_fetch_on_attend()
         # plain pinned copy, 256 MiB, for scale
         n_c = 128 << 20
         src = torch.from_numpy(hk.numpy(np.int16, (n_c,)))
@@ -320,14 +357,25 @@ def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
         torch.cuda.synchronize()
         memcpy_gbps = 4 * n_c * 2 / (c0.elapsed_time(c1) * 1e-3) / 1e9
         timed = (steps - 1) * layers
+        n_l = (steps - 1) * (layers - 1)
         return {
             "workload": w.name,
             "rows": w.rows, "ctx": w.ctx, "k_blocks": w.k_blocks, "capacity_slots": w.capacity,
             "layers_run": layers, "timed_layer_steps": timed,
             "host_source": "one layer's K and V (8 GiB) in pinned mapped host memory, read by every layer",
-            "miss_blocks_per_layer": round(m_g / timed, 1),
-            "gather_h2d_gbps": round(m_g * blk2 / (us_g * 1e-6) / 1e9, 2),
-            "gather_us_per_layer": round(us_g / timed, 1),
+            "miss_blocks_per_layer": round(plain["crit"], 1),
+            "gather_h2d_gbps": round(plain["m_total"] * blk2 / (plain["upd_ms"] * 1e-3) / 1e9, 2),
+            "gather_us_per_layer": round(plain["update_us"], 1),
+            "cross_layer_prefetch": {
+                "critical_miss_blocks_per_layer": round(cross["crit"], 1),
+                "prefetched_blocks_per_layer": round(cross["pf"], 1),
+                "critical_update_us_per_layer": round(cross["update_us"], 1),
+                "prefetch_us_per_layer": round(cross["prefetch_us"], 1),
+                "miss_stall_hidden": round(1.0 - cross["update_us"] / plain["update_us"], 3),
+                "sweep_us_per_layer": round(cross["wall_us_per_layer"], 1),
+                "sweep_us_per_layer_without": round(plain["wall_us_per_layer"], 1),
+                "layers_counted": n_l,
+            },
             "fetch_on_attend_h2d_gbps": round(m_f * blk2 / (us_f * 1e-6) / 1e9, 2),
             "attention_with_fetch_us_per_layer": round(us_f / timed, 1),
             "pinned_memcpy_h2d_gbps": round(memcpy_gbps, 2),

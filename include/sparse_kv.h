@@ -183,6 +183,13 @@ skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int
  * outside [0, NB), a count outside [0, k_blocks], or a corrupt slot table:
  * an id outside [-1, NB), or a selected block held by two slots) leaves the
  * row untouched and sets miss_count = -1 for it.
+ * Cross-layer prefetch (HiSparse promo, insight 3: picks overlap between
+ * layers, so the previous layer's picks are fetched for the next layer
+ * before its own are known): call this for layer l+1's state and source with
+ * layer l's sel_blocks / sel_count, on a second stream while layer l
+ * attends, with separate list outputs.  It is an ordinary update (clock tick
+ * and stamps included); layer l+1's own update then finds the shared blocks
+ * resident.  The two calls on one layer's state must not overlap in time.
  * Limits: 1 <= k_blocks <= capacity <= 1024.
  */
 skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int32_t capacity,

@@ -100,6 +100,73 @@ def test_host_tier_layers_reduced(mode):
             L["hv"].free()
 
 
+@pytest.mark.parametrize("prefetch", [False, True])
+def test_layer_sweep_cross_layer_prefetch(prefetch):
+    # one decode step over consecutive layers (each with its own host K/V and
+    # working set); with prefetch, layer l+1's set is first updated with layer
+    # l's selection on a second stream.  The oracle: the same two LRU steps.
+    from top_sparse_kv_block_amd.step import layer_sweep
+    w = synth.WORKLOADS["host_tier_32l"].scaled(batch=2, ctx=16384, layers=3, steps=3)
+    sels = synth.gen_layer_selections(w)
+    P, k, C, nb = w.rows, w.k_blocks, w.capacity, w.nb_max
+    lens = synth.gen_seq_lens(w)
+    dlens = dev(lens)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    cnt = np.full((w.batch, w.n_kv_heads), k, dtype=np.int32)
+    side = torch.cuda.Stream()
+    Ks, Vs, qs, hbs, bufs, lrus = [], [], [], [], [], []
+    try:
+        for l in range(w.layers):
+            K, V = synth.gen_kv(w, l)
+            q, _ = synth.gen_queries(w, l)
+            Ks.append(K), Vs.append(V), qs.append(q)
+            hbs.append((_host_copy(K), _host_copy(V)))
+            cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, k, C)
+            bufs.append(LayerBuffers(cfg))
+            lrus.append(oracle.LRU(P, C))
+        srcs = [(hk.device_ptr, hv.device_ptr) for hk, hv in hbs]
+        for s in range(w.steps):
+            log("layer sweep, prefetch", prefetch, "step", s)
+            for l, buf in enumerate(bufs):
+                buf.sel_blocks.copy_(dev(sels[s, l]))
+                buf.sel_count.copy_(dev(cnt))
+            layer_sweep(bufs, [dev(q[s]) for q in qs], dlens, srcs, B.SKV_SRC_HOST_MAPPED, prefetch=prefetch,
+                        side_stream=side)
+            torch.cuda.synchronize()
+            for l, buf in enumerate(bufs):
+                if prefetch and l > 0:
+                    pf = lrus[l].step(sels[s, l - 1].reshape(P, k), cnt.reshape(P), nb)
+                    np.testing.assert_array_equal(host(buf.pf_miss_count).reshape(P), pf["miss_count"])
+                    np.testing.assert_array_equal(host(buf.pf_miss_block).reshape(P, k), pf["miss_block"])
+                out = lrus[l].step(sels[s, l].reshape(P, k), cnt.reshape(P), nb)
+                for name in ("sel_slot", "sel_hit", "miss_block", "miss_slot"):
+                    np.testing.assert_array_equal(host(getattr(buf, name)).reshape(P, k), out[name], name)
+                np.testing.assert_array_equal(host(buf.miss_count).reshape(P), out["miss_count"])
+                np.testing.assert_array_equal(host(buf.slot_block).reshape(P, C), lrus[l].slot_block())
+                if s > 0 and l > 0:
+                    # the shared blocks were fetched ahead: about half of the misses remain
+                    now, prev = sels[s, l].reshape(P, k), sels[s - 1, l].reshape(P, k)
+                    new = sum(len(set(a) - set(b)) for a, b in zip(now, prev))
+                    frac = out["miss_count"].sum() / new
+                    assert (frac < 0.75) if prefetch else (frac > 0.75), frac
+                pk = host(buf.pool_k).reshape(P, C, 16, w.head_dim)
+                pv = host(buf.pool_v).reshape(P, C, 16, w.head_dim)
+                sb = lrus[l].slot_block()
+                for r_ in range(P):
+                    b, j = divmod(r_, w.n_kv_heads)
+                    for slot, blk in enumerate(sb[r_]):
+                        if blk >= 0:
+                            assert np.array_equal(pk[r_, slot], Ks[l][b, j, 16 * blk:16 * blk + 16])
+                            assert np.array_equal(pv[r_, slot], Vs[l][b, j, 16 * blk:16 * blk + 16])
+                o_ref, _ = oracle.attention(qs[l][s], Ks[l], Vs[l], sels[s, l], cnt, lens, scale)
+                assert max_rel_row_err(host(buf.out), o_ref) <= 1e-4
+    finally:
+        torch.cuda.synchronize()
+        for hk, hv in hbs:
+            hk.free()
+            hv.free()
+
+
 def test_host_source_equals_device_source_bit_exact():
     # the tier does not change any result: the same step from a host-mapped
     # and from a device source gives identical lists, pools and outputs

@@ -115,6 +115,25 @@ class LayerBuffers:
                                  self.miss_slot, self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
                                  stream)
 
+    def prefetch(self, hint: "LayerBuffers", src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None):
+        """Cross-layer prefetch: an ordinary working-set update of this layer
+        with another layer's selection (hint.sel_blocks / hint.sel_count) as
+        the pick, fetching its misses from this layer's source.  Blocks the
+        layers share are then hits for this layer's own update.  Its lists go
+        to separate buffers (pf_*), so the layer's own lists are untouched."""
+        c = self.cfg
+        if not hasattr(self, "pf_miss_count"):
+            bh, k = self.sel_blocks.shape[:2], c.k_blocks
+            self.pf_sel_slot = torch.empty(*bh, k, dtype=torch.int32, device=self.sel_blocks.device)
+            self.pf_sel_hit = torch.empty(*bh, k, dtype=torch.uint8, device=self.sel_blocks.device)
+            self.pf_miss_block = torch.empty_like(self.pf_sel_slot)
+            self.pf_miss_slot = torch.empty_like(self.pf_sel_slot)
+            self.pf_miss_count = torch.empty(*bh, dtype=torch.int32, device=self.sel_blocks.device)
+        B.sparse_kv_cache_update(self.shape, c.k_blocks, c.capacity, hint.sel_blocks, hint.sel_count,
+                                 self.slot_block, self.slot_stamp, self.clock, self.pf_sel_slot, self.pf_sel_hit,
+                                 self.pf_miss_block, self.pf_miss_slot, self.pf_miss_count, src_k, src_v, src_kind,
+                                 self.pool_k, self.pool_v, stream)
+
     def append(self, new_k, new_v, seq_lens, keys, values, meta=None, stream=None):
         """Append one token per sequence (seq_lens grows on the device); the
         pool copies of resident blocks stay current."""
@@ -163,3 +182,47 @@ def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, sr
         buf.cache_update(src_k, src_v, src_kind, stream)
         buf.attention(q, seq_lens, stream=stream)
 
+
+def layer_sweep(bufs, q, seq_lens, srcs, src_kind=B.SKV_SRC_DEVICE, prefetch=False, side_stream=None, events=None):
+    """Enqueue one decode step over consecutive layers whose selections are
+    already in ``bufs[l].sel_blocks`` / ``sel_count`` (a selector outside
+    the library picked them).  Per layer: working-set update with the miss
+    fetch from ``srcs[l] = (src_k, src_v)``, then attention over the pool.
+
+    prefetch=True adds the cross-layer prefetch: once layer l's own fetch is
+    done, layer l+1's working set is updated with layer l's selection on
+    ``side_stream`` (fetching layer l+1's bytes of those blocks) while layer
+    l attends; layer l+1's own update waits for it and then finds the shared
+    blocks resident.  ``events``, if a list, receives per layer a dict of
+    (start, end) timing events: "update" (the layer's own update, current
+    stream) and, with prefetch, "prefetch" (the next layer's, side stream).
+    """
+    main = torch.cuda.current_stream()
+    if prefetch and side_stream is None:
+        raise ValueError("prefetch needs a side stream")
+    timed = events is not None
+
+    def ev():
+        return torch.cuda.Event(enable_timing=timed)
+
+    pf_done = [None] * len(bufs)
+    for l, buf in enumerate(bufs):
+        if pf_done[l] is not None:
+            main.wait_event(pf_done[l])
+        rec = {"update": (ev(), ev())}
+        rec["update"][0].record(main)
+        buf.cache_update(*srcs[l], src_kind)
+        rec["update"][1].record(main)
+        if prefetch and l + 1 < len(bufs):
+            side_stream.wait_event(rec["update"][1])
+            rec["prefetch"] = (ev(), ev())
+            rec["prefetch"][0].record(side_stream)
+            with torch.cuda.stream(side_stream):
+                bufs[l + 1].prefetch(buf, *srcs[l + 1], src_kind, side_stream)
+            rec["prefetch"][1].record(side_stream)
+            pf_done[l + 1] = rec["prefetch"][1]
+        buf.attention(q[l] if isinstance(q, (list, tuple)) else q, seq_lens)
+        if timed:
+            events.append(rec)
+    if prefetch:
+        main.wait_stream(side_stream)
