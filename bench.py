@@ -393,9 +393,12 @@ def run(args):
 
     from top_sparse_kv_block_amd import binding as B
     from top_sparse_kv_block_amd import synth
-    from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
+    from top_sparse_kv_block_amd.step import Lag1Pipeline, LayerBuffers, StepConfig
 
     w = synth.WORKLOADS[args.workload]
+    if args.lag1:
+        # lag-1 keeps the previous selection resident while the next update runs: 2k slots
+        w = w.scaled(capacity=max(w.capacity, 2 * w.k_blocks))
     if w.scoring == "given":
         raise SystemExit("the host-tier workload has no scoring stage; its PCIe fetch is the host_fetch leg")
     nsteps = args.warmup + args.steps
@@ -439,7 +442,11 @@ def run(args):
     shape, st = cfg.shape, None
     scale = cfg.softmax_scale
 
+    pipe = Lag1Pipeline(buf) if args.lag1 else None
+
     def step(t, ev=None):
+        if pipe is not None:
+            return step_lag1(t, ev)
         if args.fused:
             return step_fused(t, ev)
         # ev: optional list of 5 events bracketing the four calls (profiling pass only)
@@ -473,6 +480,18 @@ def run(args):
         if ev is not None:
             ev[4].record()
 
+    def step_lag1(t, ev=None):
+        # attention over the previous step's selection on this stream; score,
+        # top-k and the working-set update of this step on the side stream.
+        # ev brackets the whole step (the two streams overlap)
+        if ev is not None:
+            ev[0].record()
+        pipe.step(q_all[t], sq_all[t], keys_or_meta, dlens, dK, dV, B.SKV_SRC_DEVICE, miss_count=miss_log[t])
+        if ev is not None:
+            pipe.join()
+            for e in ev[1:]:
+                e.record()
+
     appended = [0]
 
     def grow():
@@ -503,9 +522,14 @@ def run(args):
                 e.record()
 
     # cold start, warm-up (not timed)
-    buf.reset()
+    if pipe is not None:
+        pipe.reset()
+    else:
+        buf.reset()
     for t in range(args.warmup):
         step(t)
+    if pipe is not None:
+        pipe.join()
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronised on both sides.  By
@@ -518,6 +542,8 @@ def run(args):
         with torch.cuda.graph(graph):
             for i in range(args.steps):
                 step(args.warmup + i)
+            if pipe is not None:
+                pipe.join()
         torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -528,6 +554,8 @@ def run(args):
     else:
         for i in range(args.steps):
             step(args.warmup + i)
+        if pipe is not None:
+            pipe.join()
     t_enq = time.perf_counter() - t0
     e1.record()
     torch.cuda.synchronize()
@@ -596,10 +624,12 @@ def run(args):
         "miss_blocks_per_step": round(misses / args.steps, 1),
         "mode": "hip-graph replay" if graph is not None else "eager",
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
-        "path": "score + fused select/update/attend" if args.fused else "four calls",
+        "path": ("lag-1 pipeline: attention over the previous selection || score, top-k, update on a second stream"
+                 if pipe is not None else "score + fused select/update/attend" if args.fused else "four calls"),
         "eviction": args.eviction,
         "grow": bool(args.grow),
-        "stage_us": ({"score": round(float(stage[:, 0].mean()), 2),
+        "stage_us": ({"step": round(float(stage.sum(axis=1).mean()), 2)} if pipe is not None else
+                     {"score": round(float(stage[:, 0].mean()), 2),
                       "select_update_attend": round(float(stage[:, 1].mean()), 2)} if args.fused else
                      {name: round(float(v), 2) for name, v in
                       zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))}),
@@ -631,6 +661,9 @@ def main(argv=None):
                     help="working-set eviction; importance (by this step's scores) runs the four calls")
     ap.add_argument("--grow", action="store_true",
                     help="append one token per sequence before every step (decode-time growth; Quest boxes kept)")
+    ap.add_argument("--lag1", action="store_true",
+                    help="lag-1 pipeline: each step attends over the previous step's selection while its own "
+                         "score, top-k and update run on a second stream (capacity raised to 2k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-fetch", action="store_true", help="skip the host-tier PCIe fetch measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -641,6 +674,11 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.eviction == "importance":
         args.fused = False  # the fused call evicts LRU only
+    if args.lag1:
+        if args.grow or args.eviction != "lru":
+            raise SystemExit("--lag1 runs on a fixed-length cache with LRU eviction")
+        args.fused = False
+        args.no_cpu_baseline = True  # the oracle leg replays the synchronous step
     if args.grow:
         args.no_cpu_baseline = True  # the oracle leg replays the fixed-length workload
     if args.traffic_summary:

@@ -285,3 +285,12 @@ def attention_pool(q, pool_k, pool_v, sel, sel_slot, sel_count, seq_lens, scale,
                                      _ptr(lse))
     assert rc == 0
     return out, lse
+
+
+def lagged(per_step, lag=1):
+    """The lag-1 schedule ("KV Cache 塞不进 HBM 了", §2.1 and the §3 loop: the
+    forward attends over the KV readied at the previous step while the next
+    retrieval runs): step t attends over the selection made at step t - lag,
+    and the first steps, which have none, over step 0's.  ``per_step`` is a
+    sequence indexed by step (selections, counts, ...)."""
+    return [per_step[max(t - lag, 0)] for t in range(len(per_step))]

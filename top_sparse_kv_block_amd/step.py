@@ -161,6 +161,97 @@ class LayerBuffers:
                                   self.fused_splits, self.out, self.lse, self.workspace, stream)
 
 
+class _Lists:
+    """One set of per-step lists: the selection and the working-set plan."""
+
+    def __init__(self, buf: LayerBuffers, own: bool):
+        names = ("sel_blocks", "sel_count", "sel_slot", "sel_hit", "miss_block", "miss_slot", "miss_count")
+        for n in names:
+            t = getattr(buf, n)
+            setattr(self, n, t if own else torch.empty_like(t))
+
+
+class Lag1Pipeline:
+    """Lag-1 decode of one layer: attention at step t runs over the selection
+    made at step t-1 (the first step over its own) on the current stream,
+    while step t's score, top-k and working-set update run on a side stream.
+    The retrieval for the next step thus overlaps the attention, which uses
+    the KV readied at the step before ("KV Cache 塞不进 HBM 了", §2.1 and the
+    §3 loop).
+
+    The working set needs capacity >= 2k and LRU eviction: the update of step
+    t then never evicts a block of S_{t-1}, which attention at step t may be
+    reading or filling (the victims are the least recently used blocks
+    outside S_t; S_{t-1}'s blocks carry the newest stamps, and at most
+    |S_t - S_{t-1}| + |S_{t-1}| <= 2k slots are needed).  The update only
+    builds lists; attention fetches the misses of the selection it attends
+    over from the source (fetch on attend).  Two list sets alternate between
+    steps.  Results of a step are complete on the current stream after
+    :meth:`join`.
+    """
+
+    def __init__(self, buf: LayerBuffers, side_stream=None):
+        c = buf.cfg
+        if c.capacity < 2 * c.k_blocks:
+            raise ValueError(f"lag-1 needs capacity >= 2*k_blocks ({c.capacity} < {2 * c.k_blocks})")
+        self.buf = buf
+        self.side = side_stream if side_stream is not None else torch.cuda.Stream()
+        self.lists = [_Lists(buf, True), _Lists(buf, False)]
+        self.t = 0
+        self._upd_prev = None
+
+    def reset(self):
+        self.buf.reset()
+        self.t = 0
+        self._upd_prev = None
+
+    def attended(self) -> _Lists:
+        """The list set the last step's attention used."""
+        return self.lists[max(self.t - 2, 0) % 2]
+
+    def step(self, q, score_q, keys_or_meta, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE, miss_count=None):
+        """Enqueue step t.  ``miss_count`` (optional [B, Hkv] int32) receives
+        this step's update's miss counts instead of the list set's own."""
+        buf, c = self.buf, self.buf.cfg
+        main, side = torch.cuda.current_stream(), self.side
+        cur = self.lists[self.t % 2]
+        # the side stream sees the caller's inputs and the previous step's
+        # attention (which read the list set written below)
+        side.wait_stream(main)
+        if not torch.cuda.is_current_stream_capturing():
+            for t in (score_q, keys_or_meta, seq_lens, miss_count):
+                if isinstance(t, torch.Tensor):
+                    t.record_stream(side)  # the allocator must not reuse them while the side stream reads
+        with torch.cuda.stream(side):
+            B.sparse_kv_score(buf.shape, c.mode, score_q, c.n_queries, keys_or_meta, seq_lens, c.softmax_scale,
+                              buf.scores, side)
+            B.sparse_kv_topk(buf.shape, buf.scores, seq_lens, c.k_blocks, c.sink, c.recent, cur.sel_blocks,
+                             cur.sel_count, side)
+            B.sparse_kv_cache_update(buf.shape, c.k_blocks, c.capacity, cur.sel_blocks, cur.sel_count,
+                                     buf.slot_block, buf.slot_stamp, buf.clock, cur.sel_slot, cur.sel_hit,
+                                     cur.miss_block, cur.miss_slot,
+                                     cur.miss_count if miss_count is None else miss_count, None, None, src_kind,
+                                     buf.pool_k, buf.pool_v, side)
+        upd = torch.cuda.Event()
+        upd.record(side)
+        use = self.lists[(self.t - 1) % 2] if self.t > 0 else cur
+        if self.t == 0:
+            main.wait_event(upd)
+        elif self._upd_prev is not None:  # None: already ordered by join()
+            main.wait_event(self._upd_prev)
+        B.sparse_decode_attention(buf.shape, q, buf.pool_k, buf.pool_v, c.capacity, use.sel_blocks, use.sel_slot,
+                                  use.sel_hit, use.sel_count, seq_lens, c.k_blocks, c.softmax_scale, buf.splits,
+                                  src_k, src_v, src_kind, buf.out, buf.lse, buf.workspace, main)
+        self._upd_prev = upd
+        self.t += 1
+
+    def join(self):
+        """Make the current stream wait for the side stream's work (call it
+        before reading a step's lists, and before a graph capture ends)."""
+        torch.cuda.current_stream().wait_stream(self.side)
+        self._upd_prev = None
+
+
 def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE,
                 stream=None, fetch_on_attend=True, fused=False):
     """Enqueue one full step: score, top-k, cache update, attention.
