@@ -77,10 +77,11 @@ def step_bytes(w, misses: float) -> dict:
 
 
 def score_launch_bytes(w) -> int:
-    """Bytes one scoring launch must move: per block 16*D*e of keys plus its
-    4-byte score, times P*NB blocks, plus the scoring queries."""
-    return w.rows * w.nb_max * (16 * w.head_dim * w.elem_bytes + 4) + \
-        w.batch * w.n_score_queries * w.n_q_heads * w.head_dim * w.elem_bytes
+    """Bytes one scoring launch must move: per block 16*D*e of keys (the
+    Quest bound: its 2*D*e min/max box) plus its 4-byte score, times P*NB
+    blocks, plus the scoring queries."""
+    per_block = (2 if w.scoring == "quest" else 16) * w.head_dim * w.elem_bytes + 4
+    return w.rows * w.nb_max * per_block + w.batch * w.n_score_queries * w.n_q_heads * w.head_dim * w.elem_bytes
 
 
 def _score_kernel_name(w) -> str:

@@ -40,6 +40,11 @@ template <> __device__ __forceinline__ float groups_max<32>(float v) { return xo
 constexpr int kScoreWaves = 16;
 constexpr int kScoreBlocksPerWave = 4;
 constexpr int kScoreThreads = 64 * kScoreWaves;
+// the Quest scan keeps 8 boxes in flight per lane (76 VGPRs): smaller
+// workgroups let six waves per SIMD stay resident
+constexpr int kQuestWaves = 4;
+constexpr int kQuestThreads = 64 * kQuestWaves;
+constexpr int kQuestBlocksPerWave = 4;  // wave iterations, each BPL blocks
 
 template <typename E, int D, int RMAX>
 __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uint8_t *__restrict__ q,
@@ -208,7 +213,7 @@ template <> __device__ __forceinline__ uint32_t neg_mask<F32>(uint32_t qw) {
 }
 
 template <typename E, int D, int RMAX>
-__global__ __launch_bounds__(kScoreThreads) void score_quest_kernel(const uint8_t *__restrict__ q,
+__global__ __launch_bounds__(kQuestThreads) void score_quest_kernel(const uint8_t *__restrict__ q,
                                                           const uint8_t *__restrict__ meta,
                                                           const int32_t *__restrict__ seq_lens,
                                                           float *__restrict__ scores, int Hq, int Hkv, int NQ, int T,
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_quest_kernel(const uint8_
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPT, bg = lane / LPT;
 
-    u32x4 qf[RMAX], qm[RMAX];
+    u32x4 qf[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
         if (r < R) {
@@ -232,35 +237,42 @@ __global__ __launch_bounds__(kScoreThreads) void score_quest_kernel(const uint8_
         } else {
             qf[r] = u32x4{0, 0, 0, 0};
         }
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            qm[r][w] = neg_mask<E>(qf[r][w]);
     }
     const int len = min(max(seq_lens[b], 0), T);
     const int nvalid = nb_of(len);
     const size_t vec_bytes = (size_t)D * E::bytes;
     const uint8_t *mrow = meta + (size_t)row * NB * 2 * vec_bytes;
     float *srow = scores + (size_t)row * NB;
-    const int per_wg = kScoreWaves * BPL * kScoreBlocksPerWave;
+    const int per_wg = kQuestWaves * BPL * kQuestBlocksPerWave;
     const int n0 = wgp * per_wg;
     const int n1 = min(n0 + per_wg, NB);
 
-    for (int nb = n0 + wave * BPL; nb < n1; nb += kScoreWaves * BPL) {
-        const int n = nb + bg;
-        const bool in = n < n1 && n < nvalid;
-        u32x4 lo = u32x4{0, 0, 0, 0}, hi = u32x4{0, 0, 0, 0};
-        if (in) {
-            lo = load_nt(mrow + (size_t)n * 2 * vec_bytes + sub * 16);
-            hi = load_nt(mrow + (size_t)n * 2 * vec_bytes + vec_bytes + sub * 16);
+    // all of the wave's boxes are loaded before any is used, so each wave
+    // keeps kQuestBlocksPerWave loads in flight instead of one
+    u32x4 lo[kQuestBlocksPerWave], hi[kQuestBlocksPerWave];
+#pragma unroll
+    for (int i = 0; i < kQuestBlocksPerWave; ++i) {
+        const int n = n0 + (i * kQuestWaves + wave) * BPL + bg;
+        lo[i] = hi[i] = u32x4{0, 0, 0, 0};
+        if (n < n1 && n < nvalid) {
+            lo[i] = load_nt(mrow + (size_t)n * 2 * vec_bytes + sub * 16);
+            hi[i] = load_nt(mrow + (size_t)n * 2 * vec_bytes + vec_bytes + sub * 16);
         }
+    }
+#pragma unroll
+    for (int i = 0; i < kQuestBlocksPerWave; ++i) {
+        const int n = n0 + (i * kQuestWaves + wave) * BPL + bg;
+        const bool in = n < n1 && n < nvalid;
         float best = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < RMAX; ++r) {
             if (r < R) {
                 u32x4 corner;
 #pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    corner[w] = (lo[w] & qm[r][w]) | (hi[w] & ~qm[r][w]);
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t m = neg_mask<E>(qf[r][w]);
+                    corner[w] = (lo[i][w] & m) | (hi[i][w] & ~m);
+                }
                 best = fmaxf(best, group_sum<LPT>(dot_chunk<E>(corner, qf[r], 0.0f)));
             }
         }
@@ -403,9 +415,9 @@ template <typename E, int D, int RMAX>
 static hipError_t quest_t(const Dims &d, const void *q, int nq, const void *meta, const int32_t *lens, float scale,
                           float *scores, hipStream_t st) {
     constexpr int LPT = D * E::bytes / 16;
-    const int per_wg = kScoreWaves * (64 / LPT) * kScoreBlocksPerWave;
+    const int per_wg = kQuestWaves * (64 / LPT) * kQuestBlocksPerWave;
     dim3 grid((d.NB + per_wg - 1) / per_wg, d.rows());
-    hipLaunchKernelGGL((score_quest_kernel<E, D, RMAX>), grid, dim3(kScoreThreads), 0, st, (const uint8_t *)q,
+    hipLaunchKernelGGL((score_quest_kernel<E, D, RMAX>), grid, dim3(kQuestThreads), 0, st, (const uint8_t *)q,
                        (const uint8_t *)meta, lens, scores, d.Hq, d.Hkv, nq, d.T, d.NB, scale);
     return hipGetLastError();
 }

@@ -133,6 +133,21 @@ __device__ __forceinline__ float wave_max(float v) {
     return rows_max(v);
 }
 
+// min / max of an unsigned value over the whole wave (all lanes receive it)
+template <bool MAX> __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+    auto pick = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_ROW_ROR8, 0xf, 0xf, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_ROW_ROR4, 0xf, 0xf, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_ROW_ROR2, 0xf, 0xf, false));
+    v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_ROW_ROR1, 0xf, 0xf, false));
+    auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = pick(p[0], p[1]);
+    p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return pick(p[0], p[1]);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_minmax_u32<false>(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_minmax_u32<true>(v); }
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
 // row broadcasts (no LDS round trips).
 template <int CTRL, int ROWMASK> __device__ __forceinline__ uint32_t dpp_zero(uint32_t v) {

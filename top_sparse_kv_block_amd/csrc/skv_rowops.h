@@ -48,6 +48,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 struct TopkScratch {
     uint32_t hist[2][256];  // passes alternate buffers, so clearing needs no barrier of its own
     uint32_t wsum[16];
+    uint32_t wlo[16], whi[16];  // per-wave key range
     uint32_t digit, remaining, n_tau;
 };
 
@@ -76,49 +77,54 @@ __device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remain
 
 // Radix select: the key of the `need`-th largest of the keys flagged in
 // `cand` (KPT per thread; need >= 1 and at most the number of flagged keys).
-// Four 8-bit passes over an LDS histogram; each pass needs two barriers (the
-// histogram buffers alternate, so clearing the next one needs none).
-// Returns the key; `remaining` = how many keys equal to it are admitted,
-// `n_tau` = how many flagged keys equal it.
+// Up to four 8-bit passes over an LDS histogram, on the keys minus the
+// smallest flagged key; each pass needs two barriers (the histogram buffers
+// alternate, so clearing the next one needs none).  Returns the key;
+// `remaining` = how many keys equal to it are admitted, `n_tau` = how many
+// flagged keys equal it.
 template <int THREADS, int KPT>
 __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uint64_t cand, uint32_t need,
                                                  TopkScratch &sc, uint32_t &remaining_out, uint32_t &n_tau_out) {
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0, mask = 0;
-    uint32_t remaining = need, n_tau = 0;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the flagged keys' range [lo, hi]: the passes take the bits of key - lo
+    // from the highest one in which the keys differ, so even the first pass
+    // spreads them over the bins (the leading bits of raw keys are shared by
+    // most scores of a row, and colliding LDS atomics serialise)
+    uint32_t lo = 0xffffffffu, hi = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+        if ((cand >> m) & 1u) {
+            lo = min(lo, key[m]);
+            hi = max(hi, key[m]);
+        }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+        sc.wlo[wave] = lo;
+        sc.whi[wave] = hi;
+    }
     if (tid < 256)
         sc.hist[0][tid] = 0;
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) {
+        lo = min(lo, sc.wlo[w]);
+        hi = max(hi, sc.whi[w]);
+    }
+    const int top = hi > lo ? 32 - __builtin_clz(hi - lo) : 1;  // significant bits of the range
+    const int passes = (top + 7) / 8;
+    uint32_t prefix = 0, mask = 0;
+    uint32_t remaining = need, n_tau = 0;
 #pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int shift = max(top - 8 * (pass + 1), 0);
+        const uint32_t dmask = (1u << (top - 8 * pass - shift)) - 1u;
         uint32_t *hist = sc.hist[pass & 1];
-        if (pass == 0) {
-            // the leading byte (sign and high exponent bits) is shared by
-            // nearly every score of a row: count each distinct digit of
-            // the wave once (ballot) instead of one contended atomic per key
-            const int lane = tid & 63;
 #pragma unroll
-            for (int m = 0; m < KPT; ++m) {
-                const uint32_t dg = key[m] >> 24;
-                bool pending = (cand >> m) & 1u;
-                uint64_t act = __builtin_amdgcn_ballot_w64(pending);
-                while (act) {
-                    const int leader = __builtin_ctzll(act);
-                    const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)dg, leader);
-                    const bool same = pending && dg == dl;
-                    const uint64_t grp = __builtin_amdgcn_ballot_w64(same);
-                    if (lane == leader)
-                        atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(grp));
-                    pending = pending && !same;
-                    act &= ~grp;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < KPT; ++m)
-                if (((cand >> m) & 1u) && (key[m] & mask) == prefix)
-                    atomicAdd(&hist[(key[m] >> shift) & 255u], 1u);
+        for (int m = 0; m < KPT; ++m) {
+            const uint32_t kr = key[m] - lo;
+            if (((cand >> m) & 1u) && (kr & mask) == prefix)
+                atomicAdd(&hist[(kr >> shift) & dmask], 1u);
         }
         if (tid < 256)
             sc.hist[(pass + 1) & 1][tid] = 0;  // last read by the previous pass's pick
@@ -127,13 +133,13 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
             pick_digit(hist, remaining, sc);
         __syncthreads();
         prefix |= sc.digit << shift;
-        mask |= 255u << shift;
+        mask |= dmask << shift;
         remaining = sc.remaining;
         n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
     }
     remaining_out = remaining;
     n_tau_out = n_tau;
-    return prefix;
+    return prefix + lo;
 }
 
 // Per-row selection under the budget (sink + recent blocks forced, the rest
@@ -160,18 +166,45 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
 
     uint32_t key[KPT];
     uint64_t cand = 0, forced = 0;
-#pragma unroll
-    for (int m = 0; m < KPT; ++m) {
-        const int i = tid * KPT + m;
+    const int base = tid * KPT;
+    auto classify = [&](int m, float v) {
+        const int i = base + m;
         key[m] = 0;
         if (i < nvalid) {
             if (i < fs || i >= fr) {
                 forced |= 1ull << m;
             } else {
                 cand |= 1ull << m;
-                key[m] = order_key(srow[i]);
+                key[m] = order_key(v);
             }
         }
+    };
+    if constexpr (KPT >= 16 && KPT % 4 == 0) {
+        // 16-byte loads: a quarter of the load instructions and cache lines
+        // touched (with fewer keys per thread the scalar loads cost little
+        // and the vector form costs registers)
+        const bool vec = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) && base + KPT <= nvalid;
+#pragma unroll
+        for (int u = 0; u < KPT / 4; ++u) {
+            float4 f;
+            if (vec) {
+                f = *reinterpret_cast<const float4 *>(srow + base + 4 * u);
+            } else {
+                const int i = base + 4 * u;
+                f.x = i < nvalid ? srow[i] : 0.0f;
+                f.y = i + 1 < nvalid ? srow[i + 1] : 0.0f;
+                f.z = i + 2 < nvalid ? srow[i + 2] : 0.0f;
+                f.w = i + 3 < nvalid ? srow[i + 3] : 0.0f;
+            }
+            classify(4 * u, f.x);
+            classify(4 * u + 1, f.y);
+            classify(4 * u + 2, f.z);
+            classify(4 * u + 3, f.w);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < KPT; ++m)
+            classify(m, base + m < nvalid ? srow[base + m] : 0.0f);
     }
     uint32_t remaining = 0, n_tau = 0;
     const uint32_t tau = need > 0 ? radix_select<THREADS, KPT>(key, cand, (uint32_t)need, sc, remaining, n_tau) : 0u;
