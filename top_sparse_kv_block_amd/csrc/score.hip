@@ -39,6 +39,13 @@ template <> __device__ __forceinline__ float groups_max<32>(float v) { return xo
 // non-temporal loads were worth another 20%.
 constexpr int kScoreWaves = 16;
 constexpr int kScoreBlocksPerWave = 4;
+// matrix-core scan: blocks per wave with one operand tile (up to 16 query
+// rows) and with two.  Measured: with one tile, one block per wave (more,
+// shorter workgroups) streams fastest (32K: 75-76 us against 77 at 4 and 82
+// at 8); with two tiles, 8 (1M, 4 drafts: 314-322 us against 323-370 at 4)
+constexpr int kMfmaBlocksPerWave1 = 1;
+constexpr int kMfmaBlocksPerWave2 = 8;
+template <int NT> constexpr int mfma_blocks_per_wave() { return NT > 1 ? kMfmaBlocksPerWave2 : kMfmaBlocksPerWave1; }
 constexpr int kScoreThreads = 64 * kScoreWaves;
 // the Quest scan keeps 8 boxes in flight per lane (76 VGPRs): smaller
 // workgroups let six waves per SIMD stay resident
@@ -158,8 +165,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_mfma_kernel(cons
     const int nvalid = nb_of(len);
     const uint8_t *krow = keys + (size_t)row * T * TB;
     float *srow = scores + (size_t)row * NB;
-    const int n0 = wgp * (kScoreWaves * kScoreBlocksPerWave);
-    const int n1 = min(n0 + kScoreWaves * kScoreBlocksPerWave, NB);
+    const int n0 = wgp * (kScoreWaves * mfma_blocks_per_wave<NT>());
+    const int n1 = min(n0 + kScoreWaves * mfma_blocks_per_wave<NT>(), NB);
 
     for (int n = n0 + wave; n < n1; n += kScoreWaves) {
         if (n >= nvalid) {
@@ -373,7 +380,7 @@ static hipError_t blockmax_t(const Dims &d, const void *q, int nq, const void *k
 template <int D, int NT>
 static hipError_t blockmax_mfma_t(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
                                   float scale, float *scores, hipStream_t st) {
-    const int per_wg = kScoreWaves * kScoreBlocksPerWave;
+    const int per_wg = kScoreWaves * mfma_blocks_per_wave<NT>();
     dim3 grid((d.NB + per_wg - 1) / per_wg, d.rows());
     hipLaunchKernelGGL((score_blockmax_mfma_kernel<D, NT>), grid, dim3(kScoreThreads), 0, st, (const uint8_t *)q,
                        (const uint8_t *)keys, lens, scores, d.Hq, d.Hkv, nq, d.T, d.NB, scale);
