@@ -136,3 +136,69 @@ def test_decoding_while_the_cache_grows():
         o_ref, _ = oracle.attention(q, k, v, g_sel, g_cnt, lens, scale)
         err = max_rel_row_err(host(buf.out), o_ref)
         assert err <= 2e-2 and err <= 1e-4, err
+
+
+@pytest.mark.timeout(400)
+def test_growth_full_size_sampled():
+    # the benchmark's growth shape: the 32K workload (8 x 8 rows) with every
+    # sequence full at 32768 tokens and room for more; each step appends one
+    # token per sequence, then scores (exact block max) and runs the fused
+    # call, so the rows pass 2048 blocks.  Checked: lengths and appended rows,
+    # sampled score rows, every row of top-k and of the working set, sampled
+    # attention heads
+    w = synth.WORKLOADS["llama8b_32k"].scaled(steps=1)
+    room = 48
+    T = w.ctx + room
+    r = np.random.default_rng(11)
+    data = synth.gen_workload(w)
+    k = np.zeros((w.batch, w.n_kv_heads, T, w.head_dim), np.uint16)
+    v = np.zeros_like(k)
+    k[:, :, :w.ctx], v[:, :, :w.ctx] = data["K"], data["V"]
+    lens = data["seq_lens"].copy()
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, T, "bf16", w.k_blocks, w.capacity)
+    buf = LayerBuffers(cfg)
+    dk, dv, dl = dev(k), dev(v), dev(lens)
+    lru = oracle.LRU(w.rows, w.capacity)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    P, nb = w.rows, T // 16
+    rows, heads = [0, 37, 63], [(0, 0), (4, 18), (7, 31)]
+    for step in range(4):
+        nk = to_dtype(r.standard_normal((w.batch, w.n_kv_heads, w.head_dim)), "bf16")
+        nv = to_dtype(r.standard_normal((w.batch, w.n_kv_heads, w.head_dim)), "bf16")
+        q = to_dtype(r.standard_normal((w.batch, w.n_q_heads, w.head_dim)), "bf16")
+        log("full-size growth step", step, "len", int(lens[0]))
+        buf.append(dev(nk), dev(nv), dl, dk, dv)
+        oracle.append(nk, nv, lens, k, v)
+        buf.score(dev(q)[:, None], dk, dl)
+        buf.select_attend(dev(q), dl, dk, dv)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(dl), lens)
+        got = host(buf.scores).astype(np.float64)
+        for rr in rows:
+            b, j = divmod(rr, w.n_kv_heads)
+            G = w.group
+            np.testing.assert_array_equal(host(dk[b, j, lens[b] - 1]), k[b, j, lens[b] - 1])
+            ref = oracle.score_blockmax(np.ascontiguousarray(q[b:b + 1, None, j * G:(j + 1) * G]),
+                                        np.ascontiguousarray(k[b:b + 1, j:j + 1]), lens[b:b + 1], scale)[0, 0]
+            fin = np.isfinite(ref)
+            assert np.array_equal(fin, np.isfinite(got[b, j]))
+            assert np.abs(got[b, j][fin] - ref[fin]).max() <= 1e-3 * max(1.0, np.abs(ref[fin]).max())
+        g_sel, g_cnt = host(buf.sel_blocks), host(buf.sel_count)
+        s_sel, s_cnt = oracle.topk(got, lens, w.k_blocks, T)
+        np.testing.assert_array_equal(g_sel, s_sel)
+        np.testing.assert_array_equal(g_cnt, s_cnt)
+        out = lru.step(g_sel.reshape(P, -1), g_cnt.reshape(P), nb)
+        for f in ("sel_slot", "sel_hit", "miss_block", "miss_slot"):
+            np.testing.assert_array_equal(host(getattr(buf, f)).reshape(P, -1), out[f], f)
+        np.testing.assert_array_equal(host(buf.slot_block).reshape(P, -1), lru.slot_block())
+        g_out = host(buf.out)
+        for b in sorted({b for b, _ in heads}):
+            o_ref, _ = oracle.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], g_sel[b:b + 1], g_cnt[b:b + 1],
+                                        lens[b:b + 1], scale)
+            hh = [h for bb, h in heads if bb == b]
+            assert max_rel_row_err(g_out[b, hh], o_ref[0, hh]) <= 1e-4
+    assert lens.min() == w.ctx + 4 and nb_of_len(lens.min()) > 2048
+
+
+def nb_of_len(n):
+    return (int(n) + 15) // 16

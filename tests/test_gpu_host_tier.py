@@ -192,3 +192,81 @@ def test_host_source_equals_device_source_bit_exact():
         torch.cuda.synchronize()
         hk.free()
         hv.free()
+
+
+@pytest.mark.timeout(400)
+def test_host_tier_full_size_sampled_with_prefetch():
+    # the benchmark's host-tier shape: 16 x 8 rows, 131072-token context,
+    # 128 of 256 slots, two layers each with its own K/V (8 GiB per layer) in
+    # pinned mapped host memory, the cross-layer prefetch on a second stream.
+    # Every row's lists and slot table against the oracle's two LRU steps;
+    # sampled rows' pool bytes and sampled heads' attention
+    from top_sparse_kv_block_amd.step import layer_sweep
+    w = synth.WORKLOADS["host_tier_32l"].scaled(layers=2, steps=2)
+    sels = synth.gen_layer_selections(w)
+    P, k, C, nb = w.rows, w.k_blocks, w.capacity, w.nb_max
+    lens = np.full(w.batch, w.ctx, np.int32)
+    dlens = dev(lens)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    cnt = np.full((w.batch, w.n_kv_heads), k, dtype=np.int32)
+    n_elem = w.rows * w.ctx * w.head_dim
+    side = torch.cuda.Stream()
+    g = torch.Generator(device="cuda").manual_seed(41)
+    hbs, views, bufs, lrus = [], [], [], []
+    try:
+        for l in range(w.layers):
+            pair = []
+            for _ in range(2):
+                hb = B.HostBuffer(n_elem * 2)
+                hbs.append(hb)
+                ht = torch.from_numpy(hb.numpy(np.int16, (n_elem,))).view(torch.bfloat16)
+                for off in range(0, n_elem, 1 << 26):
+                    n = min(1 << 26, n_elem - off)
+                    ht[off:off + n].copy_(torch.randn(n, generator=g, device="cuda").to(torch.bfloat16))
+                pair.append(hb)
+            views.append([hb.numpy(np.uint16, (w.batch, w.n_kv_heads, w.ctx, w.head_dim)) for hb in pair])
+            cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, k, C)
+            bufs.append(LayerBuffers(cfg))
+            lrus.append(oracle.LRU(P, C))
+        srcs = [(hbs[2 * l].device_ptr, hbs[2 * l + 1].device_ptr) for l in range(w.layers)]
+        rows, heads = [0, 77, 127], [(0, 0), (9, 14), (15, 31)]
+        r = np.random.default_rng(5)
+        for s in range(w.steps):
+            qs = [synth.f32_to_bf16_bits(r.standard_normal((w.batch, w.n_q_heads, w.head_dim)).astype(np.float32))
+                  for _ in range(w.layers)]
+            for l, buf in enumerate(bufs):
+                buf.sel_blocks.copy_(dev(sels[s, l]))
+                buf.sel_count.copy_(dev(cnt))
+            log("host tier full size, step", s)
+            layer_sweep(bufs, [dev(q) for q in qs], dlens, srcs, B.SKV_SRC_HOST_MAPPED, prefetch=True,
+                        side_stream=side)
+            torch.cuda.synchronize()
+            for l, buf in enumerate(bufs):
+                if l > 0:
+                    pf = lrus[l].step(sels[s, l - 1].reshape(P, k), cnt.reshape(P), nb)
+                    np.testing.assert_array_equal(host(buf.pf_miss_count).reshape(P), pf["miss_count"])
+                out = lrus[l].step(sels[s, l].reshape(P, k), cnt.reshape(P), nb)
+                for name in ("sel_slot", "sel_hit", "miss_block", "miss_slot"):
+                    np.testing.assert_array_equal(host(getattr(buf, name)).reshape(P, k), out[name], name)
+                np.testing.assert_array_equal(host(buf.miss_count).reshape(P), out["miss_count"])
+                sb = lrus[l].slot_block()
+                np.testing.assert_array_equal(host(buf.slot_block).reshape(P, C), sb)
+                Kh, Vh = views[l]
+                pk = host(buf.pool_k).reshape(P, C, 16, w.head_dim)
+                pv = host(buf.pool_v).reshape(P, C, 16, w.head_dim)
+                for r_ in rows:
+                    b, j = divmod(r_, w.n_kv_heads)
+                    for slot, blk in enumerate(sb[r_]):
+                        if blk >= 0:
+                            assert np.array_equal(pk[r_, slot], Kh[b, j, 16 * blk:16 * blk + 16])
+                            assert np.array_equal(pv[r_, slot], Vh[b, j, 16 * blk:16 * blk + 16])
+                g_out = host(buf.out)
+                for b in sorted({b for b, _ in heads}):
+                    o_ref, _ = oracle.attention(qs[l][b:b + 1], Kh[b:b + 1], Vh[b:b + 1], sels[s, l][b:b + 1],
+                                                cnt[b:b + 1], lens[b:b + 1], scale)
+                    hh = [h for bb, h in heads if bb == b]
+                    assert max_rel_row_err(g_out[b, hh], o_ref[0, hh]) <= 1e-4
+    finally:
+        torch.cuda.synchronize()
+        for hb in hbs:
+            hb.free()
