@@ -27,6 +27,9 @@ FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "
     # rows just past 2048 and 4096 blocks: the 8- and 16-keys-per-thread variants
     ("llama8b_32k", dict(batch=1, ctx=32768 + 16 * 5, budget=2048), 3, 0),
     ("quest_128k", dict(batch=1, ctx=65536 + 16 * 3), 3, 0),
+    # the largest budget and working set (1024 blocks of 1024 slots), and the largest GQA group (16)
+    ("llama8b_32k", dict(batch=1, ctx=65536, budget=16384, capacity=1024), 2, 0),
+    ("llama8b_32k", dict(batch=2, n_kv_heads=2, ctx=4096, budget=512), 3, 0),
     ("lookahead_1m", dict(ctx=16384), 3, 0),
 ])
 def test_fused_equals_separate_calls(name, kw, steps, splits):
