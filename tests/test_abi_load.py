@@ -48,6 +48,8 @@ def test_host_side_validation_needs_no_gpu():
     assert binding.sparse_decode_attention_workspace_bytes(s, 8, 0) == 0
     ok = binding.make_shape(8, 32, 8, 128, 32768, "bf16")
     splits = binding.sparse_decode_attention_splits(ok, 128)
-    assert splits == 16
+    assert splits == 8  # two workgroups per CU: 512 / 64 rows
     # the per-split partials: rows x splits x G x (D + 2) floats
-    assert binding.sparse_decode_attention_workspace_bytes(ok, 128, 0) == 64 * 16 * 4 * 130 * 4
+    assert binding.sparse_decode_attention_workspace_bytes(ok, 128, 0) == 64 * 8 * 4 * 130 * 4
+    few = binding.make_shape(1, 64, 8, 128, 1 << 20, "bf16")  # 8 rows: capped at one block per wave
+    assert binding.sparse_decode_attention_splits(few, 128) == 16
