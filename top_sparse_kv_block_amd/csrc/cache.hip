@@ -22,7 +22,9 @@
 // exactly the order of a linked list that appends S in ascending order, so
 // parallel code reproduces the list bit for bit.
 //
-// cache_update_kernel: one 256-thread workgroup per row, state in LDS.
+// cache_update_kernel: one 1024-thread workgroup per row, state in LDS (with
+// 1024 threads each candidate slot is ranked by 8 lanes: 9.5 us per call at
+// 64 rows x 128 slots against 12.5 us with 256 threads).
 //   hits:    every occupied slot binary-searches its block in S (S is
 //            ascending); a hit claims S[i] with an LDS compare-and-swap, so
 //            a block resident twice is detected.
@@ -42,7 +44,7 @@
 
 namespace skv {
 
-constexpr int kCacheThreads = 256;
+constexpr int kCacheThreads = 1024;
 
 __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_count, int k, int C, int NB,
