@@ -37,14 +37,16 @@ template <> __device__ __forceinline__ float groups_max<32>(float v) { return xo
 // keys at D=128): a launch-shape sweep on the 32K workload measured this
 // shape fastest (78 us, 6.9 TB/s, against 82 us for 4 waves x 8 blocks);
 // non-temporal loads were worth another 20%.
-constexpr int kScoreWaves = 16;
+constexpr int kScoreWaves = 4;
 constexpr int kScoreBlocksPerWave = 4;
 // matrix-core scan: blocks per wave with one operand tile (up to 16 query
-// rows) and with two.  Measured: with one tile, one block per wave (more,
-// shorter workgroups) streams fastest (32K: 75-76 us against 77 at 4 and 82
-// at 8); with two tiles, 8 (1M, 4 drafts: 314-322 us against 323-370 at 4)
+// rows) and with two.  Measured with 4-wave workgroups: 32K, one tile, one
+// block per wave 72.8 us (2 blocks: 78.3); 1M with 4 drafts, two tiles, 4
+// blocks per wave 300-308 us (16 blocks: 316-321).  Workgroups of 16 waves
+// were slower at every setting (32K: 75-77 us; 1M: 314-350 us), as were 8
+// (73.7-74.6 / 308-312), 2 (78.2 / 303-305) and 1 (80.1-80.6 / 300).
 constexpr int kMfmaBlocksPerWave1 = 1;
-constexpr int kMfmaBlocksPerWave2 = 8;
+constexpr int kMfmaBlocksPerWave2 = 4;
 template <int NT> constexpr int mfma_blocks_per_wave() { return NT > 1 ? kMfmaBlocksPerWave2 : kMfmaBlocksPerWave1; }
 constexpr int kScoreThreads = 64 * kScoreWaves;
 // the Quest scan keeps 8 boxes in flight per lane (76 VGPRs): smaller
