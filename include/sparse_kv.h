@@ -201,6 +201,26 @@ skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int3
                                   void *stream);
 
 /*
+ * Stages 2 and 3 in one launch: sparse_kv_topk followed by
+ * sparse_kv_cache_update (LRU), with the selection kept on chip between the
+ * two and the plan committed by the same workgroup.  Same arguments, same
+ * outputs and the same results bit for bit as the two calls in that order
+ * (the selection goes to sel_blocks / sel_count as well); with src_k/src_v
+ * the misses are gathered into the pool afterwards, else only the lists are
+ * built (as sparse_kv_cache_update with NULL sources).  For pipelines that
+ * attend separately, e.g. one step behind ("KV Cache 塞不进 HBM 了" §2.1:
+ * the next step's retrieval runs while the forward uses the KV already
+ * resident).
+ * Limits: those of the two calls.
+ */
+skv_status sparse_kv_select(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                            int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t capacity,
+                            int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
+                            uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                            int32_t *miss_slot, int32_t *miss_count, const void *src_k, const void *src_v,
+                            int32_t src_kind, void *pool_k, void *pool_v, void *stream);
+
+/*
  * Stage 3 with importance-capped eviction instead of LRU (OasisKV summary,
  * key module 3: only the delta moves, and when the capped cache has no room
  * the least important blocks are evicted).  Everything as in

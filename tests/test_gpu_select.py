@@ -1,0 +1,87 @@
+"""GPU parity of the one-launch selection (sparse_kv_select): top-k and the
+LRU working-set update in one workgroup per row must give exactly what the
+two calls give in sequence (sparse_kv_topk, then sparse_kv_cache_update):
+selection, lists, slot table, stamps, clock and, with a source, the pool.
+
+Scores are seeded random rows that drift from step to step (so hits, misses
+and evictions all occur), at row lengths covering each launch shape: up to
+8192 blocks (512 threads), up to 16384 (1024 threads) and the long-row
+top-k beyond, with ragged lengths, forced sink / recent blocks and a working
+set larger than the budget.
+"""
+import numpy as np
+import pytest
+import torch
+
+from top_sparse_kv_block_amd import binding as B
+from gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("sel_blocks", "sel_count", "sel_slot", "sel_hit", "miss_block", "miss_slot", "miss_count")
+
+
+def _state(P, k, C, device="cuda"):
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(sel_blocks=torch.empty(P, k, **i32), sel_count=torch.empty(P, **i32),
+                slot_block=torch.full((P, C), -1, **i32), slot_stamp=torch.zeros(P, C, **i32),
+                clock=torch.zeros(P, **i32), sel_slot=torch.empty(P, k, **i32),
+                sel_hit=torch.empty(P, k, dtype=torch.uint8, device=device), miss_block=torch.empty(P, k, **i32),
+                miss_slot=torch.empty(P, k, **i32), miss_count=torch.empty(P, **i32))
+
+
+@pytest.mark.parametrize("B_,Hkv,T,k,C,sink,recent,steps", [
+    (2, 4, 16 * 2048, 128, 128, 0, 0, 4),         # 2048 blocks, C = k
+    (3, 2, 16 * 8192, 32, 48, 64, 128, 4),        # 8192 blocks with forced blocks, C > k
+    (1, 3, 16 * 12000, 64, 64, 16, 16, 3),        # 1024 threads
+    (1, 2, 16 * 40000, 128, 160, 0, 256, 3),      # long-row top-k
+])
+def test_select_equals_topk_then_update(B_, Hkv, T, k, C, sink, recent, steps):
+    rng = np.random.default_rng(T + k)
+    P, NB, D = B_ * Hkv, T // 16, 64
+    shape = B.make_shape(B_, 4 * Hkv, Hkv, D, T, "f32")
+    lens = rng.integers(T // 2, T + 1, size=B_).astype(np.int32)
+    lens[0] = T
+    dl = dev(lens)
+    K = torch.randn(B_, Hkv, T, D, device="cuda")
+    V = torch.randn(B_, Hkv, T, D, device="cuda")
+    a, b = _state(P, k, C), _state(P, k, C)
+    pa = [torch.zeros(P, C, 16, D, device="cuda") for _ in range(2)]
+    pb = [torch.zeros(P, C, 16, D, device="cuda") for _ in range(2)]
+    base = rng.standard_normal((P, NB)).astype(np.float32)
+    for t in range(steps):
+        sc = dev((base + 0.3 * rng.standard_normal((P, NB))).astype(np.float32))
+        log("select", (B_, Hkv, T, k, C, sink, recent), "step", t)
+        B.sparse_kv_topk(shape, sc, dl, k, sink, recent, a["sel_blocks"], a["sel_count"])
+        B.sparse_kv_cache_update(shape, k, C, a["sel_blocks"], a["sel_count"], a["slot_block"], a["slot_stamp"],
+                                 a["clock"], a["sel_slot"], a["sel_hit"], a["miss_block"], a["miss_slot"],
+                                 a["miss_count"], K, V, B.SKV_SRC_DEVICE, pa[0], pa[1])
+        B.sparse_kv_select(shape, sc, dl, k, sink, recent, C, b["sel_blocks"], b["sel_count"], b["slot_block"],
+                           b["slot_stamp"], b["clock"], b["sel_slot"], b["sel_hit"], b["miss_block"], b["miss_slot"],
+                           b["miss_count"], K, V, B.SKV_SRC_DEVICE, pb[0], pb[1])
+        torch.cuda.synchronize()
+        for f in FIELDS + ("slot_block", "slot_stamp", "clock"):
+            np.testing.assert_array_equal(host(b[f]), host(a[f]), err_msg=f"{f} at step {t}")
+        for x, y in zip(pa, pb):
+            assert torch.equal(x, y)
+        if t > 0:
+            m = host(b["miss_count"])
+            assert 0 < m.sum() < host(b["sel_count"]).sum()
+
+
+def test_select_lists_only_and_corrupt_table():
+    shape = B.make_shape(1, 8, 2, 64, 16 * 1024, "f32")
+    P, k, C = 2, 16, 16
+    s = _state(P, k, C)
+    table = np.full((P, C), -1, np.int32)
+    table[0, :2] = [5, 1024 + 3]  # row 0 holds a block id past the end
+    s["slot_block"].copy_(dev(table))
+    sc = dev(np.random.default_rng(0).standard_normal((P, 1024)).astype(np.float32))
+    B.sparse_kv_select(shape, sc, dev(np.array([16 * 1024], np.int32)), k, 0, 0, C, s["sel_blocks"], s["sel_count"],
+                       s["slot_block"], s["slot_stamp"], s["clock"], s["sel_slot"], s["sel_hit"], s["miss_block"],
+                       s["miss_slot"], s["miss_count"])
+    torch.cuda.synchronize()
+    assert host(s["miss_count"]).tolist() == [-1, k]
+    np.testing.assert_array_equal(host(s["slot_block"])[0], table[0])  # untouched
+    assert host(s["clock"]).tolist() == [0, 1]
+    assert host(s["sel_count"]).tolist() == [k, k]

@@ -31,7 +31,7 @@ EXPORTS = (
     "sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
     "sparse_decode_attention_splits", "sparse_decode_attention_workspace_bytes", "sparse_kv_quest_meta",
     "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
-    "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append",
+    "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
 )
 
 
@@ -68,6 +68,8 @@ def load():
     L.sparse_kv_cache_update_importance.argtypes = [S, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                                     _p, _i32, _p, _p, _p]
     L.sparse_kv_append.argtypes = [S, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p]
+    L.sparse_kv_select.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                   _i32, _p, _p, _p]
     L.sparse_decode_attention.argtypes = [S, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _i32, _p, _p,
                                           _p, _sz, _p]
     L.sparse_kv_select_attend.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -217,6 +219,33 @@ def sparse_kv_cache_update_importance(shape, k_blocks, capacity, sel_blocks, sel
         int(src_kind), _ptr(pool_k, dt, "pool_k", allow_none=True, numel=pc * 16 * d),
         _ptr(pool_v, dt, "pool_v", allow_none=True, numel=pc * 16 * d), _stream(stream))
     _check("sparse_kv_cache_update_importance", rc)
+
+
+def sparse_kv_select(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity, sel_blocks, sel_count,
+                     slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, src_k=None,
+                     src_v=None, src_kind=SKV_SRC_DEVICE, pool_k=None, pool_v=None, stream=None):
+    """sparse_kv_topk then sparse_kv_cache_update (LRU) in one launch, same results."""
+    dt = _torch_dtype(shape.dtype)
+    P, d, t = shape.batch * shape.n_kv_heads, shape.head_dim, shape.max_ctx
+    pk, pc = P * k_blocks, P * capacity
+
+    def src(x, name):
+        if x is None or isinstance(x, int):
+            return x
+        return _ptr(x, dt, name, numel=P * t * d)
+
+    rc = load().sparse_kv_select(
+        C.byref(shape), _ptr(scores, torch.float32, "scores", numel=P * (t // 16)),
+        _ptr(seq_lens, torch.int32, "seq_lens", numel=shape.batch), int(k_blocks), int(sink_tokens),
+        int(recent_tokens), int(capacity), _ptr(sel_blocks, torch.int32, "sel_blocks", numel=pk),
+        _ptr(sel_count, torch.int32, "sel_count", numel=P), _ptr(slot_block, torch.int32, "slot_block", numel=pc),
+        _ptr(slot_stamp, torch.int32, "slot_stamp", numel=pc), _ptr(clock, torch.int32, "clock", numel=P),
+        _ptr(sel_slot, torch.int32, "sel_slot", numel=pk), _ptr(sel_hit, torch.uint8, "sel_hit", numel=pk),
+        _ptr(miss_block, torch.int32, "miss_block", numel=pk), _ptr(miss_slot, torch.int32, "miss_slot", numel=pk),
+        _ptr(miss_count, torch.int32, "miss_count", numel=P), src(src_k, "src_k"), src(src_v, "src_v"),
+        int(src_kind), _ptr(pool_k, dt, "pool_k", allow_none=True, numel=pc * 16 * d),
+        _ptr(pool_v, dt, "pool_v", allow_none=True, numel=pc * 16 * d), _stream(stream))
+    _check("sparse_kv_select", rc)
 
 
 def sparse_kv_append(shape, new_k, new_v, seq_lens, keys, values, meta=None, slot_block=None, capacity=0,

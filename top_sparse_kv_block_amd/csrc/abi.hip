@@ -140,6 +140,49 @@ SKV_API skv_status sparse_kv_cache_update_importance(const skv_shape *shape, int
                              pool_v, stream);
 }
 
+SKV_API skv_status sparse_kv_select(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                                    int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t capacity,
+                                    int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block,
+                                    uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit,
+                                    int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
+                                    const void *src_k, const void *src_v, int32_t src_kind, void *pool_k,
+                                    void *pool_v, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!scores || !seq_lens || !sel_blocks || !sel_count || !slot_block || !slot_stamp || !clock || !sel_slot ||
+        !sel_hit || !miss_block || !miss_slot || !miss_count)
+        return SKV_ERR_NULL;
+    if (d.NB > skv::kMaxTopkBlocks)
+        return SKV_ERR_UNSUPPORTED;
+    if (k_blocks < 1 || k_blocks > d.NB || k_blocks > skv::kMaxK || sink_tokens < 0 || recent_tokens < 0 ||
+        capacity < 1)
+        return SKV_ERR_SHAPE;
+    if (capacity < k_blocks)
+        return SKV_ERR_CAPACITY;
+    if (capacity > skv::kMaxCapacity)
+        return SKV_ERR_UNSUPPORTED;
+    if (sink_tokens > 0 || recent_tokens > 0) {
+        const long long forced_max = (long long)nb_blocks(sink_tokens) + nb_blocks(recent_tokens) + 1;
+        if (forced_max > k_blocks)
+            return SKV_ERR_CAPACITY;
+    }
+    if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
+        return SKV_ERR_SHAPE;
+    const bool fetch = src_k || src_v;
+    if (fetch && (!src_k || !src_v || !pool_k || !pool_v))
+        return SKV_ERR_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = skv::launch_select(d, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity, sel_blocks,
+                                      sel_count, slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block,
+                                      miss_slot, miss_count, s);
+    if (e != hipSuccess || !fetch)
+        return hip_status(e);
+    return hip_status(skv::launch_gather(d, k_blocks, capacity, miss_block, miss_slot, miss_count, src_k, src_v,
+                                         pool_k, pool_v, s));
+}
+
 SKV_API skv_status sparse_kv_append(const skv_shape *shape, const void *new_k, const void *new_v, int32_t *seq_lens,
                                     void *keys, void *values, void *meta, const int32_t *slot_block, int32_t capacity,
                                     void *pool_k, void *pool_v, void *stream) {

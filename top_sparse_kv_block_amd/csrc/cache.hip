@@ -95,6 +95,70 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     }
 }
 
+// select_kernel: the top-k and the working-set update of one row in one
+// workgroup (the two calls' code, so the same results): the row's selection
+// stays in LDS between the two, the slot table is read while the top-k runs,
+// and the plan is committed by the same workgroup.  Rows up to 8192 blocks
+// run with 512 threads, up to 16384 with 1024, longer rows take the long-row
+// top-k with 1024 threads.
+template <int THREADS, int KPT> struct SelectTopk {
+    TopkScratch sc;
+    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int32_t *out) {
+        return topk_row<THREADS, KPT>(srow, len, NB, k, sink, recent, out, sc);
+    }
+};
+template <int THREADS> struct SelectTopk<THREADS, 0> {
+    TopkLongScratch ls;
+    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int32_t *out) {
+        return topk_long_row<THREADS>(srow, len, NB, k, sink, recent, out, ls);
+    }
+};
+
+template <int THREADS, int KPT>
+__global__ __launch_bounds__(THREADS) void select_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int Hkv, int T, int NB, int k, int sink,
+    int recent, int C, int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
+    int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp, uint32_t *__restrict__ clock,
+    int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit, int32_t *__restrict__ miss_block,
+    int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count) {
+    __shared__ SelectTopk<THREADS, KPT> tk;
+    __shared__ int32_t sS[kMaxK];
+    __shared__ CacheScratch cs;
+    __shared__ uint32_t sClock;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    int32_t *sb = slot_block + (size_t)row * C;
+    uint32_t *ss = slot_stamp + (size_t)row * C;
+    SlotRegs<THREADS> regs;  // in flight while the top-k runs
+    load_slots<THREADS>(regs, C, sb, ss);
+    const int n = tk.run(scores + (size_t)row * NB, len, NB, k, sink, recent, sS);
+    for (int i = tid; i < k; i += THREADS)
+        sel_blocks[(size_t)row * k + i] = sS[i];
+    if (tid == 0)
+        sel_count[row] = n;
+    int bad;
+    const int nm = cache_plan_row<THREADS>(sS, n, C, NB, regs, cs, bad);
+    if (bad) {
+        if (tid == 0)
+            miss_count[row] = -1;
+        return;
+    }
+    if (tid == 0)
+        sClock = atomicAdd(&clock[row], 1u) + 1u;
+    __syncthreads();
+    const uint32_t now = sClock;
+    write_lists<THREADS>(sS, n, nm, k, cs, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
+                         miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);
+    for (int i = tid; i < n; i += THREADS) {
+        const int s = cs.slot_of[i];
+        if (s >= 0 && s < C) {
+            sb[s] = sS[i];
+            ss[s] = now;
+        }
+    }
+}
+
 // One wave copies one missed block: K then V, 16*D elements each.
 template <int BLOCK_BYTES>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t *__restrict__ miss_block,
@@ -137,6 +201,41 @@ hipError_t launch_cache_update(const Dims &d, int k, int cap, const int32_t *sel
                        cap, d.NB, slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block, miss_slot,
                        miss_count, scores);
     return hipGetLastError();
+}
+
+template <int THREADS, int KPT>
+static hipError_t select_t(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
+                           int cap, int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
+                           uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                           int32_t *miss_slot, int32_t *miss_count, hipStream_t st) {
+    hipLaunchKernelGGL((select_kernel<THREADS, KPT>), dim3(d.rows()), dim3(THREADS), 0, st, scores, lens, d.Hkv, d.T,
+                       d.NB, k, sink, recent, cap, sel_blocks, sel_count, slot_block, slot_stamp, clock, sel_slot,
+                       sel_hit, miss_block, miss_slot, miss_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
+                         int cap, int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
+                         uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                         int32_t *miss_slot, int32_t *miss_count, hipStream_t st) {
+#define SKV_SELECT(TH, KP)                                                                                          \
+    return select_t<TH, KP>(d, scores, lens, k, sink, recent, cap, sel_blocks, sel_count, slot_block, slot_stamp, \
+                            clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, st)
+    const int kpt = (d.NB + 511) / 512;
+    if (kpt <= 1)
+        SKV_SELECT(512, 1);
+    if (kpt <= 2)
+        SKV_SELECT(512, 2);
+    if (kpt <= 4)
+        SKV_SELECT(512, 4);
+    if (kpt <= 8)
+        SKV_SELECT(512, 8);
+    if (kpt <= 16)
+        SKV_SELECT(512, 16);
+    if (kpt <= 32)
+        SKV_SELECT(1024, 16);
+    SKV_SELECT(1024, 0);
+#undef SKV_SELECT
 }
 
 template <int BB>

@@ -115,6 +115,16 @@ class LayerBuffers:
                                  self.miss_slot, self.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
                                  stream)
 
+    def select(self, seq_lens, src_k=None, src_v=None, src_kind=B.SKV_SRC_DEVICE, stream=None, lists=None):
+        """Top-k and working-set update (LRU) in one launch; ``lists`` (an
+        object with the list attributes, default self) receives the
+        selection and the lists."""
+        c, o = self.cfg, lists if lists is not None else self
+        B.sparse_kv_select(self.shape, self.scores, seq_lens, c.k_blocks, c.sink, c.recent, c.capacity, o.sel_blocks,
+                           o.sel_count, self.slot_block, self.slot_stamp, self.clock, o.sel_slot, o.sel_hit,
+                           o.miss_block, o.miss_slot, o.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
+                           stream)
+
     def prefetch(self, hint: "LayerBuffers", src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None):
         """Cross-layer prefetch: an ordinary working-set update of this layer
         with another layer's selection (hint.sel_blocks / hint.sel_count) as
@@ -174,7 +184,8 @@ class _Lists:
 class Lag1Pipeline:
     """Lag-1 decode of one layer: attention at step t runs over the selection
     made at step t-1 (the first step over its own) on the current stream,
-    while step t's score, top-k and working-set update run on a side stream.
+    while step t's score and selection (top-k + working-set update in one
+    launch) run on a side stream.
     The retrieval for the next step thus overlaps the attention, which uses
     the KV readied at the step before ("KV Cache 塞不进 HBM 了", §2.1 and the
     §3 loop).
@@ -225,13 +236,11 @@ class Lag1Pipeline:
         with torch.cuda.stream(side):
             B.sparse_kv_score(buf.shape, c.mode, score_q, c.n_queries, keys_or_meta, seq_lens, c.softmax_scale,
                               buf.scores, side)
-            B.sparse_kv_topk(buf.shape, buf.scores, seq_lens, c.k_blocks, c.sink, c.recent, cur.sel_blocks,
-                             cur.sel_count, side)
-            B.sparse_kv_cache_update(buf.shape, c.k_blocks, c.capacity, cur.sel_blocks, cur.sel_count,
-                                     buf.slot_block, buf.slot_stamp, buf.clock, cur.sel_slot, cur.sel_hit,
-                                     cur.miss_block, cur.miss_slot,
-                                     cur.miss_count if miss_count is None else miss_count, None, None, src_kind,
-                                     buf.pool_k, buf.pool_v, side)
+            B.sparse_kv_select(buf.shape, buf.scores, seq_lens, c.k_blocks, c.sink, c.recent, c.capacity,
+                               cur.sel_blocks, cur.sel_count, buf.slot_block, buf.slot_stamp, buf.clock, cur.sel_slot,
+                               cur.sel_hit, cur.miss_block, cur.miss_slot,
+                               cur.miss_count if miss_count is None else miss_count, None, None, src_kind,
+                               buf.pool_k, buf.pool_v, side)
         upd = torch.cuda.Event()
         upd.record(side)
         use = self.lists[(self.t - 1) % 2] if self.t > 0 else cur
