@@ -18,7 +18,7 @@
 // partial dot products (packed bf16 dot2 or fp32 FMA), and the LPT-lane
 // partials are summed with DPP row rotations; no LDS is used.  The work is
 // HBM-bound (about 4 flop per byte at G=4), so the kernel is organised
-// around keeping many 16-byte loads in flight: 16 waves per workgroup walk
+// around keeping many 16-byte loads in flight: the waves of a workgroup walk
 // interleaved blocks of one row, non-temporal loads for the key stream.
 #include "skv_device.h"
 #include "skv_launch.h"
@@ -33,10 +33,9 @@ template <> __device__ __forceinline__ float groups_max<8>(float v) {
 template <> __device__ __forceinline__ float groups_max<16>(float v) { return rows_max(v); }
 template <> __device__ __forceinline__ float groups_max<32>(float v) { return xor32_max(v); }
 
-// 16 waves x 4 blocks per wave per workgroup (64 blocks = 256 KiB of bf16
-// keys at D=128): a launch-shape sweep on the 32K workload measured this
-// shape fastest (78 us, 6.9 TB/s, against 82 us for 4 waves x 8 blocks);
-// non-temporal loads were worth another 20%.
+// Workgroups of 4 waves (the vector kernel walks 4 blocks per wave, the
+// matrix-core kernel the counts below); non-temporal loads for the key
+// stream were worth 20% on the 32K workload.
 constexpr int kScoreWaves = 4;
 constexpr int kScoreBlocksPerWave = 4;
 // matrix-core scan: blocks per wave with one operand tile (up to 16 query
