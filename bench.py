@@ -5,7 +5,9 @@ A step is one pass of the whole path for one attention layer over one batch:
 block scoring -> top-k under the budget -> working-set update -> split-K GQA
 attention that also fetches the step's misses into the pool.  By default
 stages 2-4 run as the library's fused select-attend call (same results as
-the three separate calls; --four-calls runs those instead).  The default
+the three separate calls; --four-calls runs those instead); rows over 8192
+blocks, beyond the fused call, run the one-launch selection (top-k and
+working-set update) followed by attention.  The default
 workload is the Llama-3.1-8B-shaped layer: batch 8, 32 q-heads / 8 kv-heads,
 head_dim 128, bf16 K/V, 32768-token context in 16-token blocks, a
 2048-token budget (128 blocks) and a 128-slot working set per (sequence,
@@ -432,8 +434,11 @@ def run(args):
     cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, T, w.dtype, w.k_blocks, w.capacity,
                      mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent, num_splits=args.splits)
     buf = LayerBuffers(cfg)
+    select = False
     if args.fused and cfg.nb > 8192:
-        args.fused = False  # rows over 8192 blocks exceed the fused call: the four calls run
+        # rows over 8192 blocks exceed the fused call: score, the one-launch
+        # selection (top-k + working-set update) and attention run instead
+        args.fused, select = False, True
     keys_or_meta = dK
     if mode == B.SKV_SCORE_QUEST:
         keys_or_meta = torch.empty(w.batch, w.n_kv_heads, cfg.nb, 2, w.head_dim, dtype=cfg.torch_dtype,
@@ -458,6 +463,20 @@ def run(args):
         B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
         if ev is not None:
             ev[1].record()
+        if select:
+            B.sparse_kv_select(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, cfg.capacity,
+                               buf.sel_blocks, buf.sel_count, buf.slot_block, buf.slot_stamp, buf.clock, buf.sel_slot,
+                               buf.sel_hit, buf.miss_block, buf.miss_slot, miss_log[t], None, None, B.SKV_SRC_DEVICE,
+                               buf.pool_k, buf.pool_v, st)
+            if ev is not None:
+                ev[2].record()
+                ev[3].record()
+            B.sparse_decode_attention(shape, q_all[t], buf.pool_k, buf.pool_v, cfg.capacity, buf.sel_blocks,
+                                      buf.sel_slot, buf.sel_hit, buf.sel_count, dlens, cfg.k_blocks, scale,
+                                      buf.splits, dK, dV, B.SKV_SRC_DEVICE, buf.out, buf.lse, buf.workspace, st)
+            if ev is not None:
+                ev[4].record()
+            return
         B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
                          buf.sel_count, st)
         if ev is not None:
@@ -626,12 +645,15 @@ def run(args):
         "mode": "hip-graph replay" if graph is not None else "eager",
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "path": ("lag-1 pipeline: attention over the previous selection || score, top-k, update on a second stream"
-                 if pipe is not None else "score + fused select/update/attend" if args.fused else "four calls"),
+                 if pipe is not None else "score + fused select/update/attend" if args.fused else
+                 "score + one-launch select (top-k, update) + attention" if select else "four calls"),
         "eviction": args.eviction,
         "grow": bool(args.grow),
         "stage_us": ({"step": round(float(stage.sum(axis=1).mean()), 2)} if pipe is not None else
                      {"score": round(float(stage[:, 0].mean()), 2),
                       "select_update_attend": round(float(stage[:, 1].mean()), 2)} if args.fused else
+                     {"score": round(float(stage[:, 0].mean()), 2), "select": round(float(stage[:, 1].mean()), 2),
+                      "attention": round(float(stage[:, 3].mean()), 2)} if select else
                      {name: round(float(v), 2) for name, v in
                       zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))}),
         "roofline": {"bound": "hbm", "kernel": _score_kernel_name(w) if mode == B.SKV_SCORE_BLOCKMAX

@@ -43,7 +43,8 @@ def _forced_sets(w, lens):
     return out
 
 
-def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_on_attend=True, fused=False):
+def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_on_attend=True, fused=False,
+                 select=False):
     """Run `steps` steps of workload `w`; check rows `rows` (None = all) of
     the scores and (b, h) pairs `heads` (None = all) of the attention."""
     steps = steps or w.steps
@@ -70,7 +71,7 @@ def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_
     for t in range(steps):
         log(w.name, "step", t, (w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx))
         decode_step(buf, dev(q[t]), dev(sq[t]), keys_or_meta, dlens, dK, dV, fetch_on_attend=fetch_on_attend,
-                    fused=fused)
+                    fused=fused, select=select)
         torch.cuda.synchronize()
         g_scores = host(buf.scores).astype(np.float64)
         g_sel, g_cnt = host(buf.sel_blocks), host(buf.sel_count)
@@ -201,3 +202,17 @@ def test_lookahead_1m_full_size_sampled():
     # the working set
     w = synth.WORKLOADS["lookahead_1m"]
     run_workload(w, steps=2, rows=[5], heads=[(0, 0), (0, 47)])
+
+
+@pytest.mark.timeout(400)
+def test_lookahead_1m_full_size_one_launch_select():
+    # the benchmark's path for rows over 8192 blocks: score, the one-launch
+    # selection (top-k + working-set update), attention with fetch on attend
+    w = synth.WORKLOADS["lookahead_1m"]
+    run_workload(w, steps=2, rows=[2], heads=[(0, 5), (0, 63)], select=True)
+
+
+@pytest.mark.parametrize("fetch_on_attend", [True, False])
+def test_llama8b_reduced_one_launch_select(fetch_on_attend):
+    w = synth.WORKLOADS["llama8b_32k"].scaled(batch=2, ctx=4096, budget=512)
+    run_workload(w, steps=4, select=True, fetch_on_attend=fetch_on_attend)

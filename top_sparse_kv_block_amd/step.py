@@ -262,17 +262,27 @@ class Lag1Pipeline:
 
 
 def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, src_v, src_kind=B.SKV_SRC_DEVICE,
-                stream=None, fetch_on_attend=True, fused=False):
+                stream=None, fetch_on_attend=True, fused=False, select=False):
     """Enqueue one full step: score, top-k, cache update, attention.
 
     The misses are copied into the pool either by the attention kernel while
     it reads them (fetch_on_attend, the default: one read and one write per
     missed block) or by the cache update's own copy pass.  fused=True runs
-    stages 2-4 as the single select-attend call (same results).
+    stages 2-4 as the single select-attend call, select=True stages 2-3 as
+    one launch (same results either way; rows over 8192 blocks exceed the
+    fused call).
     """
     buf.score(score_q, keys_or_meta, seq_lens, stream)
     if fused:
         buf.select_attend(q, seq_lens, src_k, src_v, src_kind, stream)
+        return
+    if select:
+        if fetch_on_attend:
+            buf.select(seq_lens, None, None, src_kind, stream)
+            buf.attention(q, seq_lens, src_k, src_v, src_kind, stream)
+        else:
+            buf.select(seq_lens, src_k, src_v, src_kind, stream)
+            buf.attention(q, seq_lens, stream=stream)
         return
     buf.topk(seq_lens, stream)
     if fetch_on_attend:
