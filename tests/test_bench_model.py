@@ -34,3 +34,14 @@ def test_score_scan_is_the_k_half_of_one_layers_cache():
 def test_multi_gpu_request_exits_with_message(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_scoring_launch_bytes_per_block():
+    # exact block max reads the block's 16 keys; the Quest bound reads its
+    # min/max box (2 vectors); both write one 4-byte score per block
+    for name, per_block in (("llama8b_32k", 16 * 128 * 2 + 4), ("quest_128k", 2 * 128 * 2 + 4)):
+        w = synth.WORKLOADS[name]
+        q = w.batch * w.n_score_queries * w.n_q_heads * w.head_dim * w.elem_bytes
+        assert bench.score_launch_bytes(w) == w.rows * w.nb_max * per_block + q
+    # the 32K figure quoted with the roofline
+    assert bench.score_launch_bytes(synth.WORKLOADS["llama8b_32k"]) == 537460736
