@@ -14,6 +14,13 @@
  *   sparse_decode_attention  GQA decode attention over only the picked
  *                            blocks, split-K with an online-softmax merge
  *
+ * Combined forms with the same results: sparse_kv_select (top-k + update in
+ * one launch) and sparse_kv_select_attend (top-k + update + attention).
+ * Around the step: sparse_kv_cache_update_importance (eviction by this
+ * step's scores instead of LRU), sparse_kv_append (decode-time growth),
+ * sparse_kv_quest_meta (the Quest boxes), sparse_kv_host_alloc / _free (a
+ * host-memory source) and the split / workspace size helpers.
+ *
  * The method (pages cited by title and section):
  *  - each head reads only its top-K past positions under a per-head,
  *    per-step KV budget ("KV Cache 塞不进 HBM 了", §1 and §3 steps 1-2);
