@@ -213,6 +213,11 @@ class Lag1Pipeline:
 
     def reset(self):
         self.buf.reset()
+        self.rewind()
+
+    def rewind(self):
+        """Restart the schedule at step 0 without touching device state
+        (e.g. before capturing the same steps into a graph)."""
         self.t = 0
         self._upd_prev = None
 
