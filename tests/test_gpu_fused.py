@@ -30,6 +30,10 @@ FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "
     # the largest budget and working set (1024 blocks of 1024 slots), and the largest GQA group (16)
     ("llama8b_32k", dict(batch=1, ctx=65536, budget=16384, capacity=1024), 2, 0),
     ("llama8b_32k", dict(batch=2, n_kv_heads=2, ctx=4096, budget=512), 3, 0),
+    # bf16 with D = 64, float32 with D = 128, and one head per group (MHA)
+    ("llama8b_32k", dict(batch=2, head_dim=64, ctx=4096, budget=512), 3, 0),
+    ("tiny", dict(head_dim=128), 3, 0),
+    ("llama8b_32k", dict(batch=2, n_q_heads=8, ctx=4096, budget=512), 3, 0),
     ("lookahead_1m", dict(ctx=16384), 3, 0),
 ])
 def test_fused_equals_separate_calls(name, kw, steps, splits):
