@@ -87,7 +87,7 @@ def load():
     L.sparse_kv_status_string.restype = C.c_char_p
     for fn in ("sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
                "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_select_attend",
-               "sparse_kv_cache_update_importance", "sparse_kv_append"):
+               "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select"):
         getattr(L, fn).restype = C.c_int
     _lib = L
     return L
