@@ -586,6 +586,7 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     const int len = min(max(seq_lens[b], 0), T);
     SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
     load_slots<kAttnThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
+    cache_plan_clear<kAttnThreads>(cs, k);  // published by the top-k's barriers
 
     const int nn = topk_row<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, sS, tsc);
     int bad;

@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     load_slots<kCacheThreads>(regs, C, sb, ss);
     for (int i = tid; i < k; i += kCacheThreads)
         sS[i] = S[i];
+    cache_plan_clear<kCacheThreads>(cs, k);  // published by the barrier below
     const bool bad_count = n < 0 || n > k || n > C;  // uniform over the workgroup
     if (bad_count) {
         if (tid == 0)
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
     uint32_t *ss = slot_stamp + (size_t)row * C;
     SlotRegs<THREADS> regs;  // in flight while the top-k runs
     load_slots<THREADS>(regs, C, sb, ss);
+    cache_plan_clear<THREADS>(cs, k);  // published by the top-k's barriers
     const int n = tk.run(scores + (size_t)row * NB, len, NB, k, sink, recent, sS);
     for (int i = tid; i < k; i += THREADS)
         sel_blocks[(size_t)row * k + i] = sS[i];

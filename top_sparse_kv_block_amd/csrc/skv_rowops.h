@@ -10,9 +10,11 @@
 namespace skv {
 
 // ------------------------------------------------------------ scans
-// Exclusive prefix sum of v over the workgroup in thread order, and the total.
-template <int THREADS, typename T>
-__device__ __forceinline__ T wg_exclusive_scan(T v, T *wsum, T &total) {
+// Exclusive prefix sum of v over the workgroup in thread order, and the
+// total.  publish(pos, total) runs between the scan's two barriers, so what
+// it writes to LDS is visible to every thread once the scan returns.
+template <int THREADS, typename T, typename F>
+__device__ __forceinline__ T wg_exclusive_scan_publish(T v, T *wsum, T &total, F &&publish) {
     constexpr int WAVES = THREADS / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     (void)lane;
@@ -27,9 +29,16 @@ __device__ __forceinline__ T wg_exclusive_scan(T v, T *wsum, T &total) {
         base += (w < wave) ? s : T(0);
         tot += s;
     }
+    const T pos = base + x - v;
+    publish(pos, tot);
     __syncthreads();
     total = tot;
-    return base + x - v;
+    return pos;
+}
+
+template <int THREADS, typename T>
+__device__ __forceinline__ T wg_exclusive_scan(T v, T *wsum, T &total) {
+    return wg_exclusive_scan_publish<THREADS, T>(v, wsum, total, [](T, T) {});
 }
 
 // Sum of v over the workgroup (every thread gets it).
@@ -81,7 +90,11 @@ __device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remain
 // smallest flagged key; each pass needs two barriers (the histogram buffers
 // alternate, so clearing the next one needs none).  Returns the key;
 // `remaining` = how many keys equal to it are admitted, `n_tau` = how many
-// flagged keys equal it.
+// flagged keys equal it.  The passes stop early once the bin holding the
+// need-th key is admitted whole (its count equals the rank still needed):
+// the returned key is then the smallest one with the decided leading bits,
+// every flagged key at or above it is admitted, and remaining == n_tau
+// (no tie to break), so the admitted set is the one the full passes give.
 template <int THREADS, int KPT>
 __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uint64_t cand, uint32_t need,
                                                  TopkScratch &sc, uint32_t &remaining_out, uint32_t &n_tau_out) {
@@ -136,6 +149,8 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
         mask |= dmask << shift;
         remaining = sc.remaining;
         n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
+        if (n_tau == remaining)  // uniform (read from LDS after the barrier)
+            break;
     }
     remaining_out = remaining;
     n_tau_out = n_tau;
@@ -145,7 +160,7 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
 // Per-row selection under the budget (sink + recent blocks forced, the rest
 // by (score desc, id asc)); writes the ascending ids to out[0, count) and -1
 // to out[count, k) and returns count.  Thread t owns ids [t*KPT, t*KPT+KPT);
-// four 8-bit radix passes over order-preserving keys find the key of the
+// up to four 8-bit radix passes over order-preserving keys find the key of the
 // last admitted block, and one pass of two prefix sums emits the ids in
 // ascending order (ties at the threshold go to the lowest ids).
 template <int THREADS, int KPT>
@@ -527,21 +542,28 @@ __device__ __forceinline__ void load_slots(SlotRegs<THREADS> &r, int C, const in
     }
 }
 
+// Clears the plan's slot column for a selection of up to k entries.  Call
+// it before a barrier that precedes cache_plan_row (a top-k, or the barrier
+// after the selection is staged): the plan relies on the cleared entries
+// being visible to every thread and has no barrier of its own for it.
+template <int THREADS> __device__ __forceinline__ void cache_plan_clear(CacheScratch &cs, int k) {
+    for (int i = threadIdx.x; i < k; i += THREADS)
+        cs.slot_of[i] = -1;
+}
+
 // Plans one step of the row's working set for the selection S[0, nn) (in
 // LDS, ascending): hit detection, compacted misses (ascending), victims
 // (empty slots by index, then (stamp, block) ascending among the slots not
 // selected) and the miss -> victim assignment, all in cs.  The slot table
-// comes in registers from load_slots.  Returns the number of misses, or -1
-// (nothing planned) if the selection or the table is invalid.  Writes no
-// global memory.  THREADS >= 256.
+// comes in registers from load_slots; cs.slot_of[0, nn) must have been
+// cleared by cache_plan_clear before an earlier barrier.  Returns the number
+// of misses, or -1 (nothing planned) if the selection or the table is
+// invalid.  Writes no global memory.  THREADS >= 256.
 template <int THREADS>
 __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const SlotRegs<THREADS> &r, CacheScratch &cs,
                               int &bad_out, const float *__restrict__ importance = nullptr) {
     const int tid = threadIdx.x;
     constexpr int SPT = SlotRegs<THREADS>::SPT;
-    for (int i = tid; i < nn; i += THREADS)
-        cs.slot_of[i] = -1;
-    __syncthreads();
     // validation and hits in one round: the selection must be ascending and
     // in range and the table's ids in [-1, NB); each occupied slot looks its
     // block up in the selection (a binary search that ends whatever S holds)
@@ -588,19 +610,22 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
             cnt += h ? 0 : 1;
         }
     }
+    // the compacted miss list is written between the scan's two barriers,
+    // so the victim pass below (other threads) reads it complete
     int nm;
-    int pos = wg_exclusive_scan<THREADS, int>(cnt, cs.wsum, nm);
-    for (int u = 0; u < per; ++u) {
-        const int i = tid * per + u;
-        if (i < nn && !cs.hit[i])
-            cs.miss_i[pos++] = i;
-    }
+    (void)wg_exclusive_scan_publish<THREADS, int>(cnt, cs.wsum, nm, [&](int pos, int) {
+        for (int u = 0; u < per; ++u) {
+            const int i = tid * per + u;
+            if (i < nn && !cs.hit[i])
+                cs.miss_i[pos++] = i;
+        }
+    });
     // victims: candidate rank r < #misses takes miss r (keys of a valid table
     // are distinct; the slot index breaks ties of a corrupt one).  Q lanes
     // share a candidate, each counting over every Q-th slot (the Q lanes
     // then read Q neighbouring keys: different LDS banks), so the loads of
     // one thread stay few and independent.  (The keys were written before
-    // the barrier of the miss scan.)
+    // the barrier of the validation round.)
     if (nm > 0) {
         constexpr int Q = THREADS >= 1024 ? 8 : (THREADS >= 512 ? 4 : 1);
         for (int base = 0; base < C * Q; base += THREADS) {
