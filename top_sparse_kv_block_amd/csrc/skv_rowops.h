@@ -531,14 +531,21 @@ template <int THREADS> struct SlotRegs {
     uint32_t stamp[SPT];
 };
 
+// The loads are unconditional (slot index clamped to C - 1, C >= 1) and the
+// out-of-range lanes are masked afterwards: with the loads inside a branch
+// the compiler moves the key arithmetic next to them and waits for the data
+// right there, before the top-k's own loads are even issued.
 template <int THREADS>
 __device__ __forceinline__ void load_slots(SlotRegs<THREADS> &r, int C, const int32_t *__restrict__ sb,
                                            const uint32_t *__restrict__ ss) {
 #pragma unroll
     for (int u = 0; u < SlotRegs<THREADS>::SPT; ++u) {
         const int s = threadIdx.x + u * THREADS;
-        r.blk[u] = s < C ? sb[s] : -1;
-        r.stamp[u] = s < C ? ss[s] : 0u;
+        const int sc = min(s, C - 1);
+        const int32_t b = sb[sc];
+        const uint32_t t = ss[sc];
+        r.blk[u] = s < C ? b : -1;
+        r.stamp[u] = s < C ? t : 0u;
     }
 }
 
