@@ -578,6 +578,7 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     __shared__ TopkScratch tsc;
     __shared__ int32_t sS[kMaxK];
     __shared__ CacheScratch cs;
+    __shared__ PlanScratch<kAttnThreads> ps;
     __shared__ AttnSmem<D, GMAX> S;
     int row, split;
     xcd_row_part(row, split);
@@ -586,11 +587,11 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     const int len = min(max(seq_lens[b], 0), T);
     SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
     load_slots<kAttnThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
-    cache_plan_clear<kAttnThreads>(cs, k);  // published by the top-k's barriers
+    select_plan_clear<kAttnThreads>(cs, ps, k);  // published by the emit's barriers
 
-    const int nn = topk_row<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, sS, tsc);
-    int bad;
-    const int nm = cache_plan_row<kAttnThreads>(sS, nn, C, NB, regs, cs, bad);
+    const uint64_t take = topk_take<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, tsc);
+    int nn, bad;
+    const int nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad);
     if (split == 0) {
         for (int i = threadIdx.x; i < k; i += kAttnThreads)
             sel_blocks[(size_t)row * k + i] = sS[i];

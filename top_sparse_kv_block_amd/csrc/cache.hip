@@ -102,16 +102,25 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
 // and the plan is committed by the same workgroup.  Rows up to 8192 blocks
 // run with 512 threads, up to 16384 with 1024, longer rows take the long-row
 // top-k with 1024 threads.
+// Register-resident rows run the top-k's bits straight into the plan
+// (select_plan_row); long rows run topk_long_row, then cache_plan_row.
 template <int THREADS, int KPT> struct SelectTopk {
     TopkScratch sc;
-    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int32_t *out) {
-        return topk_row<THREADS, KPT>(srow, len, NB, k, sink, recent, out, sc);
+    PlanScratch<THREADS> ps;
+    __device__ void clear(CacheScratch &cs, int k) { select_plan_clear<THREADS>(cs, ps, k); }
+    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
+                       const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
+        const uint64_t take = topk_take<THREADS, KPT>(srow, len, NB, k, sink, recent, sc);
+        return select_plan_row<THREADS, KPT>(take, k, C, NB, regs, out, cs, ps, n, bad);
     }
 };
 template <int THREADS> struct SelectTopk<THREADS, 0> {
     TopkLongScratch ls;
-    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int32_t *out) {
-        return topk_long_row<THREADS>(srow, len, NB, k, sink, recent, out, ls);
+    __device__ void clear(CacheScratch &cs, int k) { cache_plan_clear<THREADS>(cs, k); }
+    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
+                       const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
+        n = topk_long_row<THREADS>(srow, len, NB, k, sink, recent, out, ls);
+        return cache_plan_row<THREADS>(out, n, C, NB, regs, cs, bad);
     }
 };
 
@@ -133,14 +142,13 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
     uint32_t *ss = slot_stamp + (size_t)row * C;
     SlotRegs<THREADS> regs;  // in flight while the top-k runs
     load_slots<THREADS>(regs, C, sb, ss);
-    cache_plan_clear<THREADS>(cs, k);  // published by the top-k's barriers
-    const int n = tk.run(scores + (size_t)row * NB, len, NB, k, sink, recent, sS);
+    tk.clear(cs, k);  // published by the top-k's barriers
+    int n, bad;
+    const int nm = tk.run(scores + (size_t)row * NB, len, NB, k, sink, recent, C, regs, sS, cs, n, bad);
     for (int i = tid; i < k; i += THREADS)
         sel_blocks[(size_t)row * k + i] = sS[i];
     if (tid == 0)
         sel_count[row] = n;
-    int bad;
-    const int nm = cache_plan_row<THREADS>(sS, n, C, NB, regs, cs, bad);
     if (bad) {
         if (tid == 0)
             miss_count[row] = -1;

@@ -158,21 +158,22 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
 }
 
 // Per-row selection under the budget (sink + recent blocks forced, the rest
-// by (score desc, id asc)); writes the ascending ids to out[0, count) and -1
-// to out[count, k) and returns count.  Thread t owns ids [t*KPT, t*KPT+KPT);
-// up to four 8-bit radix passes over order-preserving keys find the key of the
-// last admitted block, and one pass of two prefix sums emits the ids in
-// ascending order (ties at the threshold go to the lowest ids).
+// by (score desc, id asc)) as bits: thread t owns ids [t*KPT, t*KPT+KPT) and
+// bit m of the result admits id t*KPT + m.  Up to four 8-bit radix passes
+// over order-preserving keys find the key of the last admitted block (ties
+// at the threshold go to the lowest ids).  A row with at most k valid blocks
+// takes all of them without reading its scores.  Contains barriers.
 template <int THREADS, int KPT>
-__device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent, int32_t *out,
-                        TopkScratch &sc) {
+__device__ uint64_t topk_take(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
+                              TopkScratch &sc) {
     const int tid = threadIdx.x;
     const int nvalid = min(nb_of(len), NB);
     if (nvalid <= k) {
-        for (int i = tid; i < k; i += THREADS)
-            out[i] = i < nvalid ? i : -1;
-        __syncthreads();
-        return nvalid;
+        uint64_t all = 0;
+#pragma unroll
+        for (int m = 0; m < KPT; ++m)
+            all |= (uint64_t)(tid * KPT + m < nvalid) << m;
+        return all;
     }
     const int fs = sink > 0 ? min(nb_of(min(sink, len)), nvalid) : 0;
     const int fr = recent > 0 ? max(0, len - recent) / 16 : nvalid;
@@ -250,17 +251,44 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
             take |= (uint64_t)s << m;
         }
     }
+    return take;
+}
+
+// Writes the ascending ids of the admitted bits to out[0, count) and -1 to
+// out[count, k), count = min(admitted, k); one prefix sum over the threads.
+// publish(pos, bits) also runs between the sum's barriers (pos = the
+// thread's first output index), so all of it is visible on return.
+template <int THREADS, int KPT, typename F>
+__device__ __forceinline__ int topk_emit(uint64_t take, int k, int32_t *out, uint32_t *wsum, F &&publish) {
+    const int tid = threadIdx.x;
     uint32_t tot;
-    uint32_t pos = wg_exclusive_scan<THREADS, uint32_t>((uint32_t)__builtin_popcountll(take), sc.wsum, tot);
+    (void)wg_exclusive_scan_publish<THREADS, uint32_t>(
+        (uint32_t)__builtin_popcountll(take), wsum, tot, [&](uint32_t pos, uint32_t total) {
+            publish(pos, take);
 #pragma unroll
-    for (int m = 0; m < KPT; ++m)
-        if (((take >> m) & 1u) && pos < (uint32_t)k)
-            out[pos++] = tid * KPT + m;
-    tot = min(tot, (uint32_t)k);
-    for (int i = (int)tot + tid; i < k; i += THREADS)
-        out[i] = -1;
-    __syncthreads();
-    return (int)tot;
+            for (int m = 0; m < KPT; ++m)
+                if (((take >> m) & 1u) && pos < (uint32_t)k)
+                    out[pos++] = tid * KPT + m;
+            for (int i = (int)min(total, (uint32_t)k) + tid; i < k; i += THREADS)
+                out[i] = -1;
+        });
+    return (int)min(tot, (uint32_t)k);
+}
+
+// topk_take + topk_emit: the row's selection, ascending, in out[0, k).
+template <int THREADS, int KPT>
+__device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent, int32_t *out,
+                        TopkScratch &sc) {
+    const int tid = threadIdx.x;
+    const int nvalid = min(nb_of(len), NB);
+    if (nvalid <= k) {
+        for (int i = tid; i < k; i += THREADS)
+            out[i] = i < nvalid ? i : -1;
+        __syncthreads();
+        return nvalid;
+    }
+    const uint64_t take = topk_take<THREADS, KPT>(srow, len, NB, k, sink, recent, sc);
+    return topk_emit<THREADS, KPT>(take, k, out, sc.wsum, [](uint32_t, uint64_t) {});
 }
 
 // ------------------------------------------------------------ long rows
@@ -659,6 +687,135 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
         }
     }
     __syncthreads();
+    bad_out = 0;
+    return nm;
+}
+
+// The selection and the working-set plan of a row in one pass, for kernels
+// that run the top-k themselves (same results as topk_row followed by
+// cache_plan_row).  The selection's index of a block is found from the
+// bits and output position of the thread that owns it (published by the
+// emit), not by a search; every candidate slot's eviction rank is computed
+// in the same round as the hit / miss flags, and each miss takes the victim
+// of its rank between the barriers of the miss prefix sum.  Five barriers
+// from the admitted bits to a complete plan.
+template <int THREADS> struct PlanScratch {
+    uint32_t pos[THREADS];   // a thread's first index in the selection
+    uint32_t take[THREADS];  // its admitted bits
+    int32_t victim[kMaxCapacity];  // the slot of eviction rank r
+    uint32_t wsum[16];
+    int iwsum[16];
+    int bad;
+};
+
+// Clears what select_plan_row expects cleared (call before a barrier that
+// precedes it, e.g. before the top-k).
+template <int THREADS>
+__device__ __forceinline__ void select_plan_clear(CacheScratch &cs, PlanScratch<THREADS> &ps, int k) {
+    cache_plan_clear<THREADS>(cs, k);
+    if (threadIdx.x == 0)
+        ps.bad = 0;
+}
+
+// take: topk_take's bits (KPT <= 32, NB <= THREADS * KPT).  Writes the
+// selection to S[0, k) (ascending, -1 padded) and returns its size in nn;
+// returns the number of misses, or -1 with bad_out set if the slot table is
+// invalid (a block id out of range, or a selected block in two slots).
+template <int THREADS, int KPT>
+__device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRegs<THREADS> &r, int32_t *S,
+                               CacheScratch &cs, PlanScratch<THREADS> &ps, int &nn_out, int &bad_out) {
+    static_assert(KPT <= 32, "take bits are kept as 32-bit words");
+    const int tid = threadIdx.x;
+    constexpr int SPT = SlotRegs<THREADS>::SPT;
+    const int nn = topk_emit<THREADS, KPT>(take, k, S, ps.wsum, [&](uint32_t pos, uint64_t t) {
+        ps.pos[tid] = pos;
+        ps.take[tid] = (uint32_t)t;
+    });
+    // claims: an occupied slot whose block is selected takes the block's
+    // selection index (a block held by two slots is caught by the second
+    // claim); every slot stores its eviction key as in cache_plan_row
+    int bad = 0;
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int s = tid + u * THREADS;
+        if (s < C) {
+            const int32_t blk = r.blk[u];
+            if (blk < -1 || blk >= NB)
+                bad = 1;
+            int i = -1;
+            if (blk >= 0 && blk < NB && blk / KPT < THREADS) {
+                const int c = blk / KPT, m = blk - c * KPT;
+                const uint32_t t = ps.take[c];
+                const uint32_t p = ps.pos[c] + (uint32_t)__builtin_popcount(t & ((1u << m) - 1u));
+                if (((t >> m) & 1u) && p < (uint32_t)nn)
+                    i = (int)p;
+            }
+            if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
+                bad = 1;
+            cs.key[s] = i >= 0 ? ~0ull
+                               : (blk < 0 ? (uint64_t)s
+                                          : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk));
+        }
+    }
+    if (bad)
+        ps.bad = 1;
+    __syncthreads();
+    nn_out = nn;
+    if (ps.bad) {  // uniform
+        bad_out = 1;
+        return -1;
+    }
+    // hit flags and miss counts of the selection indices a thread owns ...
+    const int per = (nn + THREADS - 1) / THREADS;
+    int cnt = 0;
+    for (int u = 0; u < per; ++u) {
+        const int i = tid * per + u;
+        if (i < nn) {
+            const bool h = cs.slot_of[i] >= 0;
+            cs.hit[i] = h ? 1 : 0;
+            cnt += h ? 0 : 1;
+        }
+    }
+    // ... and, in the same round, every candidate slot's eviction rank (Q
+    // lanes per candidate, as in cache_plan_row); candidates outnumber the
+    // misses since C >= k
+    {
+        constexpr int Q = THREADS >= 1024 ? 8 : (THREADS >= 512 ? 4 : 1);
+        for (int base = 0; base < C * Q; base += THREADS) {
+            const int t = base + tid;
+            const int s = t / Q, part = t % Q;
+            const bool on = s < C;
+            const uint64_t key = on ? cs.key[s] : ~0ull;
+            int rank = 0;
+            if (on && key != ~0ull) {
+#pragma unroll 8
+                for (int o = part; o < C; o += Q) {
+                    const uint64_t ok = cs.key[o];
+                    rank += (ok < key || (ok == key && o < s)) ? 1 : 0;
+                }
+            }
+            if constexpr (Q >= 2)
+                rank += __builtin_amdgcn_update_dpp(0, rank, DPP_QUAD_XOR1, 0xf, 0xf, false);
+            if constexpr (Q >= 4)
+                rank += __builtin_amdgcn_update_dpp(0, rank, DPP_QUAD_XOR2, 0xf, 0xf, false);
+            if constexpr (Q >= 8)
+                rank += __builtin_amdgcn_update_dpp(0, rank, DPP_ROW_HALF_MIRROR, 0xf, 0xf, false);
+            if (on && part == 0 && key != ~0ull)
+                ps.victim[rank] = s;
+        }
+    }
+    // misses in ascending selection order: miss j takes the victim of rank j
+    int nm;
+    (void)wg_exclusive_scan_publish<THREADS, int>(cnt, ps.iwsum, nm, [&](int pos, int) {
+        for (int u = 0; u < per; ++u) {
+            const int i = tid * per + u;
+            if (i < nn && !cs.hit[i]) {
+                cs.miss_i[pos] = i;
+                cs.slot_of[i] = ps.victim[pos];
+                ++pos;
+            }
+        }
+    });
     bad_out = 0;
     return nm;
 }
