@@ -695,17 +695,20 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
 // that run the top-k themselves (same results as topk_row followed by
 // cache_plan_row).  The selection's index of a block is found from the
 // bits and output position of the thread that owns it (published by the
-// emit), not by a search; every candidate slot's eviction rank is computed
-// in the same round as the hit / miss flags, and each miss takes the victim
-// of its rank between the barriers of the miss prefix sum.  Five barriers
-// from the admitted bits to a complete plan.
+// emit), not by a search; the eviction candidates (slots whose block is not
+// selected) are gathered into a short list while the slots claim their
+// blocks, each is ranked against that list only, in the same round as the
+// hit / miss flags, and each miss takes the victim of its rank between the
+// barriers of the miss prefix sum.  Five barriers from the admitted bits to
+// a complete plan.
 template <int THREADS> struct PlanScratch {
     uint32_t pos[THREADS];   // a thread's first index in the selection
     uint32_t take[THREADS];  // its admitted bits
     int32_t victim[kMaxCapacity];  // the slot of eviction rank r
+    int32_t cand_slot[kMaxCapacity];  // candidate list (keys in CacheScratch::key), any order
     uint32_t wsum[16];
     int iwsum[16];
-    int bad;
+    int bad, n_cand;
 };
 
 // Clears what select_plan_row expects cleared (call before a barrier that
@@ -713,8 +716,10 @@ template <int THREADS> struct PlanScratch {
 template <int THREADS>
 __device__ __forceinline__ void select_plan_clear(CacheScratch &cs, PlanScratch<THREADS> &ps, int k) {
     cache_plan_clear<THREADS>(cs, k);
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         ps.bad = 0;
+        ps.n_cand = 0;
+    }
 }
 
 // take: topk_take's bits (KPT <= 32, NB <= THREADS * KPT).  Writes the
@@ -733,7 +738,8 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
     });
     // claims: an occupied slot whose block is selected takes the block's
     // selection index (a block held by two slots is caught by the second
-    // claim); every slot stores its eviction key as in cache_plan_row
+    // claim); every other slot joins the candidate list with its eviction
+    // key (as in cache_plan_row: empty slots by index, then (stamp, block))
     int bad = 0;
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
@@ -750,11 +756,14 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
                 if (((t >> m) & 1u) && p < (uint32_t)nn)
                     i = (int)p;
             }
-            if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
-                bad = 1;
-            cs.key[s] = i >= 0 ? ~0ull
-                               : (blk < 0 ? (uint64_t)s
-                                          : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk));
+            if (i >= 0) {
+                if (atomicCAS(&cs.slot_of[i], -1, s) != -1)
+                    bad = 1;
+            } else {
+                const int c = atomicAdd(&ps.n_cand, 1);
+                cs.key[c] = blk < 0 ? (uint64_t)s : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk);
+                ps.cand_slot[c] = s;
+            }
         }
     }
     if (bad)
@@ -776,22 +785,27 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
             cnt += h ? 0 : 1;
         }
     }
-    // ... and, in the same round, every candidate slot's eviction rank (Q
-    // lanes per candidate, as in cache_plan_row); candidates outnumber the
-    // misses since C >= k
+    // ... and, in the same round, every candidate's eviction rank among the
+    // candidates (Q lanes per candidate, each counting over every Q-th list
+    // entry; equal keys of a corrupt table rank by slot index); candidates
+    // outnumber the misses since C >= k
     {
         constexpr int Q = THREADS >= 1024 ? 8 : (THREADS >= 512 ? 4 : 1);
-        for (int base = 0; base < C * Q; base += THREADS) {
+        const int nc = ps.n_cand;
+        for (int base = 0; base < nc * Q; base += THREADS) {
             const int t = base + tid;
-            const int s = t / Q, part = t % Q;
-            const bool on = s < C;
-            const uint64_t key = on ? cs.key[s] : ~0ull;
+            const int c = t / Q, part = t % Q;
+            const bool on = c < nc;
+            const uint64_t key = on ? cs.key[c] : ~0ull;
+            const int s = on ? ps.cand_slot[c] : 0;
             int rank = 0;
-            if (on && key != ~0ull) {
-#pragma unroll 8
-                for (int o = part; o < C; o += Q) {
+            if (on) {
+#pragma unroll 4
+                for (int o = part; o < nc; o += Q) {
                     const uint64_t ok = cs.key[o];
-                    rank += (ok < key || (ok == key && o < s)) ? 1 : 0;
+                    rank += ok < key ? 1 : 0;
+                    if (ok == key && o != c)
+                        rank += ps.cand_slot[o] < s ? 1 : 0;
                 }
             }
             if constexpr (Q >= 2)
@@ -800,7 +814,7 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
                 rank += __builtin_amdgcn_update_dpp(0, rank, DPP_QUAD_XOR2, 0xf, 0xf, false);
             if constexpr (Q >= 8)
                 rank += __builtin_amdgcn_update_dpp(0, rank, DPP_ROW_HALF_MIRROR, 0xf, 0xf, false);
-            if (on && part == 0 && key != ~0ull)
+            if (on && part == 0)
                 ps.victim[rank] = s;
         }
     }
