@@ -321,8 +321,39 @@ template <int D, int GMAX> __device__ void combine_waves(const AttnRow &a, AttnS
 // dims (l%16)*D/16 .. of tokens 4(l/16) .. +4, and p[token][head g] reaches
 // it by a row broadcast of lane g.  The lane's output is summed over its
 // row's tokens; the 4 rows are added at the end.
+// One block's K and V in the matrix-core body's lane layout (below).
+template <int D> struct MfmaBlock {
+    using VT = typename std::conditional<D / 8 == 16, u32x4, u32x2>::type;
+    u32x4 kf[D / 32];
+    VT vf[4];
+    bool have;  // wave-uniform: loaded ahead for the wave's first block
+};
+
+// Loads block blk from the source (fetch) or pool slot s into b.
+template <int D>
+__device__ __forceinline__ void mfma_load_block(const AttnRow &a, int blk, int s, bool fetch, MfmaBlock<D> &b) {
+    constexpr int KCH = D / 32, TB = D * 2, VB = D / 8;
+    constexpr size_t kBlockBytes = (size_t)16 * TB;
+    using VT = typename MfmaBlock<D>::VT;
+    const int lane = threadIdx.x & 63, col = lane & 15, rsub = lane >> 4;
+    const size_t k_off = (size_t)col * TB + rsub * 16;       // + 64 c
+    const size_t v_off = (size_t)(4 * rsub) * TB + col * VB;  // + TB i
+    const uint8_t *rk = fetch ? a.src_k + (size_t)blk * kBlockBytes : a.pool_k + (size_t)s * kBlockBytes;
+    const uint8_t *rv = fetch ? a.src_v + (size_t)blk * kBlockBytes : a.pool_v + (size_t)s * kBlockBytes;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+        b.kf[c] = fetch ? load_nt(rk + k_off + c * 64) : load16(rk + k_off + c * 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const VT *pv = reinterpret_cast<const VT *>(rv + v_off + i * TB);
+        b.vf[i] = fetch ? __builtin_nontemporal_load(pv) : *pv;
+    }
+}
+
+// first: the wave's first block (a.i0 + wave), when already loaded
+// (first.have); its K and V registers are used in place of a load.
 template <int D, int GMAX, int DEPTH>
-__device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+__device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMAX> &S, const MfmaBlock<D> &first) {
     constexpr int KCH = D / 32;   // 32-dim chunks of the contraction
     constexpr int VB = D / 8;     // bytes of a token's V per lane
     constexpr int EPLV = D / 16;  // V elements per lane per token
@@ -359,16 +390,14 @@ __device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMA
         return nv > 0 || fetch;
     };
     auto load_block = [&](int blk, int s, bool fetch, u32x4 *kf, VT *vf) {
-        const uint8_t *rk = fetch ? a.src_k + (size_t)blk * kBlockBytes : a.pool_k + (size_t)s * kBlockBytes;
-        const uint8_t *rv = fetch ? a.src_v + (size_t)blk * kBlockBytes : a.pool_v + (size_t)s * kBlockBytes;
+        MfmaBlock<D> t;
+        mfma_load_block<D>(a, blk, s, fetch, t);
 #pragma unroll
         for (int c = 0; c < KCH; ++c)
-            kf[c] = fetch ? load_nt(rk + k_off + c * 64) : load16(rk + k_off + c * 64);
+            kf[c] = t.kf[c];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const VT *pv = reinterpret_cast<const VT *>(rv + v_off + i * TB);
-            vf[i] = fetch ? __builtin_nontemporal_load(pv) : *pv;
-        }
+        for (int i = 0; i < 4; ++i)
+            vf[i] = t.vf[i];
     };
     auto attend_block = [&](int s, int nv, bool fetch, const u32x4 *kf, const VT *vf) {
         if (fetch) {
@@ -452,7 +481,15 @@ __device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMA
         }
     } else {
         static_assert(DEPTH == 1, "one or two blocks in flight");
-        for (int i = a.i0 + wave; i < a.i1; i += kAttnWaves) {
+        int i = a.i0 + wave;
+        if (first.have) {  // wave-uniform; i < a.i1 when set
+            int blk, s, nv;
+            bool f;
+            if (describe(i, blk, s, nv, f))
+                attend_block(s, nv, f, first.kf, first.vf);
+            i += kAttnWaves;
+        }
+        for (; i < a.i1; i += kAttnWaves) {
             int blk, s, nv;
             bool f;
             u32x4 kf[KCH];
@@ -489,11 +526,18 @@ __device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMA
 }
 
 template <typename E, int D, int GMAX, int DEPTH>
-__device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+__device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S, const MfmaBlock<D> &first) {
     if constexpr (E::bytes == 2)
-        attn_body_mfma<D, GMAX, DEPTH>(a, S);
+        attn_body_mfma<D, GMAX, DEPTH>(a, S, first);
     else
         attn_body_valu<E, D, GMAX, DEPTH>(a, S);
+}
+
+template <typename E, int D, int GMAX, int DEPTH>
+__device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S) {
+    MfmaBlock<D> none;
+    none.have = false;
+    attn_body<E, D, GMAX, DEPTH>(a, S, none);
 }
 
 template <typename E, int D>
@@ -588,10 +632,32 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
     load_slots<kAttnThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
     select_plan_clear<kAttnThreads>(cs, ps, k);  // published by the emit's barriers
+    AttnRow a;
+    init_row<E, D>(a, q, pool_k, pool_v, src_k, src_v, row, b, j, Hq, Hq / Hkv, C, T, split, splits, scale_log2,
+                   part, out, lse);
+    constexpr int depth = fused_min_waves<E, D, GMAX, KPT>() == 4 ? 1 : fused_depth<E, D, GMAX>();
 
     const uint64_t take = topk_take<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, tsc);
+    // once the hits are known, each wave loads its first block (a hit from
+    // its pool slot, a miss from the source) so that the load is in flight
+    // while the rest of the plan is worked out
+    MfmaBlock<D> first;
+    first.have = false;
+    auto load_first = [&](int nn) {
+        if constexpr (E::bytes == 2 && depth == 1) {
+            const int i0 = split * per_split;
+            const int i = i0 + (threadIdx.x >> 6);
+            if (i < min(i0 + per_split, nn)) {
+                const int s = cs.slot_of[i];
+                if (s >= 0 || src_k) {
+                    mfma_load_block<D>(a, sS[i], s, s < 0, first);
+                    first.have = true;
+                }
+            }
+        }
+    };
     int nn, bad;
-    const int nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad);
+    const int nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad, load_first);
     if (split == 0) {
         for (int i = threadIdx.x; i < k; i += kAttnThreads)
             sel_blocks[(size_t)row * k + i] = sS[i];
@@ -605,17 +671,13 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
                                       miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);
         }
     }
-    AttnRow a;
-    init_row<E, D>(a, q, pool_k, pool_v, src_k, src_v, row, b, j, Hq, Hq / Hkv, C, T, split, splits, scale_log2,
-                   part, out, lse);
     a.blk = sS;
     a.slot = cs.slot_of;
     a.hit = cs.hit;
     a.len = len;
     a.i0 = split * per_split;
     a.i1 = bad ? a.i0 : min(a.i0 + per_split, nn);  // an invalid row attends nothing
-    constexpr int depth = fused_min_waves<E, D, GMAX, KPT>() == 4 ? 1 : fused_depth<E, D, GMAX>();
-    attn_body<E, D, GMAX, depth>(a, S);
+    attn_body<E, D, GMAX, depth>(a, S, first);
 }
 
 // One workgroup per row: merge the row's G heads over the splits (when

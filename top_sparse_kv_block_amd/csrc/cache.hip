@@ -111,7 +111,7 @@ template <int THREADS, int KPT> struct SelectTopk {
     __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
                        const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
         const uint64_t take = topk_take<THREADS, KPT>(srow, len, NB, k, sink, recent, sc);
-        return select_plan_row<THREADS, KPT>(take, k, C, NB, regs, out, cs, ps, n, bad);
+        return select_plan_row<THREADS, KPT>(take, k, C, NB, regs, out, cs, ps, n, bad, [](int) {});
     }
 };
 template <int THREADS> struct SelectTopk<THREADS, 0> {

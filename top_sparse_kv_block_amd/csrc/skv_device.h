@@ -188,6 +188,16 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int nb_of(int len) { return (len + 15) >> 4; }
 
+// Workgroup barrier that orders LDS accesses only: each wave waits for its
+// own LDS operations, not for its global loads and stores, so global loads
+// issued before it stay in flight across it.  For barriers whose only
+// purpose is to share LDS data (the row routines' scans and histograms).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // (row, part) handled by this workgroup of a (parts x rows) grid.  The
 // dispatcher deals workgroups to the 8 XCDs in turn, so with rows % 8 == 0
 // the parts of one row are laid out 8 apart in dispatch order: they run on

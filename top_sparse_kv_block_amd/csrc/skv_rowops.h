@@ -12,7 +12,8 @@ namespace skv {
 // ------------------------------------------------------------ scans
 // Exclusive prefix sum of v over the workgroup in thread order, and the
 // total.  publish(pos, total) runs between the scan's two barriers, so what
-// it writes to LDS is visible to every thread once the scan returns.
+// it writes to LDS is visible to every thread once the scan returns.  The
+// barriers order LDS only (global writes made in publish are not ordered).
 template <int THREADS, typename T, typename F>
 __device__ __forceinline__ T wg_exclusive_scan_publish(T v, T *wsum, T &total, F &&publish) {
     constexpr int WAVES = THREADS / 64;
@@ -21,7 +22,7 @@ __device__ __forceinline__ T wg_exclusive_scan_publish(T v, T *wsum, T &total, F
     const T x = (T)wave_incl_scan((uint32_t)v);
     if (lane == 63)
         wsum[wave] = x;
-    __syncthreads();
+    lds_barrier();
     T base = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) {
@@ -31,7 +32,7 @@ __device__ __forceinline__ T wg_exclusive_scan_publish(T v, T *wsum, T &total, F
     }
     const T pos = base + x - v;
     publish(pos, tot);
-    __syncthreads();
+    lds_barrier();
     total = tot;
     return pos;
 }
@@ -118,7 +119,7 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
     }
     if (tid < 256)
         sc.hist[0][tid] = 0;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int w = 0; w < THREADS / 64; ++w) {
         lo = min(lo, sc.wlo[w]);
@@ -141,10 +142,10 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
         }
         if (tid < 256)
             sc.hist[(pass + 1) & 1][tid] = 0;  // last read by the previous pass's pick
-        __syncthreads();
+        lds_barrier();
         if (tid < 64)
             pick_digit(hist, remaining, sc);
-        __syncthreads();
+        lds_barrier();
         prefix |= sc.digit << shift;
         mask |= dmask << shift;
         remaining = sc.remaining;
@@ -726,9 +727,13 @@ __device__ __forceinline__ void select_plan_clear(CacheScratch &cs, PlanScratch<
 // selection to S[0, k) (ascending, -1 padded) and returns its size in nn;
 // returns the number of misses, or -1 with bad_out set if the slot table is
 // invalid (a block id out of range, or a selected block in two slots).
-template <int THREADS, int KPT>
+// after_claims(nn) runs once the selection is in S and the hits have their
+// slots in cs.slot_of (misses still -1); the barriers after it order LDS
+// only, so global loads it issues stay in flight through the rest.
+template <int THREADS, int KPT, typename F>
 __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRegs<THREADS> &r, int32_t *S,
-                               CacheScratch &cs, PlanScratch<THREADS> &ps, int &nn_out, int &bad_out) {
+                               CacheScratch &cs, PlanScratch<THREADS> &ps, int &nn_out, int &bad_out,
+                               F &&after_claims) {
     static_assert(KPT <= 32, "take bits are kept as 32-bit words");
     const int tid = threadIdx.x;
     constexpr int SPT = SlotRegs<THREADS>::SPT;
@@ -768,12 +773,13 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
     }
     if (bad)
         ps.bad = 1;
-    __syncthreads();
+    lds_barrier();
     nn_out = nn;
     if (ps.bad) {  // uniform
         bad_out = 1;
         return -1;
     }
+    after_claims(nn);  // the selection and its hits are known here
     // hit flags and miss counts of the selection indices a thread owns ...
     const int per = (nn + THREADS - 1) / THREADS;
     int cnt = 0;
