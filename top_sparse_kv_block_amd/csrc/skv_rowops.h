@@ -165,7 +165,7 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
 // at the threshold go to the lowest ids).  A row with at most k valid blocks
 // takes all of them without reading its scores.  Contains barriers.
 template <int THREADS, int KPT>
-__device__ uint64_t topk_take(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
+__device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
                               TopkScratch &sc) {
     const int tid = threadIdx.x;
     const int nvalid = min(nb_of(len), NB);
