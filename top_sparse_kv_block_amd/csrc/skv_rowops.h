@@ -199,24 +199,34 @@ __device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, in
     if constexpr ((KPT == 4 || KPT >= 16) && KPT % 4 == 0) {
         // 16-byte loads: a quarter of the load instructions and cache lines
         // touched (measured: 1.4% on the whole 32K step at 4 keys per
-        // thread; at 8 the vector form spills in the fused kernel)
-        const bool vec = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) && base + KPT <= nvalid;
+        // thread; at 8 the vector form spills in the fused kernel).  With a
+        // 16-byte aligned row of NB % 4 == 0 blocks (uniform) the loads are
+        // unconditional, the index clamped into the row and ids past the
+        // valid length masked afterwards, so all of a thread's loads are in
+        // flight at once (a branch around each one makes the compiler wait
+        // for it before the next).
+        const bool vec = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) && (NB & 3) == 0;
+        if (vec) {
+            float4 f[KPT / 4];
 #pragma unroll
-        for (int u = 0; u < KPT / 4; ++u) {
-            float4 f;
-            if (vec) {
-                f = *reinterpret_cast<const float4 *>(srow + base + 4 * u);
-            } else {
-                const int i = base + 4 * u;
-                f.x = i < nvalid ? srow[i] : 0.0f;
-                f.y = i + 1 < nvalid ? srow[i + 1] : 0.0f;
-                f.z = i + 2 < nvalid ? srow[i + 2] : 0.0f;
-                f.w = i + 3 < nvalid ? srow[i + 3] : 0.0f;
+            for (int u = 0; u < KPT / 4; ++u)
+                f[u] = *reinterpret_cast<const float4 *>(srow + min(base + 4 * u, NB - 4));
+#pragma unroll
+            for (int u = 0; u < KPT / 4; ++u) {
+                classify(4 * u, f[u].x);
+                classify(4 * u + 1, f[u].y);
+                classify(4 * u + 2, f[u].z);
+                classify(4 * u + 3, f[u].w);
             }
-            classify(4 * u, f.x);
-            classify(4 * u + 1, f.y);
-            classify(4 * u + 2, f.z);
-            classify(4 * u + 3, f.w);
+        } else {
+#pragma unroll
+            for (int u = 0; u < KPT / 4; ++u) {
+                const int i = base + 4 * u;
+                classify(4 * u, i < nvalid ? srow[i] : 0.0f);
+                classify(4 * u + 1, i + 1 < nvalid ? srow[i + 1] : 0.0f);
+                classify(4 * u + 2, i + 2 < nvalid ? srow[i + 2] : 0.0f);
+                classify(4 * u + 3, i + 3 < nvalid ? srow[i + 3] : 0.0f);
+            }
         }
     } else {
 #pragma unroll
@@ -358,22 +368,32 @@ __device__ int topk_long_row(const float *__restrict__ srow, int len, int NB, in
     }
     // f(id, key, is_candidate) for this thread's ids, every lane of a wave
     // calling f together (keys of non-candidates are 0).  Thread t reads the
-    // 4-id groups t, t + THREADS, ... with 16-byte loads when the row is
-    // 16-byte aligned (BATCH groups in flight), else single floats.
-    const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+    // 4-id groups t, t + THREADS, ... with BATCH groups in flight: 16-byte
+    // loads when the row is 16-byte aligned and NB a multiple of 4, else
+    // single floats.  The 16-byte loads are unconditional (group index
+    // clamped into the row, ids past the valid length masked afterwards):
+    // with each load in a branch of its own the compiler waits for every
+    // one before issuing the next.
+    const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0 && (NB & 3) == 0;  // uniform
+    const int gmax = (NB >> 2) - 1;
     auto stream = [&](auto &&f) {
         const int ngroups = (nvalid + 3) >> 2;
         for (int g0 = tid; g0 < ngroups; g0 += BATCH * THREADS) {
             float v[BATCH][4];
+            if (vec) {
+                u32x4 w[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const int g = g0 + u * THREADS;
-                if (vec && 4 * g + 3 < nvalid) {
-                    const u32x4 w = load16(srow + 4 * g);
+                for (int u = 0; u < BATCH; ++u)
+                    w[u] = load16(srow + 4 * min(g0 + u * THREADS, gmax));
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        v[u][e] = __uint_as_float(w[e]);
-                } else {
+                        v[u][e] = 4 * (g0 + u * THREADS) + e < nvalid ? __uint_as_float(w[u][e]) : 0.0f;
+            } else {
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u) {
+                    const int g = g0 + u * THREADS;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         v[u][e] = 4 * g + e < nvalid ? srow[4 * g + e] : 0.0f;
