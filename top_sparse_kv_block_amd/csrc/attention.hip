@@ -26,8 +26,10 @@
 //
 // select_attend_kernel: grid (splits, rows).  Every workgroup of a row first
 // recomputes the row's top-k and working-set plan in LDS (a few KB of scores
-// and slot state, identical code to the standalone kernels, so identical
-// results), then attends its share.  Split 0 also writes the selection and
+// and slot state: the standalone kernels' radix select, then a plan built
+// straight from the top-k's per-thread bits that gives the standalone
+// working-set update's result bit for bit), then attends its share, the
+// first block of each wave loaded as soon as the plan knows its hits.  Split 0 also writes the selection and
 // the step's lists.  The slot table is only read here; merge_commit_kernel
 // applies the plan after every workgroup has read the old table.  This
 // replaces three launches and their global round trips with one: the

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
 }
 
 // select_kernel: the top-k and the working-set update of one row in one
-// workgroup (the two calls' code, so the same results): the row's selection
+// workgroup (the same results as the two calls, bit for bit): the row's selection
 // stays in LDS between the two, the slot table is read while the top-k runs,
 // and the plan is committed by the same workgroup.  Rows up to 8192 blocks
 // run with 512 threads, up to 16384 with 1024, longer rows take the long-row
