@@ -79,3 +79,30 @@ def test_fused_flags_a_corrupt_table():
     G = w.group
     assert not host(buf.out)[0, :G].any() and np.all(np.isneginf(host(buf.lse)[0, :G]))
     assert np.isfinite(host(buf.lse)[0, G:]).all()
+
+
+@pytest.mark.parametrize("capacity", [32, 48])
+def test_fused_rows_shorter_than_the_budget(capacity):
+    """Rows with at most k valid blocks take every valid block without
+    reading their scores; an empty row selects and attends nothing.  Lengths:
+    full, a partial 5-block row, empty, exactly k blocks."""
+    w = synth.WORKLOADS["llama8b_32k"].scaled(batch=4, ctx=4096, budget=512, capacity=capacity, steps=3)
+    data = synth.gen_workload(w)
+    lens_np = np.array([w.ctx, 16 * 5 - 3, 0, 16 * w.k_blocks], dtype=np.int32)
+    splits = B.sparse_kv_select_attend_splits(B.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx,
+                                                           w.dtype), w.k_blocks)
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
+                     num_splits=splits)
+    a, b = LayerBuffers(cfg), LayerBuffers(cfg)
+    K, V, lens = dev(data["K"]), dev(data["V"]), dev(lens_np)
+    for t in range(w.steps):
+        log("fused vs separate, short rows", capacity, "step", t)
+        q, sq = dev(data["q"][t]), dev(data["score_q"][t])
+        decode_step(a, q, sq, K, lens, K, V, fused=False)
+        decode_step(b, q, sq, K, lens, K, V, fused=True)
+        torch.cuda.synchronize()
+        for f in FIELDS:
+            np.testing.assert_array_equal(host(getattr(b, f)), host(getattr(a, f)), err_msg=f"{f} at step {t}")
+    counts = host(b.sel_count).reshape(w.batch, w.n_kv_heads)
+    assert (counts[1] == 5).all() and (counts[2] == 0).all() and (counts[3] == w.k_blocks).all()
+    assert not host(b.out)[2].any() and np.all(np.isneginf(host(b.lse)[2]))
