@@ -85,3 +85,37 @@ def test_select_lists_only_and_corrupt_table():
     np.testing.assert_array_equal(host(s["slot_block"])[0], table[0])  # untouched
     assert host(s["clock"]).tolist() == [0, 1]
     assert host(s["sel_count"]).tolist() == [k, k]
+
+
+@pytest.mark.parametrize("sink,recent", [(0, 0), (16, 48)])
+def test_select_rows_shorter_than_the_budget(sink, recent):
+    """Rows with at most k valid blocks (take-all, no score reads), a partial
+    5-block row, an empty row and a row of exactly k blocks, C > k."""
+    B_, Hkv, T, k, C, D = 4, 2, 16 * 1024, 32, 40, 64
+    P, NB = B_ * Hkv, T // 16
+    rng = np.random.default_rng(7 + sink)
+    shape = B.make_shape(B_, 4 * Hkv, Hkv, D, T, "f32")
+    dl = dev(np.array([T, 16 * 5 - 3, 0, 16 * k], dtype=np.int32))
+    K = torch.randn(B_, Hkv, T, D, device="cuda")
+    V = torch.randn(B_, Hkv, T, D, device="cuda")
+    a, b = _state(P, k, C), _state(P, k, C)
+    pa = [torch.zeros(P, C, 16, D, device="cuda") for _ in range(2)]
+    pb = [torch.zeros(P, C, 16, D, device="cuda") for _ in range(2)]
+    base = rng.standard_normal((P, NB)).astype(np.float32)
+    for t in range(3):
+        sc = dev((base + 0.3 * rng.standard_normal((P, NB))).astype(np.float32))
+        log("select short rows", (sink, recent), "step", t)
+        B.sparse_kv_topk(shape, sc, dl, k, sink, recent, a["sel_blocks"], a["sel_count"])
+        B.sparse_kv_cache_update(shape, k, C, a["sel_blocks"], a["sel_count"], a["slot_block"], a["slot_stamp"],
+                                 a["clock"], a["sel_slot"], a["sel_hit"], a["miss_block"], a["miss_slot"],
+                                 a["miss_count"], K, V, B.SKV_SRC_DEVICE, pa[0], pa[1])
+        B.sparse_kv_select(shape, sc, dl, k, sink, recent, C, b["sel_blocks"], b["sel_count"], b["slot_block"],
+                           b["slot_stamp"], b["clock"], b["sel_slot"], b["sel_hit"], b["miss_block"], b["miss_slot"],
+                           b["miss_count"], K, V, B.SKV_SRC_DEVICE, pb[0], pb[1])
+        torch.cuda.synchronize()
+        for f in FIELDS + ("slot_block", "slot_stamp", "clock"):
+            np.testing.assert_array_equal(host(b[f]), host(a[f]), err_msg=f"{f} at step {t}")
+        for x, y in zip(pa, pb):
+            assert torch.equal(x, y)
+    counts = host(b["sel_count"]).reshape(B_, Hkv)
+    assert (counts[1] == 5).all() and (counts[2] == 0).all() and (counts[3] == k).all()
