@@ -61,6 +61,7 @@ def _declare(L):
     L.oracle_lru_flush.argtypes = [_p]
     L.oracle_lru_get.argtypes = [_p, _p]
     L.oracle_lru_order.argtypes = [_p, _p]
+    L.oracle_lru_load.argtypes = [_p, _p, _p]
     L.oracle_lru_step.argtypes = [_p, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_gather.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_capped_step.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
@@ -169,6 +170,18 @@ class LRU:
     def flush(self):
         lib().oracle_lru_flush(self._h)
 
+    def load(self, slot_block, slot_stamp):
+        """Start every row from a given table: ``slot_block`` [rows, cap]
+        int32 as given, the occupied slots ordered least recent first by
+        (stamp, block id, slot) from ``slot_stamp`` [rows, cap] (uint32 or
+        int32 bits): the stamp is the step of a slot's last touch, and blocks
+        touched in one step count in ascending id order.  The table is not
+        checked here; a step flags a row whose table is invalid."""
+        sb = _c(slot_block, np.int32).reshape(self.rows, self.cap)
+        st = _c(np.asarray(slot_stamp).view(np.uint32) if np.asarray(slot_stamp).dtype == np.int32
+                else slot_stamp, np.uint32).reshape(self.rows, self.cap)
+        lib().oracle_lru_load(self._h, _ptr(sb), _ptr(st))
+
     def slot_block(self):
         out = np.empty((self.rows, self.cap), dtype=np.int32)
         lib().oracle_lru_get(self._h, _ptr(out))
@@ -199,8 +212,9 @@ def capped_step(slot_block, sel, sel_count, scores, nb_limit):
     the unselected resident slots with the lowest current score (ties: lower
     block id).  ``slot_block`` [rows, cap] int32 is updated in place; scores
     [rows, nb_max] are the step's block scores (float64).  Returns the lists
-    like ``LRU.step``; a row with invalid input gets miss_count = -1 and is
-    left untouched."""
+    like ``LRU.step``; a row with invalid input (a bad selection, a table id
+    outside [-1, nb_limit) or a block held by two slots) gets miss_count = -1
+    and padded lists and is left untouched."""
     assert slot_block.dtype == np.int32 and slot_block.flags.c_contiguous
     rows, cap = slot_block.shape
     sel = _c(sel, np.int32).reshape(rows, -1)

@@ -13,6 +13,11 @@ LRU, hit detection + replacement + fetch in one pass; "KV Cache å¡žä¸è¿› HBM äº
 * victims are the empty slots in ascending slot order, then resident slots
   from the least recently used end whose block is not selected;
 * afterwards every selected block is touched in ascending block order.
+
+A step refuses (returns None and changes nothing) a selection that is not
+strictly ascending, too long or out of range, and a slot table that holds
+an id out of range or one block in two slots (the table maps each resident
+block to one slot: KV-Cache åŽ‹ç¼©æŠ€æœ¯çš„å·¥ç¨‹åŽŸç† Â§5.2).
 """
 
 from __future__ import annotations
@@ -31,6 +36,15 @@ class ListLRU:
         self.slot_block = [-1] * self.cap
         self.lru.clear()
 
+    def load(self, slot_block, last_touch):
+        """Start from a given table; ``last_touch[s]`` is the step at which
+        slot s was last touched (blocks touched in one step count in
+        ascending id order)."""
+        self.slot_block = [int(b) for b in slot_block]
+        occupied = [s for s in range(self.cap) if self.slot_block[s] >= 0]
+        occupied.sort(key=lambda s: (int(last_touch[s]), self.slot_block[s], s))
+        self.lru = OrderedDict((s, None) for s in occupied)
+
     def step(self, S, nb_limit=None):
         """Apply one selection; returns (sel_slot, sel_hit, misses[(block, slot)]) or None if invalid."""
         S = list(S)
@@ -39,6 +53,11 @@ class ListLRU:
         if any(b < 0 or (nb_limit is not None and b >= nb_limit) for b in S):
             return None
         if any(S[i] <= S[i - 1] for i in range(1, len(S))):
+            return None
+        resident = [b for b in self.slot_block if b != -1]
+        if any(b < -1 or (nb_limit is not None and b >= nb_limit) for b in self.slot_block):
+            return None
+        if len(set(resident)) != len(resident):
             return None
         where = {b: s for s, b in enumerate(self.slot_block) if b >= 0}
         chosen = set(S)

@@ -300,9 +300,20 @@ int oracle_topk(int B, int Hkv, int nb_max, const double *scores, const int32_t 
  *             from the least-recent end, skipping slots that hold a block of S
  *   miss i goes to victim i; then every block of S is touched in ascending
  *   block order (moved or appended to the most-recent end).
- * An invalid selection (count outside [0, min(k, cap)], not strictly
- * ascending, or an id outside [0, nb_limit)) leaves the row untouched and
- * reports miss_count = -1.
+ * An invalid row leaves its state untouched, reports miss_count = -1 and
+ * gets padded lists (sel_slot -1, sel_hit 0, miss_block / miss_slot -1).  A
+ * row is invalid when its selection is (count outside [0, min(k, cap)], not
+ * strictly ascending, or an id outside [0, nb_limit)) or when its slot table
+ * is: an id outside [-1, nb_limit), or one block held by two slots, selected
+ * or not.  The slot table is a block table (KV-Cache 压缩技术的工程原理
+ * §5.2): it maps each resident block to the one slot holding its bytes, so
+ * a block that appears twice is a broken mapping whatever this step picks.
+ *
+ * oracle_lru_load starts the rows from a given table: slot_block as given,
+ * and the occupied slots linked least recent first in the order of
+ * (stamp, block id, slot) -- the stamp of a slot being the step at which it
+ * was last touched, and blocks touched in one step counting in ascending id
+ * order, as the step below touches them.
  */
 typedef struct {
     int rows, cap;
@@ -408,6 +419,76 @@ static int in_sorted(const int32_t *S, int n, int32_t x)
     return 0;
 }
 
+/* 1 if the row's selection S[0, n) and slot table sb[0, C) are valid input
+ * for a working-set step (see the rules above), else 0. */
+static int row_input_ok(const int32_t *S, int n, int k_max, int nb_limit, const int32_t *sb, int C)
+{
+    if (n < 0 || n > k_max || n > C)
+        return 0;
+    for (int i = 0; i < n; ++i)
+        if (S[i] < 0 || S[i] >= nb_limit || (i > 0 && S[i] <= S[i - 1]))
+            return 0;
+    for (int s = 0; s < C; ++s) {
+        if (sb[s] < -1 || sb[s] >= nb_limit)
+            return 0;
+        for (int t = 0; t < s; ++t)
+            if (sb[s] >= 0 && sb[t] == sb[s])
+                return 0;
+    }
+    return 1;
+}
+
+/* the lists of an invalid row: nothing selected, nothing missed */
+static void pad_invalid_row(int k_max, int32_t *ss, uint8_t *sh, int32_t *mb, int32_t *ms, int32_t *mc)
+{
+    for (int i = 0; i < k_max; ++i) {
+        ss[i] = -1;
+        sh[i] = 0;
+        mb[i] = ms[i] = -1;
+    }
+    *mc = -1;
+}
+
+typedef struct {
+    uint32_t stamp;
+    int32_t blk, slot;
+} orc_touch;
+
+static int by_touch(const void *a, const void *b)
+{
+    const orc_touch *x = (const orc_touch *)a, *y = (const orc_touch *)b;
+    if (x->stamp != y->stamp)
+        return x->stamp < y->stamp ? -1 : 1;
+    if (x->blk != y->blk)
+        return x->blk < y->blk ? -1 : 1;
+    return (x->slot > y->slot) - (x->slot < y->slot);
+}
+
+void oracle_lru_load(oracle_lru *h, const int32_t *slot_block, const uint32_t *slot_stamp)
+{
+    const int C = h->cap;
+    orc_touch *t = (orc_touch *)malloc(sizeof(orc_touch) * (size_t)(C > 0 ? C : 1));
+    for (int r = 0; r < h->rows; ++r) {
+        int32_t *sb = h->slot_block + (size_t)r * C;
+        int n = 0;
+        for (int s = 0; s < C; ++s) {
+            sb[s] = slot_block[(size_t)r * C + s];
+            h->prev[(size_t)r * C + s] = h->next[(size_t)r * C + s] = -1;
+            if (sb[s] >= 0) {
+                t[n].stamp = slot_stamp[(size_t)r * C + s];
+                t[n].blk = sb[s];
+                t[n].slot = s;
+                ++n;
+            }
+        }
+        h->head[r] = h->tail[r] = -1;
+        qsort(t, (size_t)n, sizeof(orc_touch), by_touch);
+        for (int i = 0; i < n; ++i)
+            append_slot(h, r, t[i].slot);
+    }
+    free(t);
+}
+
 int oracle_lru_step(oracle_lru *h, int k_max, int nb_limit, const int32_t *sel, const int32_t *sel_count,
                     int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block, int32_t *miss_slot,
                     int32_t *miss_count)
@@ -416,19 +497,15 @@ int oracle_lru_step(oracle_lru *h, int k_max, int nb_limit, const int32_t *sel, 
 #pragma omp parallel for schedule(dynamic)
     for (int r = 0; r < h->rows; ++r) {
         const int32_t *S = sel + (size_t)r * k_max;
-        int n = sel_count[r];
-        int ok = n >= 0 && n <= k_max && n <= C;
-        for (int i = 0; ok && i < n; ++i)
-            if (S[i] < 0 || S[i] >= nb_limit || (i > 0 && S[i] <= S[i - 1]))
-                ok = 0;
-        if (!ok) {
-            miss_count[r] = -1;
-            continue;
-        }
+        const int n = sel_count[r];
         int32_t *sb = h->slot_block + (size_t)r * C;
         int32_t *ss = sel_slot + (size_t)r * k_max;
         uint8_t *sh = sel_hit + (size_t)r * k_max;
         int32_t *mb = miss_block + (size_t)r * k_max, *ms = miss_slot + (size_t)r * k_max;
+        if (!row_input_ok(S, n, k_max, nb_limit, sb, C)) {
+            pad_invalid_row(k_max, ss, sh, mb, ms, miss_count + r);
+            continue;
+        }
         int32_t *victim = (int32_t *)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
         int nm = 0;
         for (int i = 0; i < n; ++i) {
@@ -490,9 +567,9 @@ int oracle_lru_step(oracle_lru *h, int k_max, int nb_limit, const int32_t *sel, 
  * ascending.  Miss i goes to victim i.
  *
  * The slot table [rows, cap] is the caller's and is updated in place.  An
- * invalid row (count outside [0, min(k, cap)], a selection not strictly
- * ascending or out of [0, nb_limit), a table id outside [-1, nb_limit), or a
- * selected block held by two slots) is left untouched with miss_count = -1.
+ * invalid row (the same rules as the LRU step: a bad selection, a table id
+ * outside [-1, nb_limit), or a block held by two slots) is left untouched
+ * with miss_count = -1 and padded lists.
  */
 typedef struct {
     double score;
@@ -516,25 +593,14 @@ int oracle_capped_step(int rows, int cap, int k_max, int nb_limit, int nb_max, c
     for (int r = 0; r < rows; ++r) {
         const int32_t *S = sel + (size_t)r * k_max;
         int32_t *sb = slot_block + (size_t)r * C;
-        int n = sel_count[r];
-        int ok = n >= 0 && n <= k_max && n <= C;
-        for (int i = 0; ok && i < n; ++i)
-            if (S[i] < 0 || S[i] >= nb_limit || (i > 0 && S[i] <= S[i - 1]))
-                ok = 0;
-        for (int s = 0; ok && s < C; ++s) {
-            if (sb[s] < -1 || sb[s] >= nb_limit)
-                ok = 0;
-            for (int t = 0; ok && t < s; ++t)
-                if (sb[s] >= 0 && sb[t] == sb[s] && in_sorted(S, n, sb[s]))
-                    ok = 0;
-        }
-        if (!ok) {
-            miss_count[r] = -1;
-            continue;
-        }
+        const int n = sel_count[r];
         int32_t *ss = sel_slot + (size_t)r * k_max;
         uint8_t *sh = sel_hit + (size_t)r * k_max;
         int32_t *mb = miss_block + (size_t)r * k_max, *ms = miss_slot + (size_t)r * k_max;
+        if (!row_input_ok(S, n, k_max, nb_limit, sb, C)) {
+            pad_invalid_row(k_max, ss, sh, mb, ms, miss_count + r);
+            continue;
+        }
         orc_cand *cand = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(C > 0 ? C : 1));
         int32_t *victim = (int32_t *)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
         int nm = 0;
