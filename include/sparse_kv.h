@@ -188,8 +188,12 @@ skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int
  *               sources build the lists only (the "no-IO" control).
  * Bad input seen on the device (a selection not strictly ascending, an id
  * outside [0, NB), a count outside [0, k_blocks], or a corrupt slot table:
- * an id outside [-1, NB), or a selected block held by two slots) leaves the
- * row untouched and sets miss_count = -1 for it.
+ * an id outside [-1, NB), or one block held by two slots, selected or not --
+ * the table maps each resident block to one slot, a block table as in
+ * KV-Cache 压缩技术的工程原理 §5.2) refuses the row: its slot table, stamps,
+ * clock and pool stay untouched, miss_count = -1, and its lists are padded
+ * (sel_slot -1, sel_hit 0, miss_block / miss_slot -1), so an attention call
+ * over them reads nothing for that row.
  * Cross-layer prefetch (HiSparse promo, insight 3: picks overlap between
  * layers, so the previous layer's picks are fetched for the next layer
  * before its own are known): call this for layer l+1's state and source with
@@ -317,8 +321,9 @@ skv_status sparse_decode_attention(const skv_shape *shape, const void *q, void *
  * attending its share, so the three stages cost one pass over the scores
  * and slot table instead of three launches with global round trips in
  * between; the plan is committed to the slot table, stamps and clock at the
- * end of the call.  A row whose slot table is found corrupt gets
- * miss_count = -1, an untouched table, out = 0 and lse = -inf.
+ * end of the call.  A row refused as in sparse_kv_cache_update (a corrupt
+ * slot table) gets miss_count = -1, padded lists, an untouched table,
+ * out = 0 and lse = -inf.
  * num_splits = 0 resolves to sparse_kv_select_attend_splits (fewer, larger
  * parts than the attention call's default: the fused call prefers one
  * resident workgroup per CU); results equal the separate calls' bit for bit

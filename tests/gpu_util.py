@@ -64,3 +64,24 @@ def topk_swaps_ok(sel_gpu, cnt_gpu, sel_ora, cnt_ora, ora_scores, tol=1e-5, forc
             if abs(sc[r, blk] - kth) > tol:
                 bad.append((r, blk, float(sc[r, blk]), float(kth)))
     return bad
+
+
+def assert_lru_state(slot_block, slot_stamp, lru, msg=""):
+    """The device slot table equals the oracle list's, and ordering each row's
+    occupied slots by the device's (stamp, block id) gives the list's order
+    (least recent first)."""
+    rows, cap = lru.rows, lru.cap
+    sb = np.asarray(slot_block).reshape(rows, cap)
+    st = np.ascontiguousarray(slot_stamp).reshape(rows, cap).view(np.uint32)
+    np.testing.assert_array_equal(sb, lru.slot_block(), err_msg=f"slot table {msg}")
+    order = lru.order()
+    for r in range(rows):
+        occ = sorted((s for s in range(cap) if sb[r, s] >= 0), key=lambda s: (int(st[r, s]), int(sb[r, s])))
+        assert occ == order[r][order[r] >= 0].tolist(), f"LRU order of row {r} {msg}"
+
+
+def assert_lists(got: dict, out: dict, rows: int, k: int, msg=""):
+    """Step lists (device arrays by name) equal the oracle's bit for bit."""
+    for f in ("miss_count", "sel_slot", "sel_hit", "miss_block", "miss_slot"):
+        shape = (rows,) if f == "miss_count" else (rows, k)
+        np.testing.assert_array_equal(np.asarray(got[f]).reshape(shape), out[f], err_msg=f"{f} {msg}")

@@ -11,8 +11,9 @@ import torch
 
 import oracle
 from top_sparse_kv_block_amd import binding as B
+from top_sparse_kv_block_amd import synth
 from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
-from gpu_util import dev, host, log, to_dtype
+from gpu_util import assert_lists, assert_lru_state, dev, host, log, to_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -109,44 +110,123 @@ def test_transfer_count_equals_selection_delta_when_capacity_equals_budget():
             assert mc[i] == len(set(chains[i][t]) - prev)
 
 
-def test_invalid_rows_are_flagged_and_left_untouched():
-    Bsz, Hkv, cap, k, nb = 1, 4, 8, 4, 64
-    cfg = StepConfig(Bsz, Hkv, Hkv, 64, nb * 16, "f32", k, cap)
-    buf = LayerBuffers(cfg, pool=False)
-    good = np.array([[1, 5, 9, 12]] * 4, dtype=np.int32)
-    buf.sel_blocks.copy_(dev(good).view(1, 4, k))
-    buf.sel_count.fill_(4)
-    log("cache_update warm-up")
-    buf.cache_update(None, None)
-    torch.cuda.synchronize()
-    before = host(buf.slot_block).copy()
-    stamps = host(buf.slot_stamp).copy()
-    bad = np.array([[1, 5, 5, 12],      # duplicate
+def _lists(buf):
+    return {f: host(getattr(buf, f)) for f in ("miss_count", "sel_slot", "sel_hit", "miss_block", "miss_slot")}
+
+
+def _start(buf, table, stamps, clock):
+    buf.slot_block.copy_(dev(np.asarray(table, np.int32)).view(buf.slot_block.shape))
+    buf.slot_stamp.copy_(dev(np.asarray(stamps, np.int32)).view(buf.slot_stamp.shape))
+    buf.clock.copy_(dev(np.asarray(clock, np.int32)).view(buf.clock.shape))
+
+
+@pytest.mark.parametrize("importance", [False, True])
+def test_invalid_rows_match_the_oracle(importance):
+    # bad selections and corrupt tables (a selected block held twice, an
+    # unselected one held twice, ids out of range) are refused: miss_count
+    # -1, padded lists, table, stamps, clock and pool untouched; the valid
+    # rows beside them step normally.  Everything against the oracle started
+    # from the same table (LRU list ordered by (stamp, block); capped step).
+    Bsz, Hkv, cap, k, nb, D = 1, 10, 8, 4, 64, 64
+    rows, T = Bsz * Hkv, nb * 16
+    r = np.random.default_rng(3 + importance)
+    cfg = StepConfig(Bsz, Hkv, Hkv, D, T, "f32", k, cap)
+    buf = LayerBuffers(cfg)
+    src_k = r.standard_normal((Bsz, Hkv, T, D)).astype(np.float32)
+    src_v = r.standard_normal((Bsz, Hkv, T, D)).astype(np.float32)
+    base = [1, 5, 9, 12, 30, -1, 40, -1]
+    table = np.array([base] * rows, np.int32)
+    table[4, 5] = 9      # unselected block 9 held twice
+    table[5, 5] = 5      # selected block 5 held twice
+    table[6, 7] = nb     # id past the end
+    table[7, 5] = -2     # id below -1
+    stamps = np.tile(np.array([3, 3, 2, 5, 1, 0, 4, 0], np.int32), (rows, 1))
+    clock = np.full(rows, 5, np.int32)
+    sel = np.array([[1, 5, 5, 12],      # duplicate selection
                     [3, 2, 7, 8],       # not ascending
-                    [0, 1, 2, 64],      # out of range (NB = 64)
-                    [2, 3, 4, 6]], dtype=np.int32)
-    cnt = np.array([4, 4, 4, 9], dtype=np.int32)  # last row: count > k
-    buf.sel_blocks.copy_(dev(bad).view(1, 4, k))
-    buf.sel_count.copy_(dev(cnt).view(1, 4))
-    log("cache_update invalid rows")
-    buf.cache_update(None, None)
+                    [0, 1, 2, nb],      # out of range
+                    [2, 3, 4, 6],       # count > k (below)
+                    [1, 5, 20, 21],     # table: unselected duplicate
+                    [1, 5, 20, 21],     # table: selected duplicate
+                    [1, 5, 20, 21],     # table: id past the end
+                    [1, 5, 20, 21],     # table: id below -1
+                    [1, 5, 20, 21],     # valid: two hits, two misses
+                    [0, 9, 40, 63]], np.int32)
+    cnt = np.array([4, 4, 4, 9, 4, 4, 4, 4, 4, 4], np.int32)
+    scores = r.standard_normal((rows, nb)).astype(np.float32)
+    pool0 = r.standard_normal((Bsz, Hkv, cap, 16, D)).astype(np.float32)
+    _start(buf, table, stamps, clock)
+    buf.pool_k.copy_(dev(pool0))
+    buf.pool_v.copy_(dev(-pool0))
+    buf.sel_blocks.copy_(dev(sel).view(Bsz, Hkv, k))
+    buf.sel_count.copy_(dev(cnt).view(Bsz, Hkv))
+    buf.scores.copy_(dev(scores).view(Bsz, Hkv, nb))
+    log("cache_update invalid rows, importance", importance)
+    buf.cache_update(dev(src_k), dev(src_v), importance=importance)
     torch.cuda.synchronize()
-    assert host(buf.miss_count).tolist() == [[-1, -1, -1, -1]]
-    np.testing.assert_array_equal(host(buf.slot_block), before)
-    np.testing.assert_array_equal(host(buf.slot_stamp), stamps)
+    pool_k, pool_v = pool0.copy(), -pool0
+    if importance:
+        ref_table = table.copy()
+        out = oracle.capped_step(ref_table, sel, cnt, scores.astype(np.float64), nb)
+        np.testing.assert_array_equal(host(buf.slot_block).reshape(rows, cap), ref_table)
+    else:
+        lru = oracle.LRU(rows, cap)
+        lru.load(table, stamps)
+        out = lru.step(sel, cnt, nb)
+        assert_lru_state(host(buf.slot_block), host(buf.slot_stamp), lru)
+    assert out["miss_count"].tolist() == [-1] * 8 + [2, 2]
+    assert_lists(_lists(buf), out, rows, k)
+    oracle.gather(out["miss_block"], out["miss_slot"], out["miss_count"], src_k, src_v, pool_k, pool_v)
+    np.testing.assert_array_equal(host(buf.pool_k), pool_k)
+    np.testing.assert_array_equal(host(buf.pool_v), pool_v)
+    # refused rows keep their stamps and clock; valid rows advance once
+    st = host(buf.slot_stamp).reshape(rows, cap)
+    np.testing.assert_array_equal(st[:8], stamps[:8])
+    assert host(buf.clock).reshape(-1).tolist() == [5] * 8 + [6, 6]
 
 
-def test_corrupt_slot_table_is_flagged():
-    Bsz, Hkv, cap, k, nb = 1, 2, 4, 2, 32
-    cfg = StepConfig(Bsz, Hkv, Hkv, 64, nb * 16, "f32", k, cap)
-    buf = LayerBuffers(cfg, pool=False)
-    buf.slot_block.copy_(dev(np.array([[[3, 3, -1, -1], [1, 99, -1, -1]]], dtype=np.int32)))
-    buf.sel_blocks.copy_(dev(np.array([[[3, 4], [1, 2]]], dtype=np.int32)))
-    buf.sel_count.fill_(2)
-    log("cache_update corrupt table")
+def test_attention_after_a_refused_update_reads_nothing():
+    # a refused row's padded lists make the separate attention (fetch on
+    # attend) skip the row: out 0, lse -inf, its pool unchanged; the oracle
+    # attends over an empty selection for it
+    w = synth.WORKLOADS["tiny"].scaled(steps=1)
+    data = synth.gen_workload(w)
+    cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity)
+    buf = LayerBuffers(cfg)
+    K, V, lens = data["K"], data["V"], data["seq_lens"]
+    rows, cap, k, nb = w.rows, w.capacity, w.k_blocks, w.nb_max
+    table = np.full((rows, cap), -1, np.int32)
+    table[0, :3] = [4, 7, 4]  # row 0: block 4 held twice (not selected below)
+    stamps = np.zeros((rows, cap), np.int32)
+    sel = np.array([np.arange(10, 10 + k)] * rows, np.int32)
+    cnt = np.full(rows, k, np.int32)
+    _start(buf, table, stamps, np.zeros(rows, np.int32))
+    buf.sel_blocks.copy_(dev(sel).view(buf.sel_blocks.shape))
+    buf.sel_count.copy_(dev(cnt).view(buf.sel_count.shape))
+    # stale lists from an earlier step must not leak into the attention
+    buf.sel_slot.copy_(dev(np.tile(np.arange(k, dtype=np.int32), (rows, 1))).view(buf.sel_slot.shape))
+    buf.sel_hit.zero_()
+    log("refused update then attention")
     buf.cache_update(None, None)
+    buf.attention(dev(data["q"][0]), dev(lens), dev(K), dev(V))
     torch.cuda.synchronize()
-    assert host(buf.miss_count).tolist() == [[-1, -1]]
+    lru = oracle.LRU(rows, cap)
+    lru.load(table, stamps)
+    out = lru.step(sel, cnt, nb)
+    assert out["miss_count"].tolist() == [-1, k]
+    assert_lists(_lists(buf), out, rows, k)
+    pool_k = np.zeros((w.batch, w.n_kv_heads, cap, 16, w.head_dim), np.float32)
+    pool_v = np.zeros_like(pool_k)
+    oracle.gather(out["miss_block"], out["miss_slot"], out["miss_count"], K, V, pool_k, pool_v)
+    np.testing.assert_array_equal(host(buf.pool_k), pool_k)
+    np.testing.assert_array_equal(host(buf.pool_v), pool_v)
+    att_cnt = np.where(out["miss_count"] < 0, 0, cnt).reshape(w.batch, w.n_kv_heads)
+    o_ref, lse_ref = oracle.attention(data["q"][0], K, V, sel.reshape(w.batch, w.n_kv_heads, k), att_cnt, lens,
+                                      1.0 / np.sqrt(w.head_dim))
+    assert np.abs(host(buf.out) - o_ref).max() <= 1e-4
+    G = w.group
+    assert not host(buf.out)[0, :G].any() and np.all(np.isneginf(host(buf.lse)[0, :G]))
+    assert np.abs(host(buf.lse)[0, G:] - lse_ref[0, G:]).max() <= 1e-4
 
 
 def test_flush_refetches_everything():

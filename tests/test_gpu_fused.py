@@ -5,10 +5,11 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from top_sparse_kv_block_amd import binding as B
 from top_sparse_kv_block_amd import synth
 from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig, decode_step
-from gpu_util import dev, host, log
+from gpu_util import assert_lists, assert_lru_state, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -61,24 +62,54 @@ def test_fused_equals_separate_calls(name, kw, steps, splits):
             np.testing.assert_array_equal(host(getattr(b, f)), host(getattr(a, f)), err_msg=f"{f} at step {t}")
 
 
-def test_fused_flags_a_corrupt_table():
-    w = synth.WORKLOADS["tiny"].scaled(steps=1)
+def test_fused_refuses_corrupt_tables():
+    # row 0's table holds an id past the end, row 1's an unselected block
+    # twice: both are refused (miss_count -1, padded lists, table, stamps and
+    # clock untouched, out 0, lse -inf).  Against the oracle: its top-k of
+    # the step's scores, its list started from the same table, its attention
+    # (an empty selection for a refused row).
+    w = synth.WORKLOADS["tiny"].scaled(batch=2, steps=1)
     data = synth.gen_workload(w)
     cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity)
     buf = LayerBuffers(cfg)
-    K, V, lens = dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
-    table = np.full((1, 2, w.capacity), -1, dtype=np.int32)
-    table[0, 0, :2] = [5, w.nb_max + 3]  # row 0 holds a block id past the end
-    buf.slot_block.copy_(dev(table))
-    log("fused corrupt table")
-    decode_step(buf, dev(data["q"][0]), dev(data["score_q"][0]), K, lens, K, V, fused=True)
+    K, V, lens = data["K"], data["V"], data["seq_lens"]
+    rows, cap, k, nb = w.rows, w.capacity, w.k_blocks, w.nb_max
+    table = np.full((rows, cap), -1, dtype=np.int32)
+    table[0, :2] = [5, nb + 3]
+    table[1, 2:5] = [nb - 1, 6, nb - 1]
+    stamps = np.tile(np.arange(cap, dtype=np.int32), (rows, 1))
+    buf.slot_block.copy_(dev(table).view(buf.slot_block.shape))
+    buf.slot_stamp.copy_(dev(stamps).view(buf.slot_stamp.shape))
+    log("fused corrupt tables")
+    decode_step(buf, dev(data["q"][0]), dev(data["score_q"][0]), dev(K), dev(lens), dev(K), dev(V), fused=True)
     torch.cuda.synchronize()
-    assert host(buf.miss_count)[0, 0] == -1 and host(buf.miss_count)[0, 1] == w.k_blocks
-    np.testing.assert_array_equal(host(buf.slot_block)[0, 0], table[0, 0])  # untouched
-    assert host(buf.clock).tolist() == [[0, 1]]
+    # the top-k decision in the kernel's precision (its fp32 scores); the
+    # selection must then avoid block nb - 1 for row 1's refusal to be about
+    # an unselected duplicate
+    o_sel, o_cnt = oracle.topk(host(buf.scores).astype(np.float64), lens, k, w.ctx)
+    np.testing.assert_array_equal(host(buf.sel_blocks), o_sel)
+    np.testing.assert_array_equal(host(buf.sel_count), o_cnt)
+    assert nb - 1 not in o_sel.reshape(rows, k)[1].tolist()
+    lru = oracle.LRU(rows, cap)
+    lru.load(table, stamps)
+    out = lru.step(o_sel.reshape(rows, k), o_cnt.reshape(rows), nb)
+    assert out["miss_count"].tolist()[:2] == [-1, -1] and (out["miss_count"][2:] == k).all()
+    assert_lists({f: host(getattr(buf, f)) for f in FIELDS[7:12]}, out, rows, k)
+    assert_lru_state(host(buf.slot_block), host(buf.slot_stamp), lru)
+    np.testing.assert_array_equal(host(buf.slot_stamp).reshape(rows, cap)[:2], stamps[:2])
+    assert host(buf.clock).reshape(-1).tolist() == [0, 0] + [1] * (rows - 2)
+    att_cnt = np.where(out["miss_count"] < 0, 0, o_cnt.reshape(-1)).reshape(o_cnt.shape)
+    o_ref, lse_ref = oracle.attention(data["q"][0], K, V, o_sel, att_cnt, lens, 1.0 / np.sqrt(w.head_dim))
+    assert np.abs(host(buf.out) - o_ref).max() <= 1e-4
     G = w.group
-    assert not host(buf.out)[0, :G].any() and np.all(np.isneginf(host(buf.lse)[0, :G]))
-    assert np.isfinite(host(buf.lse)[0, G:]).all()
+    out_rows, lse_rows = host(buf.out).reshape(rows, G, -1), host(buf.lse).reshape(rows, G)
+    assert not out_rows[:2].any() and np.all(np.isneginf(lse_rows[:2]))
+    assert np.abs(lse_rows[2:] - lse_ref.reshape(rows, G)[2:]).max() <= 1e-4
+    pool_k = np.zeros((w.batch, w.n_kv_heads, cap, 16, w.head_dim), np.float32)
+    pool_v = np.zeros_like(pool_k)
+    oracle.gather(out["miss_block"], out["miss_slot"], out["miss_count"], K, V, pool_k, pool_v)
+    np.testing.assert_array_equal(host(buf.pool_k), pool_k)
+    np.testing.assert_array_equal(host(buf.pool_v), pool_v)
 
 
 @pytest.mark.parametrize("capacity", [32, 48])

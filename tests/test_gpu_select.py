@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from top_sparse_kv_block_amd import binding as B
-from gpu_util import dev, host, log
+from gpu_util import assert_lists, assert_lru_state, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -69,22 +70,44 @@ def test_select_equals_topk_then_update(B_, Hkv, T, k, C, sink, recent, steps):
             assert 0 < m.sum() < host(b["sel_count"]).sum()
 
 
-def test_select_lists_only_and_corrupt_table():
-    shape = B.make_shape(1, 8, 2, 64, 16 * 1024, "f32")
-    P, k, C = 2, 16, 16
-    s = _state(P, k, C)
+def test_select_lists_only_and_corrupt_tables():
+    # rows whose table holds an id past the end, an unselected block twice
+    # and a selected block twice are refused (miss_count -1, padded lists,
+    # table, stamps and clock untouched); the selection itself is still
+    # written.  Against the oracle's top-k of the same scores and its list
+    # started from the same table.
+    B_, Hkv, NB, k, C = 2, 2, 1024, 16, 16
+    P, T = B_ * Hkv, 16 * NB
+    shape = B.make_shape(B_, 4 * Hkv, Hkv, 64, T, "f32")
+    scores = np.random.default_rng(0).standard_normal((P, NB)).astype(np.float32)
+    lens = np.array([T, T], np.int32)
+    o_sel, o_cnt = oracle.topk(scores.reshape(B_, Hkv, NB).astype(np.float64), lens, k, T)
+    o_sel, o_cnt = o_sel.reshape(P, k), o_cnt.reshape(P)
+    unselected = [b for b in range(NB) if b not in set(o_sel[1].tolist())][:1] * 2
     table = np.full((P, C), -1, np.int32)
-    table[0, :2] = [5, 1024 + 3]  # row 0 holds a block id past the end
+    table[0, :2] = [5, NB + 3]                # an id past the end
+    table[1, 3:5] = unselected                # an unselected block twice
+    table[2, [1, 6]] = o_sel[2, 3]            # a selected block twice
+    table[3, :3] = [o_sel[3, 0], 7, o_sel[3, 5]]  # valid
+    stamps = np.tile(np.arange(C, dtype=np.int32)[::-1].copy(), (P, 1))
+    s = _state(P, k, C)
     s["slot_block"].copy_(dev(table))
-    sc = dev(np.random.default_rng(0).standard_normal((P, 1024)).astype(np.float32))
-    B.sparse_kv_select(shape, sc, dev(np.array([16 * 1024], np.int32)), k, 0, 0, C, s["sel_blocks"], s["sel_count"],
+    s["slot_stamp"].copy_(dev(stamps))
+    log("select corrupt tables")
+    B.sparse_kv_select(shape, dev(scores), dev(lens), k, 0, 0, C, s["sel_blocks"], s["sel_count"],
                        s["slot_block"], s["slot_stamp"], s["clock"], s["sel_slot"], s["sel_hit"], s["miss_block"],
                        s["miss_slot"], s["miss_count"])
     torch.cuda.synchronize()
-    assert host(s["miss_count"]).tolist() == [-1, k]
-    np.testing.assert_array_equal(host(s["slot_block"])[0], table[0])  # untouched
-    assert host(s["clock"]).tolist() == [0, 1]
-    assert host(s["sel_count"]).tolist() == [k, k]
+    np.testing.assert_array_equal(host(s["sel_blocks"]), o_sel)
+    np.testing.assert_array_equal(host(s["sel_count"]), o_cnt)
+    lru = oracle.LRU(P, C)
+    lru.load(table, stamps)
+    out = lru.step(o_sel, o_cnt, NB)
+    assert out["miss_count"].tolist()[:3] == [-1, -1, -1] and out["miss_count"][3] == k - 2
+    assert_lists({f: host(s[f]) for f in FIELDS}, out, P, k)
+    assert_lru_state(host(s["slot_block"]), host(s["slot_stamp"]), lru)
+    np.testing.assert_array_equal(host(s["slot_stamp"])[:3], stamps[:3])
+    assert host(s["clock"]).tolist() == [0, 0, 0, 1]
 
 
 @pytest.mark.parametrize("sink,recent", [(0, 0), (16, 48)])

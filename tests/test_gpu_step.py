@@ -17,7 +17,7 @@ import oracle
 from top_sparse_kv_block_amd import binding as B
 from top_sparse_kv_block_amd import synth
 from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig, decode_step
-from gpu_util import dev, host, log, max_rel_row_err, topk_swaps_ok
+from gpu_util import assert_lru_state, dev, host, log, max_rel_row_err, topk_swaps_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -43,10 +43,32 @@ def _forced_sets(w, lens):
     return out
 
 
+def _exact_bound(sq_t, K, lens, scale, b, j, G):
+    """scale * max over the block's valid tokens and the row's query rows of
+    sum_d |q_d| |k_d|: the size of the terms an fp32 accumulation adds, for
+    the score tolerance (NumPy float32; only a tolerance, not a reference)."""
+    qa = np.abs(synth.bf16_bits_to_f32(sq_t[b, :, j * G:(j + 1) * G]) if sq_t.dtype == np.uint16
+                else sq_t[b, :, j * G:(j + 1) * G]).astype(np.float32).reshape(-1, sq_t.shape[-1])
+    L = int(lens[b])
+    nb = K.shape[2] // 16
+    out = np.full(nb, -np.inf)
+    if L == 0:
+        return out
+    kr = K[b, j, :L]
+    ka = np.abs(synth.bf16_bits_to_f32(kr) if kr.dtype == np.uint16 else kr).astype(np.float32)
+    tok = (ka @ qa.T).max(axis=1).astype(np.float64)
+    nv = -(-L // 16)
+    pad = np.full(nv * 16, -np.inf)
+    pad[:L] = tok
+    out[:nv] = scale * pad.reshape(nv, 16).max(axis=1)
+    return out
+
+
 def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_on_attend=True, fused=False,
                  select=False):
     """Run `steps` steps of workload `w`; check rows `rows` (None = all) of
-    the scores and (b, h) pairs `heads` (None = all) of the attention."""
+    the scores and the pool, and (b, h) pairs `heads` (None = all) of the
+    attention.  Top-k and the working set are checked on every row."""
     steps = steps or w.steps
     data = synth.gen_workload(w.scaled(steps=steps))
     q, sq, K, V, lens = data["q"], data["score_q"], data["K"], data["V"], data["seq_lens"]
@@ -56,17 +78,20 @@ def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_
     buf = LayerBuffers(cfg)
     dK, dV, dlens = dev(K), dev(V), dev(lens)
     scale = 1.0 / math.sqrt(w.head_dim)
-    P = w.rows
+    P, G = w.rows, w.group
     if mode == B.SKV_SCORE_QUEST:
         meta = torch.empty(w.batch, w.n_kv_heads, w.nb_max, 2, w.head_dim, dtype=cfg.torch_dtype, device="cuda")
         B.sparse_kv_quest_meta(cfg.shape, dK, dlens, meta)
         keys_or_meta = meta
         meta_ref = oracle.quest_meta(K, lens)
+        box = np.maximum(np.abs(meta_ref[..., 0, :]), np.abs(meta_ref[..., 1, :]))
+        box_meta = np.ascontiguousarray(np.stack([box, box], -2))
     else:
         keys_or_meta = dK
     lru = oracle.LRU(P, w.capacity)
     forced = _forced_sets(w, lens)
     rows = list(range(P)) if rows is None else rows
+    hs = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)] if heads is None else heads
     total_miss = 0
     for t in range(steps):
         log(w.name, "step", t, (w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx))
@@ -75,27 +100,33 @@ def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_
         torch.cuda.synchronize()
         g_scores = host(buf.scores).astype(np.float64)
         g_sel, g_cnt = host(buf.sel_blocks), host(buf.sel_count)
-        # stage 1: sampled rows against the fp64 oracle
+        # stage 1: rows against the fp64 oracle
         ora_rows = {}
         if check_scores:
+            all_rows = len(rows) == P
+            if all_rows:  # one oracle call over every row (its rows run in parallel)
+                if mode == B.SKV_SCORE_QUEST:
+                    ref_all = oracle.score_quest(sq[t], meta_ref, lens, scale, T=w.ctx)
+                else:
+                    ref_all = oracle.score_blockmax(sq[t], K, lens, scale)
             for r_ in rows:
                 b, j = divmod(r_, w.n_kv_heads)
-                G = w.group
                 qr = np.ascontiguousarray(sq[t][b:b + 1, :, j * G:(j + 1) * G])
                 if mode == B.SKV_SCORE_QUEST:
-                    mr = np.ascontiguousarray(meta_ref[b:b + 1, j:j + 1])
-                    ref = oracle.score_quest(qr, mr, lens[b:b + 1], scale, T=w.ctx)[0, 0]
-                    box = np.maximum(np.abs(mr[..., 0, :]), np.abs(mr[..., 1, :]))
+                    ref = ref_all[b, j] if all_rows else oracle.score_quest(
+                        qr, np.ascontiguousarray(meta_ref[b:b + 1, j:j + 1]), lens[b:b + 1], scale, T=w.ctx)[0, 0]
                     qa = np.abs(synth.bf16_bits_to_f32(qr) if qr.dtype == np.uint16 else qr).astype(np.float32)
-                    bound = oracle.score_quest(qa, np.stack([box, box], -2), lens[b:b + 1], scale, T=w.ctx)[0, 0]
+                    bound = oracle.score_quest(qa, np.ascontiguousarray(box_meta[b:b + 1, j:j + 1]), lens[b:b + 1],
+                                               scale, T=w.ctx)[0, 0]
                 else:
-                    kr = np.ascontiguousarray(K[b:b + 1, j:j + 1])
-                    ref = oracle.score_blockmax(qr, kr, lens[b:b + 1], scale)[0, 0]
-                    bound = oracle.score_blockmax(_abs(qr), _abs(kr), lens[b:b + 1], scale)[0, 0]
+                    ref = ref_all[b, j] if all_rows else oracle.score_blockmax(
+                        qr, np.ascontiguousarray(K[b:b + 1, j:j + 1]), lens[b:b + 1], scale)[0, 0]
+                    bound = _exact_bound(sq[t], K, lens, scale, b, j, G)
                 got = g_scores[b, j]
                 fin = np.isfinite(ref)
-                assert np.array_equal(fin, np.isfinite(got))
-                assert np.all(np.abs(got[fin] - ref[fin]) <= GAMMA * bound[fin] + 2.0 ** -23 * np.abs(ref[fin]))
+                assert np.array_equal(fin, np.isfinite(got)), f"row {r_}"
+                assert np.all(np.abs(got[fin] - ref[fin]) <= GAMMA * bound[fin] + 2.0 ** -23 * np.abs(ref[fin])), \
+                    f"scores of row {r_} step {t}"
                 ora_rows[r_] = ref
         # stage 2: exact on the GPU's scores, tolerance rule on fp64 scores
         s_sel, s_cnt = oracle.topk(g_scores, lens, w.k_blocks, w.ctx, sink=w.sink, recent=w.recent)
@@ -115,29 +146,30 @@ def run_workload(w, steps=None, rows=None, heads=None, check_scores=True, fetch_
         np.testing.assert_array_equal(host(buf.sel_hit).reshape(P, -1), out["sel_hit"])
         np.testing.assert_array_equal(host(buf.miss_block).reshape(P, -1), out["miss_block"])
         np.testing.assert_array_equal(host(buf.miss_slot).reshape(P, -1), out["miss_slot"])
-        np.testing.assert_array_equal(host(buf.slot_block).reshape(P, -1), lru.slot_block())
+        assert_lru_state(host(buf.slot_block), host(buf.slot_stamp), lru, f"step {t}")
         total_miss += int(out["miss_count"].sum())
-        # pool bytes of the sampled rows equal the source blocks they hold
-        pk, pv = host(buf.pool_k).reshape(P, w.capacity, 16, w.head_dim), host(buf.pool_v).reshape(
-            P, w.capacity, 16, w.head_dim)
+        # pool bytes equal the source blocks the slots hold
+        pk = host(buf.pool_k).reshape(P, w.capacity, 16, w.head_dim)
+        pv = host(buf.pool_v).reshape(P, w.capacity, 16, w.head_dim)
         sb = lru.slot_block()
-        for r_ in rows[:4]:
+        for r_ in rows:
             b, j = divmod(r_, w.n_kv_heads)
-            for s_, blk in enumerate(sb[r_]):
-                if blk >= 0:
-                    assert np.array_equal(pk[r_, s_], K[b, j, blk * 16:blk * 16 + 16])
-                    assert np.array_equal(pv[r_, s_], V[b, j, blk * 16:blk * 16 + 16])
+            occ = np.nonzero(sb[r_] >= 0)[0]
+            blk = sb[r_, occ]
+            src_k = K[b, j].reshape(-1, 16, w.head_dim)[blk]
+            src_v = V[b, j].reshape(-1, 16, w.head_dim)[blk]
+            assert np.array_equal(pk[r_, occ], src_k) and np.array_equal(pv[r_, occ], src_v), f"pool row {r_}"
         # stage 4: attention from the source by block id
         g_out = host(buf.out)
-        hs = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)] if heads is None else heads
-        for b in sorted({b for b, _ in hs}):
-            o_ref, _ = oracle.attention(q[t][b:b + 1], K[b:b + 1], V[b:b + 1], g_sel[b:b + 1], g_cnt[b:b + 1],
-                                        lens[b:b + 1], scale)
+        bs = sorted({b for b, _ in hs})
+        o_ref, _ = oracle.attention(np.ascontiguousarray(q[t][bs]), np.ascontiguousarray(K[bs]),
+                                    np.ascontiguousarray(V[bs]), g_sel[bs], g_cnt[bs], lens[bs], scale)
+        for i, b in enumerate(bs):
             hh = [h for bb, h in hs if bb == b]
-            err = max_rel_row_err(g_out[b, hh], o_ref[0, hh])
+            err = max_rel_row_err(g_out[b, hh], o_ref[i, hh])
             if w.dtype == "f32":
-                assert np.abs(g_out[b, hh] - o_ref[0, hh]).max() <= 1e-4
-            assert err <= 2e-2 and err <= 1e-4, err
+                assert np.abs(g_out[b, hh] - o_ref[i, hh]).max() <= 1e-4
+            assert err <= 2e-2 and err <= 1e-4, (err, b)
     return total_miss
 
 
@@ -171,45 +203,41 @@ def test_lookahead_drafts_reduced():
     run_workload(w, steps=3)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("fused", [False, True])
-def test_llama8b_full_size_sampled(fused):
-    # full throughput workload (the benchmark runs the fused call); the
-    # oracle checks sampled score rows and attention heads, and every row of
-    # top-k (on the GPU's scores) and of the working set
-    w = synth.WORKLOADS["llama8b_32k"]
-    run_workload(w, steps=3, rows=[0, 21, 63], heads=[(0, 0), (2, 13), (7, 31)], fused=fused)
+def test_llama8b_full_size_all_steps(fused):
+    # the benchmarked workload at full size (8 x 8 rows of 2048 blocks, 32
+    # steps; the benchmark runs the fused call): every score row, top-k row,
+    # working-set row, pool slot and attention head of every step
+    run_workload(synth.WORKLOADS["llama8b_32k"], fused=fused)
 
 
 def test_tiny_workload_fused():
     run_workload(synth.WORKLOADS["tiny"], fused=True)
 
 
-@pytest.mark.timeout(400)
-def test_quest_full_size_sampled():
+@pytest.mark.timeout(900)
+def test_quest_full_size_all_steps():
     # Quest-scored 128K-context workload at full size (4 x 8 rows, 8192
     # blocks per row, 512-token budget with 4 sink and 128 recent tokens
-    # forced): sampled score rows and attention heads, every row of top-k and
-    # of the working set
-    w = synth.WORKLOADS["quest_128k"]
-    run_workload(w, steps=2, rows=[0, 31], heads=[(0, 0), (3, 31)], fused=True)
+    # forced), fused call, all 16 steps: every row and head
+    run_workload(synth.WORKLOADS["quest_128k"], fused=True)
 
 
-@pytest.mark.timeout(400)
-def test_lookahead_1m_full_size_sampled():
-    # 1M-context workload with 4 lookahead drafts (8 rows of 65536 blocks, 32
-    # scoring query rows per kv head, matrix-core scoring, long-row top-k):
-    # one sampled score row, two attention heads, every row of top-k and of
-    # the working set
-    w = synth.WORKLOADS["lookahead_1m"]
-    run_workload(w, steps=2, rows=[5], heads=[(0, 0), (0, 47)])
-
-
-@pytest.mark.timeout(400)
+@pytest.mark.timeout(900)
 def test_lookahead_1m_full_size_one_launch_select():
-    # the benchmark's path for rows over 8192 blocks: score, the one-launch
-    # selection (top-k + working-set update), attention with fetch on attend
-    w = synth.WORKLOADS["lookahead_1m"]
-    run_workload(w, steps=2, rows=[2], heads=[(0, 5), (0, 63)], select=True)
+    # the benchmark's path for rows over 8192 blocks at full size (8 rows of
+    # 65536 blocks, 32 scoring query rows per kv head, matrix-core scoring):
+    # score, the one-launch selection (top-k + working-set update), attention
+    # with fetch on attend; all 8 steps, every row and head
+    run_workload(synth.WORKLOADS["lookahead_1m"], select=True)
+
+
+@pytest.mark.timeout(900)
+def test_lookahead_1m_full_size_four_calls():
+    # the same workload through the four separate calls (long-row top-k),
+    # two steps, every row and head
+    run_workload(synth.WORKLOADS["lookahead_1m"], steps=2)
 
 
 @pytest.mark.parametrize("fetch_on_attend", [True, False])

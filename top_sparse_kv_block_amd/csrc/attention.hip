@@ -633,7 +633,7 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     const int len = min(max(seq_lens[b], 0), T);
     SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
     load_slots<kAttnThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
-    select_plan_clear<kAttnThreads>(cs, ps, k);  // published by the emit's barriers
+    select_plan_clear<kAttnThreads>(cs, ps, k, C);  // published by the emit's barriers
     AttnRow a;
     init_row<E, D>(a, q, pool_k, pool_v, src_k, src_v, row, b, j, Hq, Hq / Hkv, C, T, split, splits, scale_log2,
                    part, out, lse);
@@ -666,8 +666,9 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
         if (threadIdx.x == 0)
             sel_count[row] = nn;
         if (bad) {
-            if (threadIdx.x == 0)
-                miss_count[row] = -1;
+            write_invalid_lists<kAttnThreads>(k, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
+                                              miss_block + (size_t)row * k, miss_slot + (size_t)row * k,
+                                              miss_count + row);
         } else {
             write_lists<kAttnThreads>(sS, nn, nm, k, cs, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
                                       miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);

@@ -27,7 +27,9 @@
 // 64 rows x 128 slots against 12.5 us with 256 threads).
 //   hits:    every occupied slot binary-searches its block in S (S is
 //            ascending); a hit claims S[i] with an LDS compare-and-swap, so
-//            a block resident twice is detected.
+//            a selected block resident twice is detected, and the other
+//            occupied slots pass an LDS set of block ids, which detects an
+//            unselected one.
 //   misses:  S indices without a slot, compacted in ascending order with a
 //            workgroup prefix count.
 //   victims: candidate slots (empty, or occupied and not hit) ranked by the
@@ -65,11 +67,13 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     load_slots<kCacheThreads>(regs, C, sb, ss);
     for (int i = tid; i < k; i += kCacheThreads)
         sS[i] = S[i];
-    cache_plan_clear<kCacheThreads>(cs, k);  // published by the barrier below
+    cache_plan_clear<kCacheThreads>(cs, k, C);  // published by the barrier below
+    int32_t *o_slot = sel_slot + (size_t)row * k, *o_mb = miss_block + (size_t)row * k;
+    int32_t *o_ms = miss_slot + (size_t)row * k;
+    uint8_t *o_hit = sel_hit + (size_t)row * k;
     const bool bad_count = n < 0 || n > k || n > C;  // uniform over the workgroup
     if (bad_count) {
-        if (tid == 0)
-            miss_count[row] = -1;
+        write_invalid_lists<kCacheThreads>(k, o_slot, o_hit, o_mb, o_ms, miss_count + row);
         return;
     }
     __syncthreads();
@@ -77,16 +81,14 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
     const int nm = cache_plan_row<kCacheThreads>(sS, n, C, NB, regs, cs, bad,
                                                  scores ? scores + (size_t)row * NB : nullptr);
     if (bad) {
-        if (tid == 0)
-            miss_count[row] = -1;
+        write_invalid_lists<kCacheThreads>(k, o_slot, o_hit, o_mb, o_ms, miss_count + row);
         return;
     }
     if (tid == 0)
         sClock = atomicAdd(&clock[row], 1u) + 1u;
     __syncthreads();
     const uint32_t now = sClock;
-    write_lists<kCacheThreads>(sS, n, nm, k, cs, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
-                               miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);
+    write_lists<kCacheThreads>(sS, n, nm, k, cs, o_slot, o_hit, o_mb, o_ms, miss_count + row);
     for (int i = tid; i < n; i += kCacheThreads) {
         const int s = cs.slot_of[i];
         if (s >= 0 && s < C) {
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
 template <int THREADS, int KPT> struct SelectTopk {
     TopkScratch sc;
     PlanScratch<THREADS> ps;
-    __device__ void clear(CacheScratch &cs, int k) { select_plan_clear<THREADS>(cs, ps, k); }
+    __device__ void clear(CacheScratch &cs, int k, int C) { select_plan_clear<THREADS>(cs, ps, k, C); }
     __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
                        const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
         const uint64_t take = topk_take<THREADS, KPT>(srow, len, NB, k, sink, recent, sc);
@@ -116,7 +118,7 @@ template <int THREADS, int KPT> struct SelectTopk {
 };
 template <int THREADS> struct SelectTopk<THREADS, 0> {
     TopkLongScratch ls;
-    __device__ void clear(CacheScratch &cs, int k) { cache_plan_clear<THREADS>(cs, k); }
+    __device__ void clear(CacheScratch &cs, int k, int C) { cache_plan_clear<THREADS>(cs, k, C); }
     __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
                        const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
         n = topk_long_row<THREADS>(srow, len, NB, k, sink, recent, out, ls);
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
     uint32_t *ss = slot_stamp + (size_t)row * C;
     SlotRegs<THREADS> regs;  // in flight while the top-k runs
     load_slots<THREADS>(regs, C, sb, ss);
-    tk.clear(cs, k);  // published by the top-k's barriers
+    tk.clear(cs, k, C);  // published by the top-k's barriers
     int n, bad;
     const int nm = tk.run(scores + (size_t)row * NB, len, NB, k, sink, recent, C, regs, sS, cs, n, bad);
     for (int i = tid; i < k; i += THREADS)
@@ -150,8 +152,8 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
     if (tid == 0)
         sel_count[row] = n;
     if (bad) {
-        if (tid == 0)
-            miss_count[row] = -1;
+        write_invalid_lists<THREADS>(k, sel_slot + (size_t)row * k, sel_hit + (size_t)row * k,
+                                     miss_block + (size_t)row * k, miss_slot + (size_t)row * k, miss_count + row);
         return;
     }
     if (tid == 0)

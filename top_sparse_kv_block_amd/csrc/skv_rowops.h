@@ -549,11 +549,39 @@ __device__ int topk_long_row(const float *__restrict__ srow, int len, int NB, in
 }
 
 // ------------------------------------------------------------ working set
+// The slot table maps each resident block to one slot, so a table that holds
+// one block in two slots is corrupt whether or not the step selects that
+// block.  A selected block held twice is caught by the claims on its
+// selection entry; the others go through a set of block ids in LDS (open
+// addressing, linear probing) sized to a power of two of at least 2C
+// entries: at most half full, so every probe sequence meets an empty entry.
+constexpr int kDupSet = 2 * kMaxCapacity;
+
+__device__ __forceinline__ int dup_set_bits(int C) {  // C >= 1
+    return max(6, 32 - __builtin_clz((unsigned)(2 * C - 1)));
+}
+
+// Adds blk (>= 0) to the set; true if it was there already.
+__device__ __forceinline__ bool dup_set_add(int32_t *set, int bits, int32_t blk) {
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t p = ((uint32_t)blk * 0x9E3779B1u) >> (32 - bits);
+    for (uint32_t n = 0; n <= mask; ++n) {
+        const int32_t old = atomicCAS(&set[p], -1, blk);
+        if (old == -1)
+            return false;
+        if (old == blk)
+            return true;
+        p = (p + 1u) & mask;
+    }
+    return true;  // not reached (the set is at most half full)
+}
+
 struct CacheScratch {
     int32_t slot_of[kMaxK];  // slot of S[i]
     uint8_t hit[kMaxK];
     int32_t miss_i[kMaxK];   // S index of miss m
     uint64_t key[kMaxCapacity];  // LRU key of a candidate slot, ~0 otherwise
+    int32_t dup[kDupSet];    // block ids of the unselected occupied slots
     int wsum[16];
 };
 
@@ -598,13 +626,17 @@ __device__ __forceinline__ void load_slots(SlotRegs<THREADS> &r, int C, const in
     }
 }
 
-// Clears the plan's slot column for a selection of up to k entries.  Call
-// it before a barrier that precedes cache_plan_row (a top-k, or the barrier
-// after the selection is staged): the plan relies on the cleared entries
-// being visible to every thread and has no barrier of its own for it.
-template <int THREADS> __device__ __forceinline__ void cache_plan_clear(CacheScratch &cs, int k) {
+// Clears the plan's slot column for a selection of up to k entries and the
+// duplicate set of a C-slot table.  Call it before a barrier that precedes
+// cache_plan_row (a top-k, or the barrier after the selection is staged):
+// the plan relies on the cleared entries being visible to every thread and
+// has no barrier of its own for it.
+template <int THREADS> __device__ __forceinline__ void cache_plan_clear(CacheScratch &cs, int k, int C) {
     for (int i = threadIdx.x; i < k; i += THREADS)
         cs.slot_of[i] = -1;
+    const int nd = 1 << dup_set_bits(C);
+    for (int i = threadIdx.x; i < nd; i += THREADS)
+        cs.dup[i] = -1;
 }
 
 // Plans one step of the row's working set for the selection S[0, nn) (in
@@ -623,8 +655,10 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
     // validation and hits in one round: the selection must be ascending and
     // in range and the table's ids in [-1, NB); each occupied slot looks its
     // block up in the selection (a binary search that ends whatever S holds)
-    // and claims the entry, so a block held by two slots is caught too.  If
-    // anything is wrong the claims are discarded with the whole plan.
+    // and claims the entry, so a selected block held by two slots is caught,
+    // and an unselected one goes into the duplicate set, which catches the
+    // rest.  If anything is wrong the claims are discarded with the plan.
+    const int dbits = dup_set_bits(C);
     int bad = 0;
     for (int i = tid; i < nn; i += THREADS) {
         const int32_t v = S[i];
@@ -644,6 +678,8 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
                 bad = 1;
             const int i = blk >= 0 ? find_sorted(S, nn, blk) : -1;
             if (i >= 0 && atomicCAS(&cs.slot_of[i], -1, s) != -1)
+                bad = 1;
+            if (i < 0 && blk >= 0 && dup_set_add(cs.dup, dbits, blk))
                 bad = 1;
             const uint32_t order = importance && blk >= 0 && blk < NB ? order_key(importance[blk]) : r.stamp[u];
             cs.key[s] = i >= 0 ? ~0ull
@@ -735,8 +771,8 @@ template <int THREADS> struct PlanScratch {
 // Clears what select_plan_row expects cleared (call before a barrier that
 // precedes it, e.g. before the top-k).
 template <int THREADS>
-__device__ __forceinline__ void select_plan_clear(CacheScratch &cs, PlanScratch<THREADS> &ps, int k) {
-    cache_plan_clear<THREADS>(cs, k);
+__device__ __forceinline__ void select_plan_clear(CacheScratch &cs, PlanScratch<THREADS> &ps, int k, int C) {
+    cache_plan_clear<THREADS>(cs, k, C);
     if (threadIdx.x == 0) {
         ps.bad = 0;
         ps.n_cand = 0;
@@ -746,7 +782,7 @@ __device__ __forceinline__ void select_plan_clear(CacheScratch &cs, PlanScratch<
 // take: topk_take's bits (KPT <= 32, NB <= THREADS * KPT).  Writes the
 // selection to S[0, k) (ascending, -1 padded) and returns its size in nn;
 // returns the number of misses, or -1 with bad_out set if the slot table is
-// invalid (a block id out of range, or a selected block in two slots).
+// invalid (a block id out of range, or a block in two slots).
 // after_claims(nn) runs once the selection is in S and the hits have their
 // slots in cs.slot_of (misses still -1); the barriers after it order LDS
 // only, so global loads it issues stay in flight through the rest.
@@ -762,9 +798,11 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
         ps.take[tid] = (uint32_t)t;
     });
     // claims: an occupied slot whose block is selected takes the block's
-    // selection index (a block held by two slots is caught by the second
-    // claim); every other slot joins the candidate list with its eviction
-    // key (as in cache_plan_row: empty slots by index, then (stamp, block))
+    // selection index (a selected block held by two slots is caught by the
+    // second claim); every other slot joins the candidate list with its
+    // eviction key (as in cache_plan_row: empty slots by index, then
+    // (stamp, block)), an occupied one after passing the duplicate set
+    const int dbits = dup_set_bits(C);
     int bad = 0;
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
@@ -785,6 +823,8 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
                 if (atomicCAS(&cs.slot_of[i], -1, s) != -1)
                     bad = 1;
             } else {
+                if (blk >= 0 && dup_set_add(cs.dup, dbits, blk))
+                    bad = 1;
                 const int c = atomicAdd(&ps.n_cand, 1);
                 cs.key[c] = blk < 0 ? (uint64_t)s : ((1ull << 63) | ((uint64_t)r.stamp[u] << 31) | (uint64_t)blk);
                 ps.cand_slot[c] = s;
@@ -858,6 +898,22 @@ __device__ int select_plan_row(uint64_t take, int k, int C, int NB, const SlotRe
     });
     bad_out = 0;
     return nm;
+}
+
+// The lists of a row refused as invalid: every entry padded (sel_slot -1,
+// sel_hit 0, miss_block / miss_slot -1) and miss_count -1, so a later
+// attention over them reads nothing.
+template <int THREADS>
+__device__ __forceinline__ void write_invalid_lists(int k, int32_t *o_slot, uint8_t *o_hit, int32_t *o_mb,
+                                                    int32_t *o_ms, int32_t *o_count) {
+    for (int i = threadIdx.x; i < k; i += THREADS) {
+        o_slot[i] = -1;
+        o_hit[i] = 0;
+        o_mb[i] = -1;
+        o_ms[i] = -1;
+    }
+    if (threadIdx.x == 0)
+        *o_count = -1;
 }
 
 // Writes the step's lists (sel_slot, sel_hit, miss_block, miss_slot for all
