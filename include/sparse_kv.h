@@ -56,7 +56,8 @@
  *    status before launching anything.  A launch failure returns
  *    SKV_ERR_HIP.  Faults inside kernels surface at the caller's next
  *    synchronisation.  No call throws.
- *  - Calls are thread-safe: they touch no global state.
+ *  - Calls are thread-safe: they touch no global state (except
+ *    sparse_kv_select_attend_noalloc, see there).
  */
 #ifndef SPARSE_KV_H
 #define SPARSE_KV_H
@@ -76,8 +77,13 @@ typedef enum skv_status {
     SKV_ERR_CAPACITY = 4,    /* capacity < k_blocks, or forced blocks exceed k_blocks */
     SKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
     SKV_ERR_UNSUPPORTED = 6, /* a valid request this library does not implement */
-    SKV_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+    SKV_ERR_HIP = 7,         /* the HIP runtime reported an error at launch */
+    SKV_ERR_SCRATCH = 8      /* sparse_kv_select_attend_noalloc: the call needs more
+                                than SKV_NOALLOC_SCRATCH_BYTES of scratch */
 } skv_status;
+
+/* Size of the static device scratch of sparse_kv_select_attend_noalloc. */
+#define SKV_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 typedef enum skv_dtype { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
 
@@ -340,6 +346,32 @@ skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, 
                                    void *pool_k, void *pool_v, const void *src_k, const void *src_v,
                                    int32_t src_kind, float scale, int32_t num_splits, float *out, float *lse,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sparse_kv_select_attend without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (minus workspace / workspace_bytes), same kernels and the
+ * same results bit for bit as sparse_kv_select_attend with the same
+ * num_splits.  The per-split partials go to a static device array of
+ * SKV_NOALLOC_SCRATCH_BYTES (8 MiB) that each GPU the library runs on holds
+ * until the process ends; its address is looked up once per device on the
+ * first call with that device current.  A call whose partials
+ * (B*Hkv * splits * G * (D + 2) * 4 bytes) exceed it returns
+ * SKV_ERR_SCRATCH before launching anything.  Nothing in the scratch needs
+ * clearing (every workgroup writes its whole partial before the merge reads
+ * it).  All calls on one GPU share that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other host threads) race; enqueue them on
+ * one stream.
+ */
+skv_status sparse_kv_select_attend_noalloc(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                                           int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens,
+                                           int32_t capacity, int32_t *sel_blocks, int32_t *sel_count,
+                                           int32_t *slot_block, uint32_t *slot_stamp, uint32_t *clock,
+                                           int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                                           int32_t *miss_slot, int32_t *miss_count, const void *q, void *pool_k,
+                                           void *pool_v, const void *src_k, const void *src_v, int32_t src_kind,
+                                           float scale, int32_t num_splits, float *out, float *lse, void *stream);
 
 /* Number of splits num_splits = 0 resolves to (attention / fused call). */
 int32_t sparse_decode_attention_splits(const skv_shape *shape, int32_t k_blocks);

@@ -24,14 +24,16 @@ SKV_SRC_DEVICE, SKV_SRC_HOST_MAPPED = 0, 1
 
 STATUS = {
     0: "SKV_OK", 1: "SKV_ERR_NULL", 2: "SKV_ERR_SHAPE", 3: "SKV_ERR_DTYPE", 4: "SKV_ERR_CAPACITY",
-    5: "SKV_ERR_WORKSPACE", 6: "SKV_ERR_UNSUPPORTED", 7: "SKV_ERR_HIP",
+    5: "SKV_ERR_WORKSPACE", 6: "SKV_ERR_UNSUPPORTED", 7: "SKV_ERR_HIP", 8: "SKV_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 8 << 20  # SKV_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = (
     "sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
     "sparse_decode_attention_splits", "sparse_decode_attention_workspace_bytes", "sparse_kv_quest_meta",
     "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
     "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
+    "sparse_kv_select_attend_noalloc",
 )
 
 
@@ -74,6 +76,8 @@ def load():
                                           _p, _sz, _p]
     L.sparse_kv_select_attend.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                           _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _p, _sz, _p]
+    L.sparse_kv_select_attend_noalloc.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                                  _p, _p, _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _p]
     L.sparse_kv_select_attend_splits.argtypes = [S, _i32]
     L.sparse_kv_select_attend_splits.restype = _i32
     L.sparse_decode_attention_splits.argtypes = [S, _i32]
@@ -87,7 +91,8 @@ def load():
     L.sparse_kv_status_string.restype = C.c_char_p
     for fn in ("sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
                "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_select_attend",
-               "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select"):
+               "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
+               "sparse_kv_select_attend_noalloc"):
         getattr(L, fn).restype = C.c_int
     _lib = L
     return L
@@ -321,6 +326,32 @@ def sparse_kv_select_attend(shape, scores, seq_lens, k_blocks, sink_tokens, rece
         _ptr(out, torch.float32, "out", numel=b * hq * d), _ptr(lse, torch.float32, "lse", allow_none=True, numel=b * hq),
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("sparse_kv_select_attend", rc)
+
+
+def sparse_kv_select_attend_noalloc(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity,
+                                    sel_blocks, sel_count, slot_block, slot_stamp, clock, sel_slot, sel_hit,
+                                    miss_block, miss_slot, miss_count, q, pool_k, pool_v, src_k, src_v, src_kind,
+                                    scale, num_splits, out, lse, stream=None):
+    """sparse_kv_select_attend with the partials in the library's static
+    device scratch: no workspace argument and no allocation."""
+    dt = _torch_dtype(shape.dtype)
+    b, hq, d, t = shape.batch, shape.n_q_heads, shape.head_dim, shape.max_ctx
+    P = b * shape.n_kv_heads
+    pk, pc = P * k_blocks, P * capacity
+    rc = load().sparse_kv_select_attend_noalloc(
+        C.byref(shape), _ptr(scores, torch.float32, "scores", numel=P * (t // 16)),
+        _ptr(seq_lens, torch.int32, "seq_lens", numel=b), int(k_blocks), int(sink_tokens), int(recent_tokens),
+        int(capacity), _ptr(sel_blocks, torch.int32, "sel_blocks", numel=pk),
+        _ptr(sel_count, torch.int32, "sel_count", numel=P), _ptr(slot_block, torch.int32, "slot_block", numel=pc),
+        _ptr(slot_stamp, torch.int32, "slot_stamp", numel=pc), _ptr(clock, torch.int32, "clock", numel=P),
+        _ptr(sel_slot, torch.int32, "sel_slot", numel=pk), _ptr(sel_hit, torch.uint8, "sel_hit", numel=pk),
+        _ptr(miss_block, torch.int32, "miss_block", numel=pk), _ptr(miss_slot, torch.int32, "miss_slot", numel=pk),
+        _ptr(miss_count, torch.int32, "miss_count", numel=P), _ptr(q, dt, "q", numel=b * hq * d),
+        _ptr(pool_k, dt, "pool_k", numel=pc * 16 * d), _ptr(pool_v, dt, "pool_v", numel=pc * 16 * d),
+        _ptr(src_k, dt, "src_k", numel=P * t * d), _ptr(src_v, dt, "src_v", numel=P * t * d), int(src_kind),
+        float(scale), int(num_splits), _ptr(out, torch.float32, "out", numel=b * hq * d),
+        _ptr(lse, torch.float32, "lse", allow_none=True, numel=b * hq), _stream(stream))
+    _check("sparse_kv_select_attend_noalloc", rc)
 
 
 def sparse_decode_attention_splits(shape, k_blocks) -> int:

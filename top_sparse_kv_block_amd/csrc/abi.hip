@@ -6,7 +6,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #define SKV_API extern "C" __attribute__((visibility("default")))
+
+// Scratch of sparse_kv_select_attend_noalloc: the per-split partials of the
+// fused call, in a device array that every GPU the library runs on holds
+// from module load to the end of the process.  Host code uses the address
+// hipGetSymbolAddress gives for the current device, never the array's name.
+static __device__ __align__(256) uint8_t scratch[SKV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -259,16 +267,18 @@ SKV_API skv_status sparse_decode_attention(const skv_shape *shape, const void *q
     return hip_status(skv::launch_attention(d, a, (hipStream_t)stream));
 }
 
-SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
-                                           int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens,
-                                           int32_t capacity, int32_t *sel_blocks, int32_t *sel_count,
-                                           int32_t *slot_block, uint32_t *slot_stamp, uint32_t *clock,
-                                           int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
-                                           int32_t *miss_slot, int32_t *miss_count, const void *q, void *pool_k,
-                                           void *pool_v, const void *src_k, const void *src_v, int32_t src_kind,
-                                           float scale, int32_t num_splits, float *out, float *lse, void *workspace,
-                                           size_t workspace_bytes, void *stream) {
-    Dims d;
+namespace {
+
+// Argument checks of the fused call (everything but the workspace); on
+// success d holds the dims and splits the resolved split count.
+skv_status check_select_attend(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                               int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t capacity,
+                               const int32_t *sel_blocks, const int32_t *sel_count, const int32_t *slot_block,
+                               const uint32_t *slot_stamp, const uint32_t *clock, const int32_t *sel_slot,
+                               const uint8_t *sel_hit, const int32_t *miss_block, const int32_t *miss_slot,
+                               const int32_t *miss_count, const void *q, const void *pool_k, const void *pool_v,
+                               const void *src_k, const void *src_v, int32_t src_kind, int32_t num_splits,
+                               const float *out, Dims &d, int &splits) {
     skv_status st = check_shape(shape, d);
     if (st != SKV_OK)
         return st;
@@ -291,7 +301,55 @@ SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *
     }
     if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
         return SKV_ERR_SHAPE;
-    const int splits = num_splits == 0 ? skv::fused_auto_splits(d, k_blocks) : num_splits;
+    splits = num_splits == 0 ? skv::fused_auto_splits(d, k_blocks) : num_splits;
+    return SKV_OK;
+}
+
+// The address of this process's scratch array on the current device,
+// looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_on_current_device(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
+                                           int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens,
+                                           int32_t capacity, int32_t *sel_blocks, int32_t *sel_count,
+                                           int32_t *slot_block, uint32_t *slot_stamp, uint32_t *clock,
+                                           int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
+                                           int32_t *miss_slot, int32_t *miss_count, const void *q, void *pool_k,
+                                           void *pool_v, const void *src_k, const void *src_v, int32_t src_kind,
+                                           float scale, int32_t num_splits, float *out, float *lse, void *workspace,
+                                           size_t workspace_bytes, void *stream) {
+    Dims d;
+    int splits = 0;
+    skv_status st = check_select_attend(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity,
+                                        sel_blocks, sel_count, slot_block, slot_stamp, clock, sel_slot, sel_hit,
+                                        miss_block, miss_slot, miss_count, q, pool_k, pool_v, src_k, src_v, src_kind,
+                                        num_splits, out, d, splits);
+    if (st != SKV_OK)
+        return st;
     const size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return SKV_ERR_WORKSPACE;
@@ -299,6 +357,38 @@ SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *
                      sel_count, slot_block, slot_stamp, clock,     sel_slot,      sel_hit,    miss_block,
                      miss_slot, miss_count, q,          pool_k,    pool_v,        src_k,      src_v,
                      scale,     splits,     out,        lse,       workspace};
+    return hip_status(skv::launch_select_attend(d, f, (hipStream_t)stream));
+}
+
+SKV_API skv_status sparse_kv_select_attend_noalloc(const skv_shape *shape, const float *scores,
+                                                   const int32_t *seq_lens, int32_t k_blocks, int32_t sink_tokens,
+                                                   int32_t recent_tokens, int32_t capacity, int32_t *sel_blocks,
+                                                   int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
+                                                   uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit,
+                                                   int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
+                                                   const void *q, void *pool_k, void *pool_v, const void *src_k,
+                                                   const void *src_v, int32_t src_kind, float scale,
+                                                   int32_t num_splits, float *out, float *lse, void *stream) {
+    Dims d;
+    int splits = 0;
+    skv_status st = check_select_attend(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity,
+                                        sel_blocks, sel_count, slot_block, slot_stamp, clock, sel_slot, sel_hit,
+                                        miss_block, miss_slot, miss_count, q, pool_k, pool_v, src_k, src_v, src_kind,
+                                        num_splits, out, d, splits);
+    if (st != SKV_OK)
+        return st;
+    if (skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits) > (size_t)SKV_NOALLOC_SCRATCH_BYTES)
+        return SKV_ERR_SCRATCH;
+    void *ws = nullptr;
+    hipError_t e = scratch_on_current_device(&ws);
+    if (e != hipSuccess)
+        return SKV_ERR_HIP;
+    // every split workgroup writes its whole partial before the merge reads
+    // it, so nothing in the scratch needs clearing between calls
+    skv::FusedArgs f{scores,   seq_lens,  k_blocks,  sink_tokens, recent_tokens, capacity,   sel_blocks,
+                     sel_count, slot_block, slot_stamp, clock,     sel_slot,      sel_hit,    miss_block,
+                     miss_slot, miss_count, q,          pool_k,    pool_v,        src_k,      src_v,
+                     scale,     splits,     out,        lse,       ws};
     return hip_status(skv::launch_select_attend(d, f, (hipStream_t)stream));
 }
 
@@ -357,6 +447,8 @@ SKV_API const char *sparse_kv_status_string(skv_status s) {
         return "request not supported by this library";
     case SKV_ERR_HIP:
         return "HIP runtime error at launch";
+    case SKV_ERR_SCRATCH:
+        return "the call needs more scratch than the library's static buffer holds (SKV_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
