@@ -44,8 +44,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "sparse decode steps/s + achieved HBM GB/s (32K ctx, 2048-token budget)"
-SCORE_SOURCES = ("top_sparse_kv_block_amd/csrc/score.hip", "top_sparse_kv_block_amd/csrc/skv_device.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_blockmax_llama8b_32k_traffic.json")
+KERNEL_SOURCES = {
+    "score": ("top_sparse_kv_block_amd/csrc/score.hip", "top_sparse_kv_block_amd/csrc/skv_device.h"),
+    "select_attend": ("top_sparse_kv_block_amd/csrc/attention.hip", "top_sparse_kv_block_amd/csrc/skv_rowops.h",
+                      "top_sparse_kv_block_amd/csrc/skv_device.h"),
+    "merge_commit": ("top_sparse_kv_block_amd/csrc/attention.hip", "top_sparse_kv_block_amd/csrc/skv_device.h"),
+}
+KERNEL_NAMES = {"score": "score_blockmax", "select_attend": "select_attend_kernel",
+                "merge_commit": "merge_commit_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama8b_32k_step_traffic.json")
 
 
 # ---------------------------------------------------------------- byte model
@@ -91,9 +98,30 @@ def _score_kernel_name(w) -> str:
     return "score_blockmax_mfma_kernel" if w.dtype == "bf16" else "score_blockmax_kernel"
 
 
-def _sources_sha() -> str:
+def fused_launch_bytes(w, misses: float, splits: int) -> int:
+    """Algorithmic bytes of one select-attend launch: the row's scores and
+    slot table (with stamps) read once, every selected block's K and V read
+    once (hits from the pool, misses from the source), each miss written
+    into its pool slot, q read, the split partials and the step's lists
+    written."""
+    P, e, D, G = w.rows, w.elem_bytes, w.head_dim, w.group
+    blk = 16 * D * e
+    return int(P * w.nb_max * 4 + P * w.capacity * 8 + P * w.k_blocks * blk * 2 + misses * blk * 2
+               + w.batch * w.n_q_heads * D * e + P * splits * G * (D + 2) * 4 + P * w.k_blocks * 17 + P * 8)
+
+
+def merge_launch_bytes(w, splits: int) -> int:
+    """Algorithmic bytes of one merge-commit launch: the partials read, the
+    output and lse written, the selection and its slots read, the selected
+    slots' blocks and stamps and the clock written."""
+    P, D, G = w.rows, w.head_dim, w.group
+    return int(P * splits * G * (D + 2) * 4 + w.batch * w.n_q_heads * (D + 1) * 4 + P * w.k_blocks * 16
+               + P * 12)
+
+
+def _sources_sha(kernel: str = "score") -> str:
     h = hashlib.sha256()
-    for p in SCORE_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -107,9 +135,28 @@ def _traffic(w):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != _sources_sha() or t.get("workload") != w.name:
+    k = t.get("kernels", {}).get("score", {})
+    if k.get("source_sha") != _sources_sha("score") or t.get("workload") != w.name:
         return None
-    return t.get("bytes_per_launch")
+    return k.get("bytes_per_launch")
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu shows it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def input_sha256(data) -> dict:
+    """SHA-256 of every generated input tensor (its raw bytes, C order)."""
+    return {name: hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+            for name, a in sorted(data.items()) if isinstance(a, np.ndarray)}
 
 
 # ---------------------------------------------------------------- oracle leg
@@ -145,7 +192,9 @@ def cpu_baseline(w, data, seconds: float):
     return dict(value=round(steps / el, 4), unit="steps/s", cores=threads, kind="oracle",
                 sample=f"{steps} whole steps (all {w.rows} rows, fp64) of the {w.name} workload, "
                        f"{el:.1f} s wall on {threads} OpenMP threads",
-                gbps=round(step_bytes(w, misses / steps)["total"] * steps / el / 1e9, 3))
+                gbps=round(step_bytes(w, misses / steps)["total"] * steps / el / 1e9, 3),
+                cpu_model=cpu_model(),
+                note="the oracle is a plain fp64 correctness reference, not a tuned CPU implementation")
 
 
 # ---------------------------------------------------------------- counters
@@ -154,8 +203,11 @@ COPY_MIB = 512  # calibration copy: 512 MiB read + 512 MiB written
 
 def pmc_pass(args):
     """Run under ``rocprofv3 --pmc <counter>``: one plain device copy of
-    COPY_MIB MiB (the calibration kernel, known bytes), then `steps` launches
-    of the scoring kernel on the benchmark workload.  Prints one line."""
+    COPY_MIB MiB (the calibration kernel, known bytes), `steps` launches of
+    the scoring kernel on the benchmark workload, then warmup + steps fused
+    steps (scoring + select-attend + merge) from a cold working set.  The
+    miss counts of the last `steps` fused steps go to ``--pmc-out`` (JSON)
+    for the algorithmic bytes of those launches.  Prints one line."""
     import torch
 
     from top_sparse_kv_block_amd import binding as B
@@ -163,13 +215,14 @@ def pmc_pass(args):
     from top_sparse_kv_block_amd.step import LayerBuffers, StepConfig
 
     w = synth.WORKLOADS[args.workload]
-    data = synth.gen_workload(w.scaled(steps=max(args.steps, 1)))
+    n_fused = args.warmup + args.steps
+    data = synth.gen_workload(w.scaled(steps=max(n_fused, 1)))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda() \
         if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    sq, dK, dlens = dev(data["score_q"]), dev(data["K"]), dev(data["seq_lens"])
+    q, sq, dK, dV, dlens = dev(data["q"]), dev(data["score_q"]), dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
     cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
                      n_queries=w.n_score_queries)
-    buf = LayerBuffers(cfg, pool=False)
+    buf = LayerBuffers(cfg)
     n = COPY_MIB << 20
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -178,8 +231,19 @@ def pmc_pass(args):
     for t in range(args.steps):
         B.sparse_kv_score(cfg.shape, B.SKV_SCORE_BLOCKMAX, sq[t], cfg.n_queries, dK, dlens, cfg.softmax_scale,
                           buf.scores)
+    buf.reset()
+    misses = torch.zeros(n_fused, dtype=torch.int64, device="cuda")
+    for t in range(n_fused):
+        buf.score(sq[t], dK, dlens)
+        buf.select_attend(q[t], dlens, dK, dV)
+        misses[t] = buf.miss_count.sum()
     torch.cuda.synchronize()
-    print(f"pmc pass done: copy {COPY_MIB} MiB, {args.steps} scoring launches on {w.name}", flush=True)
+    if args.pmc_out:
+        with open(args.pmc_out, "w") as f:
+            json.dump({"workload": w.name, "warmup": args.warmup, "steps": args.steps,
+                       "splits": buf.fused_splits, "misses": misses[args.warmup:].tolist()}, f)
+    print(f"pmc pass done: copy {COPY_MIB} MiB, {args.steps} scoring launches, {n_fused} fused steps on {w.name}",
+          flush=True)
 
 
 def _counter_rows(path):
@@ -195,50 +259,143 @@ def _counter_rows(path):
     return rows
 
 
-def traffic_summary(fetch_dir, write_dir, workload):
-    """Counter-derived HBM traffic of the scoring kernel from two rocprofv3
-    --pmc runs of ``--pmc-pass`` (FETCH_SIZE, then WRITE_SIZE, KiB per
-    dispatch), each scaled by the factor that makes the calibration copy
-    read (write) exactly COPY_MIB MiB.  Writes the JSON the benchmark reads
-    and a short markdown summary under profiles/."""
+def _dispatch_order(r):
+    for key in ("Dispatch_Id", "Correlation_Id", "Index"):
+        if r.get(key, "").strip().isdigit():
+            return int(r[key])
+    return 0
+
+
+XCHECK_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_MISS_sum")
+
+
+def _xcheck(path, steps):
+    """Raw counters of a third --pmc run (XCHECK_COUNTERS): L2-to-memory
+    read requests, their 32-byte and 128-byte ('bubble') parts, and L2
+    misses (reads and writes), per kernel."""
+    rows = _counter_rows(path)
+    out = {}
+    for counter in XCHECK_COUNTERS:
+        rs = [r for r in rows if r.get("Counter_Name") == counter]
+        copy = [float(r["Counter_Value"]) for r in rs if "copybuffer" in r["Kernel_Name"].lower()]
+        per = {}
+        for kname, pat in KERNEL_NAMES.items():
+            ks = sorted((r for r in rs if pat in r["Kernel_Name"]), key=_dispatch_order)
+            vals = [float(r["Counter_Value"]) for r in ks][-steps:]
+            per[kname] = float(np.mean(vals)) if vals else None
+        out[counter] = dict(copy=max(copy) if copy else None, kernels=per)
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, misses_file, workload, xcheck_dir=None):
+    """Counter-derived HBM traffic of the step's kernels (the scan, the fused
+    select-attend, the merge-commit) from two rocprofv3 --pmc runs of
+    ``--pmc-pass`` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each
+    scaled by the factor that makes the calibration copy read (write)
+    exactly COPY_MIB MiB, against each launch's algorithmic bytes.  Writes
+    the JSON the benchmark reads and a short markdown summary under
+    profiles/."""
     from top_sparse_kv_block_amd import synth
 
     w = synth.WORKLOADS[workload]
-    out = {}
+    with open(misses_file) as f:
+        mf = json.load(f)
+    steps, splits, miss = mf["steps"], mf["splits"], mf["misses"]
+    algo = {"score": [score_launch_bytes(w)] * steps,
+            "select_attend": [fused_launch_bytes(w, m, splits) for m in miss],
+            "merge_commit": [merge_launch_bytes(w, splits)] * steps}
+    counters = {}
     for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
         copy = [float(r["Counter_Value"]) for r in rows if "copybuffer" in r["Kernel_Name"].lower()]
-        score = [float(r["Counter_Value"]) for r in rows if "score_blockmax" in r["Kernel_Name"]]
-        if not copy or not score:
-            raise SystemExit(f"{counter}: copy dispatches {len(copy)}, scoring dispatches {len(score)}")
+        if not copy:
+            raise SystemExit(f"{counter}: no calibration copy dispatch")
         factor = (COPY_MIB << 20) / (max(copy) * 1024.0)
-        out[counter] = dict(copy_kib=max(copy), factor=factor, score_kib_avg=float(np.mean(score)),
-                            score_bytes=float(np.mean(score)) * 1024.0 * factor, dispatches=len(score))
-    total = out["FETCH_SIZE"]["score_bytes"] + out["WRITE_SIZE"]["score_bytes"]
-    res = dict(workload=w.name, kernel=_score_kernel_name(w), source_sha=_sources_sha(),
-               bytes_per_launch=int(round(total)), algorithmic_bytes_per_launch=score_launch_bytes(w),
-               counters=out)
+        per = {}
+        for kname, pat in KERNEL_NAMES.items():
+            ks = sorted((r for r in rows if pat in r["Kernel_Name"]), key=_dispatch_order)
+            vals = [float(r["Counter_Value"]) for r in ks][-steps:]
+            if not vals:
+                raise SystemExit(f"{counter}: no {pat} dispatches")
+            per[kname] = dict(kib_avg=float(np.mean(vals)), bytes=float(np.mean(vals)) * 1024.0 * factor,
+                              dispatches=len(vals))
+        counters[counter] = dict(copy_kib=max(copy), factor=factor, kernels=per)
+    kernels = {}
+    for kname in KERNEL_NAMES:
+        fetch = counters["FETCH_SIZE"]["kernels"][kname]["bytes"]
+        write = counters["WRITE_SIZE"]["kernels"][kname]["bytes"]
+        a = float(np.mean(algo[kname]))
+        kernels[kname] = dict(kernel=KERNEL_NAMES[kname], source_sha=_sources_sha(kname),
+                              bytes_per_launch=int(round(fetch + write)), fetch_bytes=int(round(fetch)),
+                              write_bytes=int(round(write)), algorithmic_bytes_per_launch=int(round(a)),
+                              ratio=round((fetch + write) / a, 4))
+    xc = None
+    if xcheck_dir:
+        xc = _xcheck(xcheck_dir, steps)
+        # read requests against the copy's reads; L2 misses against the
+        # copy's reads and writes (a write also misses once per line)
+        for counter, copy_bytes in (("TCC_EA0_RDREQ_sum", float(COPY_MIB << 20)),
+                                    ("TCC_MISS_sum", float(2 * (COPY_MIB << 20)))):
+            c = xc[counter]
+            if not c["copy"]:
+                continue
+            unit = copy_bytes / c["copy"]  # bytes per request / per miss of the calibration copy
+            c["bytes_per_unit"] = unit
+            for kname in KERNEL_NAMES:
+                v = c["kernels"][kname]
+                kernels[kname][f"bytes_from_{counter}"] = int(round(v * unit)) if v is not None else None
+    res = dict(workload=w.name, steps=steps, splits=splits, miss_blocks_per_step=float(np.mean(miss)),
+               kernels=kernels, counters=counters, xcheck=xc)
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(res, f, indent=1)
     md = TRAFFIC_FILE.replace(".json", ".md")
     with open(md, "w") as f:
-        f.write(f"# HBM traffic of {_score_kernel_name(w)}, {w.name} workload\n\n"
-                "Two counter runs (one MI355X; `$REPO` is the repository root), then the summary:\n\n```\n"
+        f.write(f"# HBM traffic of the step's kernels, {w.name} workload\n\n"
+                "Counter runs (one MI355X; `$REPO` is the repository root), then the summary:\n\n```\n"
                 "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o f -- "
-                f"python3 $REPO/bench.py --pmc-pass --steps 4 --workload {w.name}\n"
+                f"python3 $REPO/bench.py --pmc-pass --steps {steps} --warmup {mf['warmup']} --workload {w.name} "
+                "--pmc-out $REPO/gpurun_out/pmc_misses.json\n"
                 "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o w -- "
-                f"python3 $REPO/bench.py --pmc-pass --steps 4 --workload {w.name}\n"
-                "python3 bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write\n```\n\n"
+                f"python3 $REPO/bench.py --pmc-pass --steps {steps} --warmup {mf['warmup']} --workload {w.name}\n"
+                "cd /tmp && rocprofv3 --pmc " + " ".join(XCHECK_COUNTERS) + " --output-format csv -d "
+                "$REPO/gpurun_out/pmc_xcheck -o x -- "
+                f"python3 $REPO/bench.py --pmc-pass --steps {steps} --warmup {mf['warmup']} --workload {w.name}\n"
+                "python3 bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write "
+                "gpurun_out/pmc_misses.json gpurun_out/pmc_xcheck\n```\n\n"
                 f"Calibration: a plain device copy of {COPY_MIB} MiB; each counter is scaled so that the copy "
-                f"reads (writes) exactly {COPY_MIB} MiB.\n\n"
-                "| counter | copy KiB | scale factor | scoring KiB / launch | scaled bytes / launch |\n"
-                "|---|---:|---:|---:|---:|\n")
-        for c, v in out.items():
-            f.write(f"| {c} | {v['copy_kib']:.0f} | {v['factor']:.4f} | {v['score_kib_avg']:.0f} | "
-                    f"{v['score_bytes']:.0f} |\n")
-        f.write(f"\nTraffic per launch: {total:.0f} B; algorithmic bytes per launch: {score_launch_bytes(w)} B "
-                f"(ratio {total / score_launch_bytes(w):.4f}). Kernel source sha {res['source_sha']}.\n")
+                f"reads (writes) exactly {COPY_MIB} MiB.  Scale factors: FETCH_SIZE "
+                f"{counters['FETCH_SIZE']['factor']:.4f}, WRITE_SIZE {counters['WRITE_SIZE']['factor']:.4f}.  The "
+                f"fused and merge launches are the last {steps} of {steps + mf['warmup']} steps from a cold working "
+                f"set ({np.mean(miss):.1f} missed blocks per step, {splits} splits).\n\n"
+                "| kernel | FETCH_SIZE KiB / launch | WRITE_SIZE KiB / launch | scaled bytes / launch | "
+                "algorithmic bytes / launch | ratio |\n|---|---:|---:|---:|---:|---:|\n")
+        for kname, v in kernels.items():
+            f.write(f"| {v['kernel']} | {counters['FETCH_SIZE']['kernels'][kname]['kib_avg']:.0f} | "
+                    f"{counters['WRITE_SIZE']['kernels'][kname]['kib_avg']:.0f} | {v['bytes_per_launch']} | "
+                    f"{v['algorithmic_bytes_per_launch']} | {v['ratio']:.4f} |\n")
+        if xc is not None:
+            f.write("\nCross-check with raw counters (a third run, `--pmc " + " ".join(XCHECK_COUNTERS) + "`): "
+                    "each counter per dispatch; the read bytes from the L2-to-memory read requests (unit: the "
+                    "copy's read bytes per request) beside the scaled FETCH_SIZE, and the read + write bytes from "
+                    "the L2 misses (unit: the copy's read + write bytes per miss) beside scaled FETCH_SIZE + "
+                    "WRITE_SIZE.\n\n"
+                    "| kernel | " + " | ".join(XCHECK_COUNTERS) + " | read bytes from RDREQ | FETCH_SIZE bytes "
+                    "| bytes from TCC_MISS | FETCH + WRITE bytes |\n|---|" + "---:|" * (len(XCHECK_COUNTERS) + 4)
+                    + "\n")
+            f.write("| copy (calibration) | " + " | ".join(f"{xc[c]['copy']:.0f}" for c in XCHECK_COUNTERS)
+                    + f" | {COPY_MIB << 20} | {COPY_MIB << 20} | {2 * (COPY_MIB << 20)} | {2 * (COPY_MIB << 20)} |\n")
+            for kname, v in kernels.items():
+                f.write(f"| {v['kernel']} | " + " | ".join(f"{xc[c]['kernels'][kname]:.0f}" for c in XCHECK_COUNTERS)
+                        + f" | {v.get('bytes_from_TCC_EA0_RDREQ_sum')} | {v['fetch_bytes']} | "
+                        f"{v.get('bytes_from_TCC_MISS_sum')} | {v['bytes_per_launch']} |\n")
+            f.write("\nUnits implied by the copy: "
+                    + ", ".join(f"{c} {xc[c].get('bytes_per_unit', 0):.1f} B" for c in ("TCC_EA0_RDREQ_sum",
+                                                                                        "TCC_MISS_sum"))
+                    + ".  Every L2-to-memory read is a 128-byte request and TCC_BUBBLE_sum stays 0, while the "
+                      "FETCH_SIZE expression counts a request that is neither a bubble nor 32 bytes as 64 bytes: "
+                      "that is the factor 2 of its scale.\n")
+        f.write("\nKernel source sha: " + ", ".join(f"{k} {v['source_sha']}" for k, v in kernels.items()) + ".\n")
     return res
 
 
@@ -325,27 +482,35 @@ def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
                         wall_us_per_layer=wall * 1e3 / ((steps - 1) * layers), m_total=m[0], upd_ms=upd)
 
         def run_fetch_on_attend():
+            # list-only updates (the no-IO control: NULL sources) followed by
+            # attention that fetches the misses over PCIe itself
             for b in bufs:
                 b.reset()
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers * steps)]
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers * steps)]
             misses = torch.zeros(steps, layers, dtype=torch.int64, device="cuda")
             for s in range(steps):
                 for l, b in enumerate(bufs):
                     b.sel_blocks.copy_(sels[s, l])
                     e = ev[s * layers + l]
+                    e[2].record()
                     b.cache_update(None, None)
+                    e[3].record()
                     e[0].record()
                     b.attention(q, lens, hk.device_ptr, hv.device_ptr, B.SKV_SRC_HOST_MAPPED)
                     e[1].record()
                     misses[s, l] = b.miss_count.sum()
             torch.cuda.synchronize()
             us = sum(e[0].elapsed_time(e[1]) for e in ev[layers:]) * 1e3
+            # per layer, the same layers as gather_us_per_layer (steps after the cold one, layers after the first)
+            no_io = [ev[s * layers + l][2].elapsed_time(ev[s * layers + l][3]) * 1e3
+                     for s in range(1, steps) for l in range(1, layers)]
             m = int(misses[1:].sum().item())
-            return m, us
+            m_crit = int(misses[1:, 1:].sum().item())
+            return m, us, float(np.mean(no_io)), m_crit
 
         plain = run_sweep(False)
         cross = run_sweep(True)
-        m_f, us_f = run_fetch_on_attend()
+        m_f, us_f, no_io_us, m_crit = run_fetch_on_attend()
         # plain pinned copy, 256 MiB, for scale
         n_c = 128 << 20
         src = torch.from_numpy(hk.numpy(np.int16, (n_c,)))
@@ -369,6 +534,8 @@ def host_fetch_leg(layers: int = 4, steps: int = 3, seed: int = 4):
             "miss_blocks_per_layer": round(plain["crit"], 1),
             "gather_h2d_gbps": round(plain["m_total"] * blk2 / (plain["upd_ms"] * 1e-3) / 1e9, 2),
             "gather_us_per_layer": round(plain["update_us"], 1),
+            "no_io_update_us_per_layer": round(no_io_us, 1),
+            "no_io_same_misses": bool(m_crit == plain["m_total"]),
             "cross_layer_prefetch": {
                 "critical_miss_blocks_per_layer": round(cross["crit"], 1),
                 "prefetched_blocks_per_layer": round(cross["pf"], 1),
@@ -552,10 +719,37 @@ def run(args):
         pipe.join()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, synchronised on both sides.  By
+    # the state after the warm-up, restored before every repetition (and
+    # before the per-call passes below) so each one runs the same steps from
+    # the same working sets: slot tables, stamps, clocks, pools, lengths
+    # (they grow with --grow, as do the Quest boxes), the lag-1 list sets
+    def state_tensors():
+        ts = [buf.slot_block, buf.slot_stamp, buf.clock, buf.pool_k, buf.pool_v, dlens]
+        if pipe is not None:
+            for lst in pipe.lists:
+                ts += [lst.sel_blocks, lst.sel_count, lst.sel_slot, lst.sel_hit, lst.miss_block, lst.miss_slot,
+                       lst.miss_count]
+        if args.grow and mode == B.SKV_SCORE_QUEST:
+            ts.append(keys_or_meta)
+        return ts
+
+    saved = [t.clone() for t in state_tensors()]
+    pipe_t = pipe.t if pipe is not None else 0
+    appended_t = appended[0]
+
+    def restore():
+        for t, v in zip(state_tensors(), saved):
+            t.copy_(v)
+        appended[0] = appended_t
+        if pipe is not None:
+            pipe.t, pipe._upd_prev = pipe_t, None
+        torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides, run
+    # `reps` times from the restored state; the median is reported.  By
     # default the steps are captured once into a HIP graph and the graph is
     # replayed (the host then only submits one launch); --eager enqueues the
-    # four calls per step from Python instead.
+    # calls per step from Python instead.
     graph = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
@@ -566,22 +760,25 @@ def run(args):
                 pipe.join()
         torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(args.steps):
-            step(args.warmup + i)
-        if pipe is not None:
-            pipe.join()
-    t_enq = time.perf_counter() - t0
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    elapsed = max(wall, gpu_ms / 1e3)
+    rep_s, enq_s = [], []
+    for _ in range(max(args.reps, 1)):
+        restore()
+        t0 = time.perf_counter()
+        e0.record()
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(args.steps):
+                step(args.warmup + i)
+            if pipe is not None:
+                pipe.join()
+        enq_s.append(time.perf_counter() - t0)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        rep_s.append(max(wall, e0.elapsed_time(e1) / 1e3))
+    elapsed = float(np.median(rep_s))
+    t_enq = float(np.median(enq_s))
     misses = miss_log[args.warmup:].sum().item()
 
     # profiling passes right after the timed region, on the same stream:
@@ -609,10 +806,78 @@ def run(args):
     torch.cuda.synchronize()
     score_avg_s = s0.elapsed_time(s1) / 1e3 / args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    restore()
     for i in range(args.steps):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     stage = np.array([[ev[c].elapsed_time(ev[c + 1]) for c in range(4)] for ev in evs]) * 1e3  # us
+
+    # achievable-read anchor: the scan's bytes read by a kernel with the
+    # scan's launch shape and load form and no arithmetic, timed like it
+    read_gbps = None
+    if mode == B.SKV_SCORE_BLOCKMAX:
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def read_pass():
+            for _ in range(args.steps):
+                B.sparse_kv_stream_read(shape, dK, sink, st)
+
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if graph is not None:
+            rgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(rgraph):
+                read_pass()
+            torch.cuda.synchronize()
+            r0.record()
+            rgraph.replay()
+        else:
+            r0.record()
+            read_pass()
+        r1.record()
+        torch.cuda.synchronize()
+        read_avg_s = r0.elapsed_time(r1) / 1e3 / args.steps
+        read_gbps = w.rows * T * w.head_dim * w.elem_bytes / read_avg_s / 1e9
+
+    # no-IO control: the same steps' working-set updates timed with NULL
+    # sources (lists only) and with the HBM source (lists, then the copy of
+    # every miss into the pool), from the same restored state, so both see
+    # the same selections and misses
+    no_io = None
+    if pipe is None and not args.grow and not select and args.eviction == "lru":
+        def update_pass(with_src):
+            restore()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                t = args.warmup + i
+                B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
+                B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
+                                 buf.sel_count, st)
+                ev[i][0].record()
+                src = (dK, dV) if with_src else (None, None)
+                B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count,
+                                         buf.slot_block, buf.slot_stamp, buf.clock, buf.sel_slot, buf.sel_hit,
+                                         buf.miss_block, buf.miss_slot, miss_log[t], *src, B.SKV_SRC_DEVICE,
+                                         buf.pool_k, buf.pool_v, st)
+                ev[i][1].record()
+                B.sparse_decode_attention(shape, q_all[t], buf.pool_k, buf.pool_v, cfg.capacity, buf.sel_blocks,
+                                          buf.sel_slot, buf.sel_hit, buf.sel_count, dlens, cfg.k_blocks, scale,
+                                          buf.splits, *((None, None) if with_src else (dK, dV)), B.SKV_SRC_DEVICE,
+                                          buf.out, buf.lse, buf.workspace, st)
+            torch.cuda.synchronize()
+            us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+            return us, miss_log[args.warmup:].sum().item() / args.steps
+
+        update_pass(False)  # untimed: the update and gather kernels' first launches (code load)
+        update_pass(True)
+        us_none, m_none = update_pass(False)
+        us_hbm, m_hbm = update_pass(True)
+        blk2 = 2 * 16 * w.head_dim * w.elem_bytes
+        no_io = {"no_io_update_us": round(us_none, 2), "update_with_hbm_gather_us": round(us_hbm, 2),
+                 "io_us": round(us_hbm - us_none, 2), "miss_blocks_per_step": round(m_hbm, 1),
+                 "same_misses": bool(m_none == m_hbm),
+                 "gather_gbps": round(m_hbm * blk2 * 2 / max(us_hbm - us_none, 1e-3) / 1e3, 1),
+                 "what": "working-set update of the same steps with NULL sources (lists only: the mechanism) "
+                         "against the HBM source (lists + copy of every miss into the pool: read + write)"}
 
     bytes_total = step_bytes(w, misses / args.steps)["total"] * args.steps
     sbytes = score_launch_bytes(w)
@@ -627,6 +892,11 @@ def run(args):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(1e3 * elapsed / args.steps, 4),
+        "reps": len(rep_s),
+        "ms_per_step_median": round(1e3 * elapsed / args.steps, 4),
+        "ms_per_step_min": round(1e3 * min(rep_s) / args.steps, 4),
+        "ms_per_step_max": round(1e3 * max(rep_s) / args.steps, 4),
+        "spread": round((max(rep_s) - min(rep_s)) / elapsed, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -661,8 +931,15 @@ def run(args):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(score_avg_s * 1e6, 2),
-                     "bytes_per_launch": sbytes},
+                     "bytes_per_launch": sbytes,
+                     "achievable_read_gbps": round(read_gbps, 1) if read_gbps else None,
+                     "frac_of_achievable": round(achieved / read_gbps, 4) if read_gbps else None,
+                     "read_anchor": "sparse_kv_stream_read: the scan's launch shape and 16-byte load form, no "
+                                    "arithmetic, over the same keys" if read_gbps else None},
+        "input_sha256": input_sha256(data),
     }
+    if no_io is not None:
+        res["no_io"] = no_io
     if not args.no_host_fetch:
         res["host_fetch"] = host_fetch_leg()
     if not args.no_cpu_baseline:
@@ -675,6 +952,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--reps", type=int, default=10,
+                    help="repetitions of the timed steps, each from the restored post-warm-up state; the median "
+                         "is reported")
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = library default)")
     ap.add_argument("--eager", action="store_true", help="enqueue every call from Python instead of a graph")
@@ -692,8 +972,10 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--pmc-pass", action="store_true",
                     help="calibration copy + scoring launches only, to run under rocprofv3 --pmc")
-    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc outputs of --pmc-pass into the traffic file under profiles/")
+    ap.add_argument("--pmc-out", default=None, help="with --pmc-pass: JSON file for the fused steps' miss counts")
+    ap.add_argument("--traffic-summary", nargs="+", metavar="DIR",
+                    help="FETCH_DIR WRITE_DIR MISSES_JSON [XCHECK_DIR]: turn the rocprofv3 --pmc outputs of "
+                         "--pmc-pass into the traffic file under profiles/")
     args = ap.parse_args(argv)
     if args.eviction == "importance":
         args.fused = False  # the fused call evicts LRU only
@@ -705,16 +987,16 @@ def main(argv=None):
     if args.grow:
         args.no_cpu_baseline = True  # the oracle leg replays the fixed-length workload
     if args.traffic_summary:
-        print(json.dumps(traffic_summary(*args.traffic_summary, args.workload)))
+        ts = args.traffic_summary
+        if len(ts) not in (3, 4):
+            raise SystemExit("--traffic-summary takes FETCH_DIR WRITE_DIR MISSES_JSON [XCHECK_DIR]")
+        print(json.dumps(traffic_summary(ts[0], ts[1], ts[2], args.workload, ts[3] if len(ts) == 4 else None)))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the step runs on a single MI355X and has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         return 2
-    if args.pmc_pass:
-        pmc_pass(args)
-        return 0
     if args.pmc_pass:
         pmc_pass(args)
         return 0

@@ -391,6 +391,18 @@ skv_status sparse_kv_quest_meta(const skv_shape *shape, const void *keys, const 
                                 void *meta, void *stream);
 
 /*
+ * Helper (measurement only, not part of the step): reads keys [B,Hkv,T,D]
+ * once, whole, in the launch shape and 16-byte load form of the exact block
+ * scan of sparse_kv_score, with no arithmetic beyond folding what it reads
+ * into one word.  It writes sink[0] only when that word equals one fixed
+ * value, which real data almost never produce (so the reads cannot be
+ * dropped).  Its duration gives the HBM read rate the scan's access pattern
+ * can reach: the measured anchor of the scan's roofline beside the
+ * nameplate peak.  sink: one uint32 of device memory.
+ */
+skv_status sparse_kv_stream_read(const skv_shape *shape, const void *keys, uint32_t *sink, void *stream);
+
+/*
  * Helper: pinned host memory mapped into the device address space, for a
  * host-resident K/V source.  *host_ptr is for the CPU, *device_ptr for the
  * kernels.  Free with sparse_kv_host_free(host_ptr).

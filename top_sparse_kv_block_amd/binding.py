@@ -16,7 +16,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsparse_kv.so")
+# SKV_LIBRARY may name another build of the same library (e.g. the A/B
+# variant from ``build.py --ab-valu``); by default the in-tree build.
+LIB_PATH = os.environ.get("SKV_LIBRARY") or os.path.join(_HERE, "libsparse_kv.so")
 
 SKV_F32, SKV_BF16 = 0, 1
 SKV_SCORE_BLOCKMAX, SKV_SCORE_QUEST = 0, 1
@@ -33,7 +35,7 @@ EXPORTS = (
     "sparse_decode_attention_splits", "sparse_decode_attention_workspace_bytes", "sparse_kv_quest_meta",
     "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
     "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
-    "sparse_kv_select_attend_noalloc",
+    "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read",
 )
 
 
@@ -85,6 +87,7 @@ def load():
     L.sparse_decode_attention_workspace_bytes.argtypes = [S, _i32, _i32]
     L.sparse_decode_attention_workspace_bytes.restype = _sz
     L.sparse_kv_quest_meta.argtypes = [S, _p, _p, _p, _p]
+    L.sparse_kv_stream_read.argtypes = [S, _p, _p, _p]
     L.sparse_kv_host_alloc.argtypes = [_sz, C.POINTER(_p), C.POINTER(_p)]
     L.sparse_kv_host_free.argtypes = [_p]
     L.sparse_kv_status_string.argtypes = [C.c_int]
@@ -92,7 +95,7 @@ def load():
     for fn in ("sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
                "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_select_attend",
                "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
-               "sparse_kv_select_attend_noalloc"):
+               "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read"):
         getattr(L, fn).restype = C.c_int
     _lib = L
     return L
@@ -373,6 +376,15 @@ def sparse_kv_quest_meta(shape, keys, seq_lens, meta, stream=None):
                                      _ptr(seq_lens, torch.int32, "seq_lens", numel=shape.batch),
                                      _ptr(meta, dt, "meta", numel=P * (t // 16) * 2 * d), _stream(stream))
     _check("sparse_kv_quest_meta", rc)
+
+
+def sparse_kv_stream_read(shape, keys, sink, stream=None):
+    """Measurement helper: one read of ``keys`` in the block scan's load form."""
+    dt = _torch_dtype(shape.dtype)
+    P, d, t = shape.batch * shape.n_kv_heads, shape.head_dim, shape.max_ctx
+    rc = load().sparse_kv_stream_read(C.byref(shape), _ptr(keys, dt, "keys", numel=P * t * d),
+                                      _ptr(sink, torch.int32, "sink", numel=1), _stream(stream))
+    _check("sparse_kv_stream_read", rc)
 
 
 class HostBuffer:

@@ -34,14 +34,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libsparse_kv.so)")
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, ab_valu: bool = False, out: str | None = None) -> str:
+    """Compile every HIP source for gfx950 and link ``libsparse_kv.so``.
+
+    ab_valu=True builds the A/B variant in which bf16 keys are scored and
+    bf16 attention logits formed on the vector ALU instead of the matrix
+    cores (define SKV_AB_VALU_BF16), into ``out`` (default
+    ``libsparse_kv_valu.so`` beside the library); it exists only for the
+    kernel-trace comparison of the two and is loaded by setting
+    SKV_LIBRARY to its path."""
     cc = hipcc()
+    lib = out or (os.path.join(HERE, "libsparse_kv_valu.so") if ab_valu else LIB)
+    defines = ["-DSKV_AB_VALU_BF16"] if ab_valu else []
     tmpdir = tempfile.mkdtemp(prefix="skv_build_")
     try:
         objs, procs = [], []
         for src in SOURCES:
             obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
-            cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIPCC_FLAGS, *defines, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -50,15 +60,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 _wait(procs.pop(0), verbose)
         while procs:
             _wait(procs.pop(0), verbose)
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = lib + ".tmp"
         link = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:
             print(" ".join(link), flush=True)
         subprocess.run(link, check=True)
-        os.replace(tmp_lib, LIB)
+        os.replace(tmp_lib, lib)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB
+    return lib
 
 
 def _wait(item, verbose):
@@ -73,4 +83,4 @@ def _wait(item, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, ab_valu="--ab-valu" in sys.argv))

@@ -403,6 +403,16 @@ SKV_API skv_status sparse_kv_quest_meta(const skv_shape *shape, const void *keys
     return hip_status(skv::launch_quest_meta(d, keys, seq_lens, meta, (hipStream_t)stream));
 }
 
+SKV_API skv_status sparse_kv_stream_read(const skv_shape *shape, const void *keys, uint32_t *sink, void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!keys || !sink)
+        return SKV_ERR_NULL;
+    return hip_status(skv::launch_stream_read(d, keys, sink, (hipStream_t)stream));
+}
+
 SKV_API skv_status sparse_kv_host_alloc(size_t bytes, void **host_ptr, void **device_ptr) {
     if (!host_ptr || !device_ptr)
         return SKV_ERR_NULL;

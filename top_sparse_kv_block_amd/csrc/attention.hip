@@ -527,9 +527,20 @@ __device__ __forceinline__ void attn_body_mfma(const AttnRow &a, AttnSmem<D, GMA
     combine_waves<D, GMAX>(a, S);
 }
 
+// bf16 takes the matrix-core body; the A/B build (SKV_AB_VALU_BF16, see
+// build.py --ab-valu) runs the vector-ALU body for bf16 too, for the
+// kernel-trace comparison only.
+template <typename E> constexpr bool attn_matrix_cores() {
+#ifdef SKV_AB_VALU_BF16
+    return false;
+#else
+    return E::bytes == 2;
+#endif
+}
+
 template <typename E, int D, int GMAX, int DEPTH>
 __device__ __forceinline__ void attn_body(const AttnRow &a, AttnSmem<D, GMAX> &S, const MfmaBlock<D> &first) {
-    if constexpr (E::bytes == 2)
+    if constexpr (attn_matrix_cores<E>())
         attn_body_mfma<D, GMAX, DEPTH>(a, S, first);
     else
         attn_body_valu<E, D, GMAX, DEPTH>(a, S);
@@ -564,11 +575,14 @@ __device__ __forceinline__ void init_row(AttnRow &a, const uint8_t *q, uint8_t *
 }
 
 // Up to 4 heads per group: at least 4 waves per SIMD (<= 128 VGPRs), i.e.
-// two 8-wave workgroups per CU; larger groups need the registers.
-constexpr int attn_min_waves(int gmax) { return gmax <= 4 ? 4 : 2; }
+// two 8-wave workgroups per CU; larger groups need the registers, and so
+// does the vector-ALU body of the A/B build for bf16.
+template <typename E> constexpr int attn_min_waves(int gmax) {
+    return gmax <= 4 && (attn_matrix_cores<E>() || E::bytes == 4) ? 4 : 2;
+}
 
 template <typename E, int D, int GMAX>
-__global__ __launch_bounds__(kAttnThreads, attn_min_waves(GMAX)) void attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, attn_min_waves<E>(GMAX)) void attn_kernel(
     const uint8_t *__restrict__ q, uint8_t *__restrict__ pool_k, uint8_t *__restrict__ pool_v, int C,
     const int32_t *__restrict__ sel_blocks, const int32_t *__restrict__ sel_slot, const uint8_t *__restrict__ sel_hit,
     const int32_t *__restrict__ sel_count, const int32_t *__restrict__ seq_lens, int Hq, int Hkv, int T, int k,
@@ -595,14 +609,14 @@ __global__ __launch_bounds__(kAttnThreads, attn_min_waves(GMAX)) void attn_kerne
 // registers) where the top-k keys and the head state are small enough,
 // else 2.  The host side (fused_waves_per_simd) applies the same rule.
 template <typename E, int D, int GMAX, int KPT> constexpr int fused_min_waves() {
-    return (E::bytes == 2 && GMAX <= 4 && KPT <= 8) ? 4 : 2;
+    return (attn_matrix_cores<E>() && GMAX <= 4 && KPT <= 8) ? 4 : 2;
 }
 
 // Blocks of K and V a wave of the fused kernel holds at once (see
 // attn_body): at 4 waves per SIMD one; else two if they fit next to the
 // per-head state in about 216 of its 256 registers.
 template <typename E, int D, int GMAX> constexpr int fused_depth() {
-    if constexpr (E::bytes == 2) {  // matrix-core body: q, accumulators, K + V of a block
+    if constexpr (attn_matrix_cores<E>()) {  // matrix-core body: q, accumulators, K + V of a block
         constexpr int fixed = D / 8 + GMAX * D / 16 + 24;
         return fixed + 2 * (D / 4) <= 216 ? 2 : 1;
     } else {
@@ -646,7 +660,7 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
     MfmaBlock<D> first;
     first.have = false;
     auto load_first = [&](int nn) {
-        if constexpr (E::bytes == 2 && depth == 1) {
+        if constexpr (attn_matrix_cores<E>() && depth == 1) {
             const int i0 = split * per_split;
             const int i = i0 + (threadIdx.x >> 6);
             if (i < min(i0 + per_split, nn)) {
@@ -800,7 +814,7 @@ int attention_auto_splits(int rows, int k) {
 // prefers as many workgroups as are resident at once (one or two per CU,
 // see fused_min_waves), each wave streaming several blocks.
 int fused_waves_per_simd(const Dims &d) {
-    return (d.dtype == 1 && d.G() <= 4 && d.NB <= kAttnThreads * 8) ? 4 : 2;
+    return (d.dtype == 1 && attn_matrix_cores<BF16>() && d.G() <= 4 && d.NB <= kAttnThreads * 8) ? 4 : 2;
 }
 
 int fused_auto_splits(const Dims &d, int k) {

@@ -388,15 +388,21 @@ static hipError_t blockmax_mfma_t(const Dims &d, const void *q, int nq, const vo
     return hipGetLastError();
 }
 
-// bf16 keys always take the matrix-core kernel: measured on the 32K
-// workload (4 query rows) it streams faster than the vector kernel (77 us
-// against 81 us per launch), and with 32 query rows (1M context, 4 drafts)
-// the vector kernel is ALU-bound (512 us against 336 us).
+// bf16 keys take the matrix-core kernel: measured on the 32K workload (4
+// query rows) it streams faster than the vector kernel, and with 32 query
+// rows (1M context, 4 drafts) the vector kernel is ALU-bound.  The A/B
+// build (SKV_AB_VALU_BF16, see build.py --ab-valu) sends bf16 to the vector
+// kernel instead, for the kernel-trace comparison only.
 template <typename E, int D>
 static hipError_t blockmax_r(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,
                              float scale, float *scores, hipStream_t st) {
     const int R = nq * d.G();
-    if constexpr (E::bytes == 2) {
+#ifdef SKV_AB_VALU_BF16
+    constexpr bool kMatrixCores = false;
+#else
+    constexpr bool kMatrixCores = E::bytes == 2;
+#endif
+    if constexpr (kMatrixCores) {
         return R <= 16 ? blockmax_mfma_t<D, 1>(d, q, nq, keys, lens, scale, scores, st)
                        : blockmax_mfma_t<D, 2>(d, q, nq, keys, lens, scale, scores, st);
     } else {
@@ -408,6 +414,50 @@ static hipError_t blockmax_r(const Dims &d, const void *q, int nq, const void *k
             return blockmax_t<E, D, 16>(d, q, nq, keys, lens, scale, scores, st);
         return blockmax_t<E, D, 32>(d, q, nq, keys, lens, scale, scores, st);
     }
+}
+
+// Achievable-read anchor (a measurement helper, not part of the step): the
+// block scan's launch shape and load form -- (NB / 4) x rows workgroups of 4
+// waves placed by xcd_row_part, each wave one 16-token block of BB bytes in
+// 16-byte non-temporal lane loads, all of a wave's loads issued before any
+// is used -- and nothing else but a XOR of what was read.  Its rate is the
+// HBM read rate the scan's access pattern can reach on this chip.  The one
+// store happens only for a XOR value the data almost never produce; it keeps
+// the loads alive.
+template <int BB>
+__global__ __launch_bounds__(kScoreThreads) void stream_read_kernel(const uint8_t *__restrict__ keys, int NB,
+                                                                    uint32_t *__restrict__ sink) {
+    constexpr int LPB = BB / 1024;  // 16-byte lane loads per block
+    int row, wgp;
+    xcd_row_part(row, wgp);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = wgp * kScoreWaves + wave;
+    if (n >= NB)
+        return;
+    const uint8_t *p = keys + ((size_t)row * NB + n) * BB + lane * 16;
+    u32x4 v[LPB];
+#pragma unroll
+    for (int i = 0; i < LPB; ++i)
+        v[i] = load_nt(p + i * 1024);
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i)
+        x ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    if (x == 0x9e3779b9u)
+        sink[0] = x;
+}
+
+hipError_t launch_stream_read(const Dims &d, const void *keys, uint32_t *sink, hipStream_t st) {
+    dim3 grid((d.NB + kScoreWaves - 1) / kScoreWaves, d.rows());
+    const int bb = 16 * d.D * d.elem_bytes();
+    const uint8_t *k = (const uint8_t *)keys;
+    if (bb == 2048)
+        hipLaunchKernelGGL(stream_read_kernel<2048>, grid, dim3(kScoreThreads), 0, st, k, d.NB, sink);
+    else if (bb == 4096)
+        hipLaunchKernelGGL(stream_read_kernel<4096>, grid, dim3(kScoreThreads), 0, st, k, d.NB, sink);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<8192>, grid, dim3(kScoreThreads), 0, st, k, d.NB, sink);
+    return hipGetLastError();
 }
 
 hipError_t launch_score_blockmax(const Dims &d, const void *q, int nq, const void *keys, const int32_t *lens,

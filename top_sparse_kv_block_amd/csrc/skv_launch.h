@@ -20,6 +20,7 @@ hipError_t launch_score_blockmax(const Dims &d, const void *q, int n_queries, co
                                  const int32_t *seq_lens, float scale, float *scores, hipStream_t st);
 hipError_t launch_score_quest(const Dims &d, const void *q, int n_queries, const void *meta,
                               const int32_t *seq_lens, float scale, float *scores, hipStream_t st);
+hipError_t launch_stream_read(const Dims &d, const void *keys, uint32_t *sink, hipStream_t st);
 hipError_t launch_quest_meta(const Dims &d, const void *keys, const int32_t *seq_lens, void *meta,
                              hipStream_t st);
 hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *seq_lens, int k, int sink,
