@@ -634,7 +634,7 @@ def run(args):
             B.sparse_kv_select(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, cfg.capacity,
                                buf.sel_blocks, buf.sel_count, buf.slot_block, buf.slot_stamp, buf.clock, buf.sel_slot,
                                buf.sel_hit, buf.miss_block, buf.miss_slot, miss_log[t], None, None, B.SKV_SRC_DEVICE,
-                               buf.pool_k, buf.pool_v, st)
+                               buf.pool_k, buf.pool_v, buf.topk_workspace, st)
             if ev is not None:
                 ev[2].record()
                 ev[3].record()
@@ -645,7 +645,7 @@ def run(args):
                 ev[4].record()
             return
         B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
-                         buf.sel_count, st)
+                         buf.sel_count, buf.topk_workspace, st)
         if ev is not None:
             ev[2].record()
         # list-only cache update; the attention kernel fetches the misses
@@ -851,7 +851,7 @@ def run(args):
                 t = args.warmup + i
                 B.sparse_kv_score(shape, mode, sq_all[t], cfg.n_queries, keys_or_meta, dlens, scale, buf.scores, st)
                 B.sparse_kv_topk(shape, buf.scores, dlens, cfg.k_blocks, cfg.sink, cfg.recent, buf.sel_blocks,
-                                 buf.sel_count, st)
+                                 buf.sel_count, buf.topk_workspace, st)
                 ev[i][0].record()
                 src = (dK, dV) if with_src else (None, None)
                 B.sparse_kv_cache_update(shape, cfg.k_blocks, cfg.capacity, buf.sel_blocks, buf.sel_count,

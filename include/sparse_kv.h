@@ -154,12 +154,21 @@ skv_status sparse_kv_score(const skv_shape *shape, int32_t mode, const void *q, 
  * sel_blocks  [B, Hkv, k_blocks] int32 (output): ascending block ids,
  *             padded with -1 after sel_count entries
  * sel_count   [B, Hkv] int32 (output)
+ * workspace   >= sparse_kv_topk_workspace_bytes(shape, k_blocks) bytes of
+ *             device memory, 256-byte aligned; may be NULL when that size is
+ *             0 (NB <= 16384).  Rows over 16384 blocks are selected by many
+ *             workgroups per row in two launches: the first keeps each
+ *             1024- (or 4096-) block chunk's best blocks there, the second
+ *             picks the row's selection from them.  Nothing in it needs
+ *             clearing; calls that share a workspace must not overlap in
+ *             time (enqueue them on one stream).
  * Limits: 1 <= k_blocks <= min(NB, 1024); NB <= 65536;
  *         ceil(sink/16) + ceil(recent/16) + 1 <= k_blocks when either is > 0.
  */
 skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
                           int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens,
-                          int32_t *sel_blocks, int32_t *sel_count, void *stream);
+                          int32_t *sel_blocks, int32_t *sel_count, void *workspace, size_t workspace_bytes,
+                          void *stream);
 
 /*
  * Stage 3: delta / working-set manager and miss fetch.
@@ -227,7 +236,8 @@ skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int3
  * built (as sparse_kv_cache_update with NULL sources).  For pipelines that
  * attend separately, e.g. one step behind ("KV Cache 塞不进 HBM 了" §2.1:
  * the next step's retrieval runs while the forward uses the KV already
- * resident).
+ * resident).  The workspace is sparse_kv_topk's (rows over 16384 blocks
+ * run that call's first launch, then one launch that selects and updates).
  * Limits: those of the two calls.
  */
 skv_status sparse_kv_select(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
@@ -235,7 +245,8 @@ skv_status sparse_kv_select(const skv_shape *shape, const float *scores, const i
                             int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
                             uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
                             int32_t *miss_slot, int32_t *miss_count, const void *src_k, const void *src_v,
-                            int32_t src_kind, void *pool_k, void *pool_v, void *stream);
+                            int32_t src_kind, void *pool_k, void *pool_v, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /*
  * Stage 3 with importance-capped eviction instead of LRU (OasisKV summary,
@@ -380,6 +391,17 @@ int32_t sparse_kv_select_attend_splits(const skv_shape *shape, int32_t k_blocks)
 /* Workspace bytes sparse_decode_attention needs (0 on invalid arguments). */
 size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, int32_t k_blocks,
                                                int32_t num_splits);
+
+/* Workspace bytes sparse_kv_topk and sparse_kv_select need: 0 when
+ * NB <= 16384, else B*Hkv * chunks * k_blocks * 8 with chunks = ceil(NB /
+ * 1024), or ceil(NB / 4096) when ceil(NB / 1024) * k_blocks > 16384
+ * (0 on invalid arguments). */
+size_t sparse_kv_topk_workspace_bytes(const skv_shape *shape, int32_t k_blocks);
+
+/* One workspace size that serves every call of a step with these k_blocks
+ * and num_splits (0 = each call's own default): the larger of the two
+ * sizes above and the fused call's partials.  0 on invalid arguments. */
+size_t sparse_kv_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits);
 
 /*
  * Helper (prefill time, not part of the step): per-block element-wise key

@@ -56,8 +56,8 @@ def test_score(L):
     assert score(L, mode=9) == UNSUPPORTED
 
 
-def topk(L, s=None, scores=P, k=8, sink=0, recent=0):
-    return L.sparse_kv_topk(s if s is not None else shape(), scores, P, k, sink, recent, P, P, NUL)
+def topk(L, s=None, scores=P, k=8, sink=0, recent=0, ws=NUL, ws_bytes=0):
+    return L.sparse_kv_topk(s if s is not None else shape(), scores, P, k, sink, recent, P, P, ws, ws_bytes, NUL)
 
 
 def test_topk(L):
@@ -68,6 +68,13 @@ def test_topk(L):
     assert topk(L, sink=-1) == SHAPE
     assert topk(L, k=8, sink=64, recent=64) == CAPACITY  # 4 + 4 + 1 forced blocks > 8
     assert topk(L, shape(ctx=16 * 65537)) == UNSUPPORTED  # rows over 65536 blocks
+    # rows over 16384 blocks need the workspace: missing, short, misaligned
+    long = shape(ctx=16 * 16385)
+    need = B.sparse_kv_topk_workspace_bytes(B.make_shape(2, 8, 2, 64, 16 * 16385, "f32"), 8)
+    assert need == 4 * 17 * 8 * 8  # 4 rows, 17 chunks of 1024 blocks, 8 (score, id) pairs each
+    assert topk(L, long) == WORKSPACE
+    assert topk(L, long, ws=P, ws_bytes=need - 1) == WORKSPACE
+    assert topk(L, long, ws=C.c_void_p(0x1010), ws_bytes=need) == WORKSPACE
 
 
 def update(L, k=8, cap=16, src=(NUL, NUL), kind=0, pool=(P, P), sel=P, fn="sparse_kv_cache_update"):
@@ -94,9 +101,9 @@ def test_importance_needs_scores(L):
     assert L.sparse_kv_cache_update_importance(*args) == NULL
 
 
-def select(L, s=None, k=8, cap=16, sink=0, recent=0, kind=0, src=(NUL, NUL), scores=P):
+def select(L, s=None, k=8, cap=16, sink=0, recent=0, kind=0, src=(NUL, NUL), scores=P, ws=NUL, ws_bytes=0):
     return L.sparse_kv_select(s if s is not None else shape(), scores, P, k, sink, recent, cap, P, P, P, P, P, P, P,
-                              P, P, P, src[0], src[1], kind, P, P, NUL)
+                              P, P, P, src[0], src[1], kind, P, P, ws, ws_bytes, NUL)
 
 
 def test_select(L):
@@ -108,6 +115,8 @@ def test_select(L):
     assert select(L, kind=2) == SHAPE
     assert select(L, src=(NUL, P)) == NULL
     assert select(L, shape(ctx=16 * 65537)) == UNSUPPORTED
+    assert select(L, shape(ctx=16 * 40000)) == WORKSPACE
+    assert select(L, shape(ctx=16 * 40000), ws=P, ws_bytes=8) == WORKSPACE
 
 
 def attention(L, s=None, k=8, cap=16, splits=0, src=(NUL, NUL), hit=P, ws=P, ws_bytes=1 << 20, kind=0):
@@ -156,3 +165,26 @@ def test_helpers(L):
     assert L.sparse_decode_attention_workspace_bytes(shape(), 8, 9) == 0
     assert L.sparse_decode_attention_splits(shape(hq=8, hkv=3), 8) == 0
     assert L.sparse_kv_select_attend_splits(shape(), 0) == 0
+
+
+def test_workspace_sizes():
+    s = B.make_shape(1, 64, 8, 128, 1 << 20, "bf16")  # 8 rows of 65536 blocks
+    # chunks of 1024, 2048 or 4096 blocks: the smallest giving at most 4096
+    # candidates (chunks x k rounded up to 4), else at most 16384
+    assert B.sparse_kv_topk_workspace_bytes(s, 128) == 8 * 32 * 128 * 8   # 2048-block chunks
+    assert B.sparse_kv_topk_workspace_bytes(s, 1024) == 8 * 16 * 1024 * 8  # 4096: 16384 candidates
+    assert B.sparse_kv_topk_workspace_bytes(s, 256) == 8 * 16 * 256 * 8   # 4096: exactly 4096
+    assert B.sparse_kv_topk_workspace_bytes(s, 257) == 8 * 32 * 260 * 8  # 2048: stride 260, 8320 candidates
+    short = B.make_shape(8, 32, 8, 128, 32768, "bf16")
+    assert B.sparse_kv_topk_workspace_bytes(short, 128) == 0
+    assert B.sparse_kv_topk_workspace_bytes(short, 0) == 0  # invalid
+    # one size for every call of the step: the largest of the three
+    for sh, k in ((s, 128), (short, 128), (s, 1024)):
+        one = B.sparse_kv_workspace_bytes(sh, k, 0)
+        assert one >= B.sparse_kv_topk_workspace_bytes(sh, k)
+        assert one >= B.sparse_decode_attention_workspace_bytes(sh, k, B.sparse_decode_attention_splits(sh, k))
+        assert one >= B.sparse_decode_attention_workspace_bytes(sh, k, B.sparse_kv_select_attend_splits(sh, k))
+    assert B.sparse_kv_workspace_bytes(short, 128, 0) == max(
+        B.sparse_decode_attention_workspace_bytes(short, 128, 0),
+        B.sparse_decode_attention_workspace_bytes(short, 128, B.sparse_kv_select_attend_splits(short, 128)))
+    assert B.sparse_kv_workspace_bytes(short, 128, 200) == 0  # more splits than blocks

@@ -5,8 +5,9 @@ selection, lists, slot table, stamps, clock and, with a source, the pool.
 
 Scores are seeded random rows that drift from step to step (so hits, misses
 and evictions all occur), at row lengths covering each launch shape: up to
-8192 blocks (512 threads), up to 16384 (1024 threads) and the long-row
-top-k beyond, with ragged lengths, forced sink / recent blocks and a working
+8192 blocks (512 threads), up to 16384 (1024 threads) and the two-launch
+long-row selection beyond (chunk candidates, then selection and update), with
+ragged lengths, forced sink / recent blocks and a working
 set larger than the budget.
 """
 import numpy as np
@@ -35,7 +36,8 @@ def _state(P, k, C, device="cuda"):
     (2, 4, 16 * 2048, 128, 128, 0, 0, 4),         # 2048 blocks, C = k
     (3, 2, 16 * 8192, 32, 48, 64, 128, 4),        # 8192 blocks with forced blocks, C > k
     (1, 3, 16 * 12000, 64, 64, 16, 16, 3),        # 1024 threads
-    (1, 2, 16 * 40000, 128, 160, 0, 256, 3),      # long-row top-k
+    (1, 2, 16 * 40000, 128, 160, 0, 256, 3),      # long rows: 1024-block chunks, 5120 candidates
+    (1, 2, 16 * 65536, 1024, 1024, 32, 0, 2),     # 4096-block chunks, 16384 candidates, C = k = 1024
 ])
 def test_select_equals_topk_then_update(B_, Hkv, T, k, C, sink, recent, steps):
     rng = np.random.default_rng(T + k)
@@ -49,22 +51,29 @@ def test_select_equals_topk_then_update(B_, Hkv, T, k, C, sink, recent, steps):
     a, b = _state(P, k, C), _state(P, k, C)
     pa = [torch.zeros(P, C, 16, D, device="cuda") for _ in range(2)]
     pb = [torch.zeros(P, C, 16, D, device="cuda") for _ in range(2)]
+    wsb = B.sparse_kv_topk_workspace_bytes(shape, k)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None for _ in range(2)]
     base = rng.standard_normal((P, NB)).astype(np.float32)
     for t in range(steps):
         sc = dev((base + 0.3 * rng.standard_normal((P, NB))).astype(np.float32))
         log("select", (B_, Hkv, T, k, C, sink, recent), "step", t)
-        B.sparse_kv_topk(shape, sc, dl, k, sink, recent, a["sel_blocks"], a["sel_count"])
+        B.sparse_kv_topk(shape, sc, dl, k, sink, recent, a["sel_blocks"], a["sel_count"], ws[0])
         B.sparse_kv_cache_update(shape, k, C, a["sel_blocks"], a["sel_count"], a["slot_block"], a["slot_stamp"],
                                  a["clock"], a["sel_slot"], a["sel_hit"], a["miss_block"], a["miss_slot"],
                                  a["miss_count"], K, V, B.SKV_SRC_DEVICE, pa[0], pa[1])
         B.sparse_kv_select(shape, sc, dl, k, sink, recent, C, b["sel_blocks"], b["sel_count"], b["slot_block"],
                            b["slot_stamp"], b["clock"], b["sel_slot"], b["sel_hit"], b["miss_block"], b["miss_slot"],
-                           b["miss_count"], K, V, B.SKV_SRC_DEVICE, pb[0], pb[1])
+                           b["miss_count"], K, V, B.SKV_SRC_DEVICE, pb[0], pb[1], ws[1])
         torch.cuda.synchronize()
         for f in FIELDS + ("slot_block", "slot_stamp", "clock"):
             np.testing.assert_array_equal(host(b[f]), host(a[f]), err_msg=f"{f} at step {t}")
         for x, y in zip(pa, pb):
             assert torch.equal(x, y)
+        # the selection itself against the oracle (the kernels' fp32 scores)
+        o_sel, o_cnt = oracle.topk(host(sc).reshape(B_, Hkv, NB).astype(np.float64), lens, k, T, sink=sink,
+                                   recent=recent)
+        np.testing.assert_array_equal(host(b["sel_blocks"]).reshape(o_sel.shape), o_sel)
+        np.testing.assert_array_equal(host(b["sel_count"]).reshape(o_cnt.shape), o_cnt)
         if t > 0:
             m = host(b["miss_count"])
             assert 0 < m.sum() < host(b["sel_count"]).sum()

@@ -20,8 +20,12 @@ def _run(scores, lens, k, sink=0, recent=0, Hkv=None):
     shape = B.make_shape(B_, hkv, hkv, 64, nb * 16, "f32")
     sel = torch.empty(B_, hkv, k, dtype=torch.int32, device="cuda")
     cnt = torch.empty(B_, hkv, dtype=torch.int32, device="cuda")
+    wsb = B.sparse_kv_topk_workspace_bytes(shape, k)
+    assert (wsb > 0) == (nb > 16384)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
     log("topk", (B_, hkv, nb), "k", k, "sink", sink, "recent", recent)
-    B.sparse_kv_topk(shape, dev(scores.astype(np.float32)), dev(np.asarray(lens, np.int32)), k, sink, recent, sel, cnt)
+    B.sparse_kv_topk(shape, dev(scores.astype(np.float32)), dev(np.asarray(lens, np.int32)), k, sink, recent, sel, cnt,
+                     ws)
     torch.cuda.synchronize()
     ref_sel, ref_cnt = oracle.topk(scores.astype(np.float32).astype(np.float64), np.asarray(lens, np.int32), k,
                                    nb * 16, sink=sink, recent=recent)
@@ -68,10 +72,14 @@ def test_topk_rejects_too_many_forced_blocks():
     assert e.value.status == 4
 
 
-# Rows longer than 16384 blocks take the long-row path (thread maxima bound
-# the threshold, exact select over the keys that reach it, bitmap emit) and
-# fall back to the register path when too many keys reach the bound.
-@pytest.mark.parametrize("nb,k", [(16385, 64), (32768, 1024), (65536, 128), (65536, 1)])
+# Rows longer than 16384 blocks are selected in two launches: each chunk of
+# 1024, 2048 or 4096 blocks keeps its best blocks in the workspace, then one
+# workgroup per row selects from those.  The cases cover every chunk size,
+# 4 to 32 candidates per thread in the second launch, a row length not a
+# multiple of 4 (scalar loads), a budget not a multiple of 4 (padded chunk
+# stride) and k = 1.
+@pytest.mark.parametrize("nb,k", [(16385, 64), (32768, 1024), (65536, 128), (65536, 1), (65536, 1024),
+                                  (65536, 256), (65536, 257), (65536, 400), (50001, 301)])
 def test_topk_long_rows(nb, k):
     r = np.random.default_rng(nb * 7 + k)
     s = r.standard_normal((1, 3, nb)).astype(np.float32)
@@ -96,9 +104,40 @@ def test_topk_long_rows_ragged_sink_recent():
     _run(s, [nb * 16, nb * 16 - 7, 16 * 129 + 3, 16 * 40], 128, sink=4, recent=128)
 
 
+def test_topk_long_rows_infinite_scores():
+    # -inf scores of valid blocks are real candidates: they tie with each
+    # other (lowest ids first) and never lose to a chunk's padding
+    r = np.random.default_rng(14)
+    nb = 40000
+    s = r.standard_normal((1, 3, nb)).astype(np.float32)
+    s[0, 0, :] = -np.inf
+    s[0, 0, 30000:30050] = 1.0     # 50 finite scores, the rest of the budget from -inf ties
+    s[0, 1, ::2] = -np.inf         # every other block
+    s[0, 2, :] = -np.inf
+    s[0, 2, 5] = np.inf
+    _run(s, [nb * 16], 128)
+    _run(s, [nb * 16], 128, sink=16, recent=64)
+
+
+def test_topk_long_rows_workspace_checked():
+    nb, k = 20000, 64
+    shape = B.make_shape(1, 1, 1, 64, nb * 16, "f32")
+    need = B.sparse_kv_topk_workspace_bytes(shape, k)
+    assert need == 1 * 20 * k * 8  # ceil(20000 / 1024) chunks of k (score, id) pairs
+    sc = torch.zeros(1, 1, nb, device="cuda")
+    lens = torch.full((1,), nb * 16, dtype=torch.int32, device="cuda")
+    sel = torch.empty(1, 1, k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, 1, dtype=torch.int32, device="cuda")
+    for ws in (None, torch.empty(need - 8, dtype=torch.uint8, device="cuda")):
+        with pytest.raises(B.SparseKVError) as e:
+            B.sparse_kv_topk(shape, sc, lens, k, 0, 0, sel, cnt, ws)
+        assert e.value.status == 5
+
+
 def test_topk_long_rows_short_valid_lengths():
-    # long allocated rows whose valid part is short: the sampled bound must
-    # not be used when the sample holds fewer candidates than the budget
+    # long allocated rows whose valid part is short: chunks past the valid
+    # length write nothing and the second launch reads only the chunks that
+    # hold valid blocks
     r = np.random.default_rng(13)
     nb = 65536
     s = r.standard_normal((6, 1, nb)).astype(np.float32)

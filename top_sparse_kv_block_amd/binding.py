@@ -35,7 +35,8 @@ EXPORTS = (
     "sparse_decode_attention_splits", "sparse_decode_attention_workspace_bytes", "sparse_kv_quest_meta",
     "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
     "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
-    "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read",
+    "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read", "sparse_kv_topk_workspace_bytes",
+    "sparse_kv_workspace_bytes",
 )
 
 
@@ -66,14 +67,14 @@ def load():
     L = C.CDLL(LIB_PATH)
     S = C.POINTER(skv_shape)
     L.sparse_kv_score.argtypes = [S, _i32, _p, _i32, _p, _p, _f32, _p, _p]
-    L.sparse_kv_topk.argtypes = [S, _p, _p, _i32, _i32, _i32, _p, _p, _p]
+    L.sparse_kv_topk.argtypes = [S, _p, _p, _i32, _i32, _i32, _p, _p, _p, _sz, _p]
     L.sparse_kv_cache_update.argtypes = [S, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
                                          _p]
     L.sparse_kv_cache_update_importance.argtypes = [S, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                                     _p, _i32, _p, _p, _p]
     L.sparse_kv_append.argtypes = [S, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p, _p]
     L.sparse_kv_select.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
-                                   _i32, _p, _p, _p]
+                                   _i32, _p, _p, _p, _sz, _p]
     L.sparse_decode_attention.argtypes = [S, _p, _p, _p, _i32, _p, _p, _p, _p, _p, _i32, _f32, _i32, _p, _p, _i32, _p, _p,
                                           _p, _sz, _p]
     L.sparse_kv_select_attend.argtypes = [S, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
@@ -86,6 +87,10 @@ def load():
     L.sparse_decode_attention_splits.restype = _i32
     L.sparse_decode_attention_workspace_bytes.argtypes = [S, _i32, _i32]
     L.sparse_decode_attention_workspace_bytes.restype = _sz
+    L.sparse_kv_topk_workspace_bytes.argtypes = [S, _i32]
+    L.sparse_kv_topk_workspace_bytes.restype = _sz
+    L.sparse_kv_workspace_bytes.argtypes = [S, _i32, _i32]
+    L.sparse_kv_workspace_bytes.restype = _sz
     L.sparse_kv_quest_meta.argtypes = [S, _p, _p, _p, _p]
     L.sparse_kv_stream_read.argtypes = [S, _p, _p, _p]
     L.sparse_kv_host_alloc.argtypes = [_sz, C.POINTER(_p), C.POINTER(_p)]
@@ -163,14 +168,24 @@ def sparse_kv_score(shape, mode, q, n_queries, keys_or_meta, seq_lens, scale, sc
     _check("sparse_kv_score", rc)
 
 
+def _workspace(ws):
+    # (pointer, bytes) of an optional workspace tensor (None: NULL, 0 bytes)
+    if ws is None:
+        return None, 0
+    return _ptr(ws, None, "workspace"), ws.numel() * ws.element_size()
+
+
 def sparse_kv_topk(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, sel_blocks, sel_count,
-                   stream=None):
+                   workspace=None, stream=None):
+    """``workspace``: a device tensor of at least
+    sparse_kv_topk_workspace_bytes(shape, k_blocks) bytes (None when that is 0)."""
     P = shape.batch * shape.n_kv_heads
     rc = load().sparse_kv_topk(C.byref(shape), _ptr(scores, torch.float32, "scores", numel=P * (shape.max_ctx // 16)),
                                _ptr(seq_lens, torch.int32, "seq_lens", numel=shape.batch), int(k_blocks),
                                int(sink_tokens), int(recent_tokens),
                                _ptr(sel_blocks, torch.int32, "sel_blocks", numel=P * k_blocks),
-                               _ptr(sel_count, torch.int32, "sel_count", numel=P), _stream(stream))
+                               _ptr(sel_count, torch.int32, "sel_count", numel=P), *_workspace(workspace),
+                               _stream(stream))
     _check("sparse_kv_topk", rc)
 
 
@@ -231,8 +246,9 @@ def sparse_kv_cache_update_importance(shape, k_blocks, capacity, sel_blocks, sel
 
 def sparse_kv_select(shape, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity, sel_blocks, sel_count,
                      slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, src_k=None,
-                     src_v=None, src_kind=SKV_SRC_DEVICE, pool_k=None, pool_v=None, stream=None):
-    """sparse_kv_topk then sparse_kv_cache_update (LRU) in one launch, same results."""
+                     src_v=None, src_kind=SKV_SRC_DEVICE, pool_k=None, pool_v=None, workspace=None, stream=None):
+    """sparse_kv_topk then sparse_kv_cache_update (LRU) in one launch (two for
+    rows over 16384 blocks), same results; ``workspace`` as for sparse_kv_topk."""
     dt = _torch_dtype(shape.dtype)
     P, d, t = shape.batch * shape.n_kv_heads, shape.head_dim, shape.max_ctx
     pk, pc = P * k_blocks, P * capacity
@@ -252,7 +268,7 @@ def sparse_kv_select(shape, scores, seq_lens, k_blocks, sink_tokens, recent_toke
         _ptr(miss_block, torch.int32, "miss_block", numel=pk), _ptr(miss_slot, torch.int32, "miss_slot", numel=pk),
         _ptr(miss_count, torch.int32, "miss_count", numel=P), src(src_k, "src_k"), src(src_v, "src_v"),
         int(src_kind), _ptr(pool_k, dt, "pool_k", allow_none=True, numel=pc * 16 * d),
-        _ptr(pool_v, dt, "pool_v", allow_none=True, numel=pc * 16 * d), _stream(stream))
+        _ptr(pool_v, dt, "pool_v", allow_none=True, numel=pc * 16 * d), *_workspace(workspace), _stream(stream))
     _check("sparse_kv_select", rc)
 
 
@@ -367,6 +383,14 @@ def sparse_kv_select_attend_splits(shape, k_blocks) -> int:
 
 def sparse_decode_attention_workspace_bytes(shape, k_blocks, num_splits) -> int:
     return int(load().sparse_decode_attention_workspace_bytes(C.byref(shape), int(k_blocks), int(num_splits)))
+
+
+def sparse_kv_topk_workspace_bytes(shape, k_blocks) -> int:
+    return int(load().sparse_kv_topk_workspace_bytes(C.byref(shape), int(k_blocks)))
+
+
+def sparse_kv_workspace_bytes(shape, k_blocks, num_splits=0) -> int:
+    return int(load().sparse_kv_workspace_bytes(C.byref(shape), int(k_blocks), int(num_splits)))
 
 
 def sparse_kv_quest_meta(shape, keys, seq_lens, meta, stream=None):

@@ -47,6 +47,12 @@ skv_status hip_status(hipError_t e) { return e == hipSuccess ? SKV_OK : SKV_ERR_
 
 int nb_blocks(int tokens) { return (tokens + 15) / 16; }
 
+// The top-k's workspace: only rows over 16384 blocks need one.
+bool topk_workspace_ok(const Dims &d, int k, const void *ws, size_t bytes) {
+    const size_t need = skv::long_row_ws_bytes(d, k);
+    return need == 0 || (ws && bytes >= need && ((uintptr_t)ws & 255u) == 0);
+}
+
 }  // namespace
 
 SKV_API skv_status sparse_kv_score(const skv_shape *shape, int32_t mode, const void *q, int32_t n_queries,
@@ -70,7 +76,7 @@ SKV_API skv_status sparse_kv_score(const skv_shape *shape, int32_t mode, const v
 
 SKV_API skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
                                   int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t *sel_blocks,
-                                  int32_t *sel_count, void *stream) {
+                                  int32_t *sel_count, void *workspace, size_t workspace_bytes, void *stream) {
     Dims d;
     skv_status st = check_shape(shape, d);
     if (st != SKV_OK)
@@ -86,8 +92,10 @@ SKV_API skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, c
         if (forced_max > k_blocks)
             return SKV_ERR_CAPACITY;
     }
+    if (!topk_workspace_ok(d, k_blocks, workspace, workspace_bytes))
+        return SKV_ERR_WORKSPACE;
     return hip_status(skv::launch_topk(d, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, sel_blocks,
-                                       sel_count, (hipStream_t)stream));
+                                       sel_count, workspace, (hipStream_t)stream));
 }
 
 static skv_status cache_update_impl(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
@@ -154,7 +162,7 @@ SKV_API skv_status sparse_kv_select(const skv_shape *shape, const float *scores,
                                     uint32_t *slot_stamp, uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit,
                                     int32_t *miss_block, int32_t *miss_slot, int32_t *miss_count,
                                     const void *src_k, const void *src_v, int32_t src_kind, void *pool_k,
-                                    void *pool_v, void *stream) {
+                                    void *pool_v, void *workspace, size_t workspace_bytes, void *stream) {
     Dims d;
     skv_status st = check_shape(shape, d);
     if (st != SKV_OK)
@@ -181,10 +189,12 @@ SKV_API skv_status sparse_kv_select(const skv_shape *shape, const float *scores,
     const bool fetch = src_k || src_v;
     if (fetch && (!src_k || !src_v || !pool_k || !pool_v))
         return SKV_ERR_NULL;
+    if (!topk_workspace_ok(d, k_blocks, workspace, workspace_bytes))
+        return SKV_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = skv::launch_select(d, scores, seq_lens, k_blocks, sink_tokens, recent_tokens, capacity, sel_blocks,
                                       sel_count, slot_block, slot_stamp, clock, sel_slot, sel_hit, miss_block,
-                                      miss_slot, miss_count, s);
+                                      miss_slot, miss_count, workspace, s);
     if (e != hipSuccess || !fetch)
         return hip_status(e);
     return hip_status(skv::launch_gather(d, k_blocks, capacity, miss_block, miss_slot, miss_count, src_k, src_v,
@@ -233,6 +243,29 @@ SKV_API size_t sparse_decode_attention_workspace_bytes(const skv_shape *shape, i
         return 0;
     const int splits = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
     return skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
+}
+
+SKV_API size_t sparse_kv_topk_workspace_bytes(const skv_shape *shape, int32_t k_blocks) {
+    Dims d;
+    if (check_shape(shape, d) != SKV_OK || k_blocks < 1 || k_blocks > d.NB || k_blocks > skv::kMaxK ||
+        d.NB > skv::kMaxTopkBlocks)
+        return 0;
+    return skv::long_row_ws_bytes(d, k_blocks);
+}
+
+SKV_API size_t sparse_kv_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits) {
+    Dims d;
+    if (check_shape(shape, d) != SKV_OK || k_blocks < 1 || k_blocks > skv::kMaxK || num_splits < 0 ||
+        num_splits > k_blocks || num_splits > skv::kMaxSplits)
+        return 0;
+    const int att = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
+    const int fused = num_splits == 0 ? skv::fused_auto_splits(d, k_blocks) : num_splits;
+    size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, att > fused ? att : fused);
+    if (k_blocks <= d.NB && d.NB <= skv::kMaxTopkBlocks) {
+        const size_t tk = skv::long_row_ws_bytes(d, k_blocks);
+        need = tk > need ? tk : need;
+    }
+    return need;
 }
 
 SKV_API skv_status sparse_decode_attention(const skv_shape *shape, const void *q, void *pool_k, void *pool_v,

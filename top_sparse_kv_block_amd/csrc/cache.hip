@@ -102,51 +102,22 @@ __global__ __launch_bounds__(kCacheThreads) void cache_update_kernel(
 // workgroup (the same results as the two calls, bit for bit): the row's selection
 // stays in LDS between the two, the slot table is read while the top-k runs,
 // and the plan is committed by the same workgroup.  Rows up to 8192 blocks
-// run with 512 threads, up to 16384 with 1024, longer rows take the long-row
-// top-k with 1024 threads.
-// Register-resident rows run the top-k's bits straight into the plan
-// (select_plan_row); long rows run topk_long_row, then cache_plan_row.
-template <int THREADS, int KPT> struct SelectTopk {
-    TopkScratch sc;
-    PlanScratch<THREADS> ps;
-    __device__ void clear(CacheScratch &cs, int k, int C) { select_plan_clear<THREADS>(cs, ps, k, C); }
-    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
-                       const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
-        const uint64_t take = topk_take<THREADS, KPT>(srow, len, NB, k, sink, recent, sc);
-        return select_plan_row<THREADS, KPT>(take, k, C, NB, regs, out, cs, ps, n, bad, [](int) {});
-    }
-};
-template <int THREADS> struct SelectTopk<THREADS, 0> {
-    TopkLongScratch ls;
-    __device__ void clear(CacheScratch &cs, int k, int C) { cache_plan_clear<THREADS>(cs, k, C); }
-    __device__ int run(const float *srow, int len, int NB, int k, int sink, int recent, int C,
-                       const SlotRegs<THREADS> &regs, int32_t *out, CacheScratch &cs, int &n, int &bad) {
-        n = topk_long_row<THREADS>(srow, len, NB, k, sink, recent, out, ls);
-        return cache_plan_row<THREADS>(out, n, C, NB, regs, cs, bad);
-    }
-};
+// run with 512 threads, up to 16384 with 1024; the top-k's bits go straight
+// into the plan (select_plan_row).  Longer rows run the top-k's phase A
+// (topk_chunk_kernel) first; select_long_kernel then takes the selection from
+// its candidates and plans it with cache_plan_row.
 
-template <int THREADS, int KPT>
-__global__ __launch_bounds__(THREADS) void select_kernel(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int Hkv, int T, int NB, int k, int sink,
-    int recent, int C, int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
-    int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp, uint32_t *__restrict__ clock,
-    int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit, int32_t *__restrict__ miss_block,
-    int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count) {
-    __shared__ SelectTopk<THREADS, KPT> tk;
-    __shared__ int32_t sS[kMaxK];
-    __shared__ CacheScratch cs;
-    __shared__ uint32_t sClock;
-    const int row = blockIdx.x;
+// Writes a row's selection and lists and commits its plan (the selected
+// slots take the blocks and the row's new clock as stamp); a refused row
+// gets padded lists and keeps its table, stamps and clock.
+template <int THREADS>
+__device__ void select_commit(int row, int k, int C, int n, int nm, int bad, const int32_t *sS, const CacheScratch &cs,
+                              int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
+                              int32_t *__restrict__ sb, uint32_t *__restrict__ ss, uint32_t *__restrict__ clock,
+                              int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit,
+                              int32_t *__restrict__ miss_block, int32_t *__restrict__ miss_slot,
+                              int32_t *__restrict__ miss_count, uint32_t &sClock) {
     const int tid = threadIdx.x;
-    const int len = min(max(seq_lens[row / Hkv], 0), T);
-    int32_t *sb = slot_block + (size_t)row * C;
-    uint32_t *ss = slot_stamp + (size_t)row * C;
-    SlotRegs<THREADS> regs;  // in flight while the top-k runs
-    load_slots<THREADS>(regs, C, sb, ss);
-    tk.clear(cs, k, C);  // published by the top-k's barriers
-    int n, bad;
-    const int nm = tk.run(scores + (size_t)row * NB, len, NB, k, sink, recent, C, regs, sS, cs, n, bad);
     for (int i = tid; i < k; i += THREADS)
         sel_blocks[(size_t)row * k + i] = sS[i];
     if (tid == 0)
@@ -169,6 +140,63 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
             ss[s] = now;
         }
     }
+}
+
+template <int THREADS, int KPT>
+__global__ __launch_bounds__(THREADS) void select_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int Hkv, int T, int NB, int k, int sink,
+    int recent, int C, int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count,
+    int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp, uint32_t *__restrict__ clock,
+    int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit, int32_t *__restrict__ miss_block,
+    int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count) {
+    __shared__ TopkScratch sc;
+    __shared__ PlanScratch<THREADS> ps;
+    __shared__ int32_t sS[kMaxK];
+    __shared__ CacheScratch cs;
+    __shared__ uint32_t sClock;
+    const int row = blockIdx.x;
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    int32_t *sb = slot_block + (size_t)row * C;
+    uint32_t *ss = slot_stamp + (size_t)row * C;
+    SlotRegs<THREADS> regs;  // in flight while the top-k runs
+    load_slots<THREADS>(regs, C, sb, ss);
+    select_plan_clear<THREADS>(cs, ps, k, C);  // published by the top-k's barriers
+    int n, bad;
+    const uint64_t take = topk_take<THREADS, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, sc);
+    const int nm = select_plan_row<THREADS, KPT>(take, k, C, NB, regs, sS, cs, ps, n, bad, [](int) {});
+    select_commit<THREADS>(row, k, C, n, nm, bad, sS, cs, sel_blocks, sel_count, sb, ss, clock, sel_slot, sel_hit,
+                           miss_block, miss_slot, miss_count, sClock);
+}
+
+// Long rows, phase B with the working-set update (after topk_chunk_kernel).
+template <int KPT>
+__global__ __launch_bounds__(kLongRowThreads) void select_long_kernel(
+    const int32_t *__restrict__ seq_lens, int Hkv, int T, int NB, int k, int sink, int recent, int C,
+    int chunk_blocks, int nchunks, const float *__restrict__ ws, int32_t *__restrict__ sel_blocks,
+    int32_t *__restrict__ sel_count, int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp,
+    uint32_t *__restrict__ clock, int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit,
+    int32_t *__restrict__ miss_block, int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count) {
+    constexpr int THREADS = kLongRowThreads;
+    __shared__ TopkScratch sc;
+    __shared__ int32_t sS[kMaxK];
+    __shared__ CacheScratch cs;
+    __shared__ uint32_t sClock;
+    const int row = blockIdx.x;
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    int32_t *sb = slot_block + (size_t)row * C;
+    uint32_t *ss = slot_stamp + (size_t)row * C;
+    SlotRegs<THREADS> regs;  // in flight while the selection runs
+    load_slots<THREADS>(regs, C, sb, ss);
+    cache_plan_clear<THREADS>(cs, k, C);  // published by the selection's barriers
+    const size_t nc = (size_t)nchunks * long_row_stride(k);
+    const float *wrow = ws + (size_t)row * 2 * nc;
+    const int ncand = (min(nb_of(len), NB) + chunk_blocks - 1) / chunk_blocks * long_row_stride(k);
+    const int n = long_row_select<THREADS, KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), ncand, len, NB, k,
+                                                sink, recent, sS, sc);
+    int bad;
+    const int nm = cache_plan_row<THREADS>(sS, n, C, NB, regs, cs, bad);
+    select_commit<THREADS>(row, k, C, n, nm, bad, sS, cs, sel_blocks, sel_count, sb, ss, clock, sel_slot, sel_hit,
+                           miss_block, miss_slot, miss_count, sClock);
 }
 
 // One wave copies one missed block: K then V, 16*D elements each.
@@ -229,7 +257,7 @@ static hipError_t select_t(const Dims &d, const float *scores, const int32_t *le
 hipError_t launch_select(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
                          int cap, int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
                          uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
-                         int32_t *miss_slot, int32_t *miss_count, hipStream_t st) {
+                         int32_t *miss_slot, int32_t *miss_count, void *ws, hipStream_t st) {
 #define SKV_SELECT(TH, KP)                                                                                          \
     return select_t<TH, KP>(d, scores, lens, k, sink, recent, cap, sel_blocks, sel_count, slot_block, slot_stamp, \
                             clock, sel_slot, sel_hit, miss_block, miss_slot, miss_count, st)
@@ -246,8 +274,31 @@ hipError_t launch_select(const Dims &d, const float *scores, const int32_t *lens
         SKV_SELECT(512, 16);
     if (kpt <= 32)
         SKV_SELECT(1024, 16);
-    SKV_SELECT(1024, 0);
 #undef SKV_SELECT
+    hipError_t e = launch_topk_chunks(d, scores, lens, k, sink, recent, static_cast<float *>(ws), st);
+    if (e != hipSuccess)
+        return e;
+    const int ch = long_row_chunk(d.NB, k), nch = long_row_chunks(d.NB, k);
+    const float *w = static_cast<const float *>(ws);
+#define SKV_SELECT_LONG(KP)                                                                                       \
+    hipLaunchKernelGGL(select_long_kernel<KP>, dim3(d.rows()), dim3(kLongRowThreads), 0, st, lens, d.Hkv, d.T,     \
+                       d.NB, k, sink, recent, cap, ch, nch, w, sel_blocks, sel_count, slot_block, slot_stamp, clock, \
+                       sel_slot, sel_hit, miss_block, miss_slot, miss_count)
+    switch (long_row_kpt(d, k)) {
+    case 4:
+        SKV_SELECT_LONG(4);
+        break;
+    case 8:
+        SKV_SELECT_LONG(8);
+        break;
+    case 16:
+        SKV_SELECT_LONG(16);
+        break;
+    default:
+        SKV_SELECT_LONG(32);
+    }
+#undef SKV_SELECT_LONG
+    return hipGetLastError();
 }
 
 template <int BB>

@@ -24,7 +24,13 @@ hipError_t launch_stream_read(const Dims &d, const void *keys, uint32_t *sink, h
 hipError_t launch_quest_meta(const Dims &d, const void *keys, const int32_t *seq_lens, void *meta,
                              hipStream_t st);
 hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *seq_lens, int k, int sink,
-                       int recent, int32_t *sel_blocks, int32_t *sel_count, hipStream_t st);
+                       int recent, int32_t *sel_blocks, int32_t *sel_count, void *ws, hipStream_t st);
+// Rows over 16384 blocks: the top-k's first (chunk) launch and its workspace
+// size (0 for shorter rows), the keys per thread of the second launch.
+hipError_t launch_topk_chunks(const Dims &d, const float *scores, const int32_t *seq_lens, int k, int sink,
+                              int recent, float *ws, hipStream_t st);
+size_t long_row_ws_bytes(const Dims &d, int k);
+int long_row_kpt(const Dims &d, int k);
 hipError_t launch_cache_update(const Dims &d, int k, int cap, const int32_t *sel_blocks,
                                const int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
                                uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
@@ -35,7 +41,7 @@ hipError_t launch_append(const Dims &d, const void *new_k, const void *new_v, in
 hipError_t launch_select(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
                          int cap, int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
                          uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
-                         int32_t *miss_slot, int32_t *miss_count, hipStream_t st);
+                         int32_t *miss_slot, int32_t *miss_count, void *ws, hipStream_t st);
 hipError_t launch_gather(const Dims &d, int k, int cap, const int32_t *miss_block, const int32_t *miss_slot,
                          const int32_t *miss_count, const void *src_k, const void *src_v, void *pool_k,
                          void *pool_v, hipStream_t st);

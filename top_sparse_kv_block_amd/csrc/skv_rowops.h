@@ -56,16 +56,18 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 struct TopkScratch {
-    uint32_t hist[2][256];  // passes alternate buffers, so clearing needs no barrier of its own
+    uint32_t hist[3][256];  // passes rotate three buffers (see radix_select)
     uint32_t wsum[16];
     uint32_t wlo[16], whi[16];  // per-wave key range
-    uint32_t digit, remaining, n_tau;
 };
 
-// Wave 0 finds the digit bin holding the `remaining`-th largest key of the
-// pass: lane l scans bins 255-4l .. 252-4l, a DPP scan adds the lanes.
-// Writes the digit, the rank left inside its bin and the bin's count.
-__device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remaining, TopkScratch &sc) {
+// Every wave finds the digit bin holding the `remaining`-th largest key of
+// the pass from the complete histogram: lane l reads bins 255-4l .. 252-4l,
+// a DPP scan adds the lanes, and the one lane whose bins hold that rank
+// broadcasts the digit, the rank left inside its bin and the bin's count.
+// The results are wave-uniform and equal in every wave.
+__device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remaining, uint32_t &digit,
+                                           uint32_t &rem_out, uint32_t &n_bin) {
     const int lane = threadIdx.x & 63;
     uint32_t c[4], t = 0;
 #pragma unroll
@@ -74,28 +76,39 @@ __device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remain
         t += c[u];
     }
     uint32_t run = wave_incl_scan(t) - t;  // keys in higher bins
+    int hit = -1;
+    uint32_t r = 0, n = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        if (run < remaining && remaining <= run + c[u]) {
-            sc.digit = 255u - (uint32_t)(4 * lane + u);
-            sc.remaining = remaining - run;
-            sc.n_tau = c[u];
+        if (hit < 0 && run < remaining && remaining <= run + c[u]) {
+            hit = u;
+            r = remaining - run;
+            n = c[u];
         }
         run += c[u];
     }
+    const uint64_t b = __builtin_amdgcn_ballot_w64(hit >= 0);  // one lane (1 <= remaining <= keys counted)
+    const int src = (int)__builtin_ctzll(b);
+    digit = 255u - (uint32_t)(4 * src + __builtin_amdgcn_readlane(hit, src));
+    rem_out = (uint32_t)__builtin_amdgcn_readlane((int)r, src);
+    n_bin = (uint32_t)__builtin_amdgcn_readlane((int)n, src);
 }
 
 // Radix select: the key of the `need`-th largest of the keys flagged in
 // `cand` (KPT per thread; need >= 1 and at most the number of flagged keys).
 // Up to four 8-bit passes over an LDS histogram, on the keys minus the
-// smallest flagged key; each pass needs two barriers (the histogram buffers
-// alternate, so clearing the next one needs none).  Returns the key;
-// `remaining` = how many keys equal to it are admitted, `n_tau` = how many
-// flagged keys equal it.  The passes stop early once the bin holding the
-// need-th key is admitted whole (its count equals the rank still needed):
-// the returned key is then the smallest one with the decided leading bits,
-// every flagged key at or above it is admitted, and remaining == n_tau
-// (no tie to break), so the admitted set is the one the full passes give.
+// smallest flagged key.  One barrier per pass: every wave reads the whole
+// histogram and picks the digit itself, and the histograms rotate over
+// three buffers, so the one a pass clears was last read two passes earlier,
+// before the barrier of the previous pass.  Returns the key; `remaining` =
+// how many keys equal to it are admitted, `n_tau` = how many flagged keys
+// equal it.  The passes stop early once the bin holding the need-th key is
+// admitted whole (its count equals the rank still needed): the returned
+// key is then the smallest one with the decided leading bits, every flagged
+// key at or above it is admitted, and remaining == n_tau (no tie to break),
+// so the admitted set is the one the full passes give.  The last pick's
+// reads are not followed by a barrier: the caller passes one before anything
+// writes sc.hist again (another radix_select included).
 template <int THREADS, int KPT>
 __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uint64_t cand, uint32_t need,
                                                  TopkScratch &sc, uint32_t &remaining_out, uint32_t &n_tau_out) {
@@ -117,8 +130,8 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
         sc.wlo[wave] = lo;
         sc.whi[wave] = hi;
     }
-    if (tid < 256)
-        sc.hist[0][tid] = 0;
+    for (int i = tid; i < 256; i += THREADS)
+        sc.hist[0][i] = 0;
     lds_barrier();
 #pragma unroll
     for (int w = 0; w < THREADS / 64; ++w) {
@@ -133,30 +146,31 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = max(top - 8 * (pass + 1), 0);
         const uint32_t dmask = (1u << (top - 8 * pass - shift)) - 1u;
-        uint32_t *hist = sc.hist[pass & 1];
+        uint32_t *hist = sc.hist[pass % 3];
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
             const uint32_t kr = key[m] - lo;
             if (((cand >> m) & 1u) && (kr & mask) == prefix)
                 atomicAdd(&hist[(kr >> shift) & dmask], 1u);
         }
-        if (tid < 256)
-            sc.hist[(pass + 1) & 1][tid] = 0;  // last read by the previous pass's pick
+        for (int i = tid; i < 256; i += THREADS)
+            sc.hist[(pass + 1) % 3][i] = 0;  // last read two passes ago
         lds_barrier();
-        if (tid < 64)
-            pick_digit(hist, remaining, sc);
-        lds_barrier();
-        prefix |= sc.digit << shift;
+        uint32_t digit;
+        pick_digit(hist, remaining, digit, remaining, n_tau);  // n_tau after the last pass: keys equal to tau
+        prefix |= digit << shift;
         mask |= dmask << shift;
-        remaining = sc.remaining;
-        n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
-        if (n_tau == remaining)  // uniform (read from LDS after the barrier)
+        if (n_tau == remaining)  // uniform
             break;
     }
     remaining_out = remaining;
     n_tau_out = n_tau;
     return prefix + lo;
 }
+
+template <int THREADS, int KPT>
+__device__ __forceinline__ uint64_t select_take(const uint32_t (&key)[KPT], uint64_t cand, uint64_t forced, int need,
+                                                TopkScratch &sc);
 
 // Per-row selection under the budget (sink + recent blocks forced, the rest
 // by (score desc, id asc)) as bits: thread t owns ids [t*KPT, t*KPT+KPT) and
@@ -233,6 +247,16 @@ __device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, in
         for (int m = 0; m < KPT; ++m)
             classify(m, base + m < nvalid ? srow[base + m] : 0.0f);
     }
+    return select_take<THREADS, KPT>(key, cand, forced, need, sc);
+}
+
+// The admitted bits of a thread's KPT keys: every forced key, and the `need`
+// largest flagged (`cand`) keys, ties at the threshold going to the lowest
+// positions (thread order, then m).  need <= number of flagged keys.
+// Contains barriers (every thread of the workgroup calls it).
+template <int THREADS, int KPT>
+__device__ __forceinline__ uint64_t select_take(const uint32_t (&key)[KPT], uint64_t cand, uint64_t forced, int need,
+                                                TopkScratch &sc) {
     uint32_t remaining = 0, n_tau = 0;
     const uint32_t tau = need > 0 ? radix_select<THREADS, KPT>(key, cand, (uint32_t)need, sc, remaining, n_tau) : 0u;
     uint64_t take = 0;
@@ -303,249 +327,179 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
 }
 
 // ------------------------------------------------------------ long rows
-// Top-k for long rows (up to 65536 blocks with 1024 threads); same result as
-// topk_row, without holding the row in registers:
-//  1. a lower bound of the threshold: the need-th largest of the per-thread
-//     maxima, since at least `need` keys reach it.  One more pass over the
-//     row puts the keys that reach it (typically not many more than need)
-//     with their ids into LDS, and a
-//     radix select over those gives the threshold key, how many keys equal
-//     it and how many of those are admitted.  If more than kLongRowCand keys
-//     reach the bound (many equal scores) the radix passes stream the row.
-//  2. the choice goes into a bitmap of the row: forced ids and keys above the
-//     threshold; keys equal to it go to a second bitmap whose prefix
-//     popcounts rank them by id (the lowest ids are admitted);
-//  3. one prefix sum over the bitmap words emits the ids in ascending order.
-constexpr int kLongRowCand = 4096;
+// Rows over kLongRowBlocks blocks are selected in two launches that spread
+// a row over many workgroups (one workgroup holding a 65536-block row streams
+// it at one CU's rate).  The row's blocks are cut into chunks of
+// long_row_chunk() blocks:
+//  A. one workgroup per (row, chunk) keeps the chunk's `need` best
+//     non-forced blocks (need = k - forced blocks; order (score desc,
+//     id asc); all of them if fewer) as (score, id) pairs, ascending by id,
+//     in the chunk's kp = long_row_stride(k) entries of the workspace,
+//     padded with id -1;
+//  B. one workgroup per row takes the `need` best of those candidates
+//     (ties to the lower position, which is the lower id) and adds the
+//     forced blocks in front (sink) and behind (recent).
+// Exact: a block among the row's `need` best is among its chunk's `need`
+// best under the same total order; padding never competes.
+constexpr int kLongRowBlocks = 16384;
+constexpr int kChunkThreads = 256;     // phase A
+constexpr int kLongRowThreads = 512;   // phase B
+constexpr int kLongRowMaxCand = 32 * kLongRowThreads;  // candidates per row phase B holds in registers
 
-struct TopkLongScratch {
-    TopkScratch sc;
-    uint32_t n_cand;
-    uint32_t cand_key[kLongRowCand];
-    int32_t cand_id[kLongRowCand];
-    uint32_t bits[kMaxTopkBlocks / 32];
-    uint32_t eq[kMaxTopkBlocks / 32];
-};
-
-// Adds `digit` to hist for every lane with `on` set, one atomic per distinct
-// digit of the wave (lanes must be converged).
-__device__ __forceinline__ void wave_hist_add(uint32_t *hist, uint32_t digit, bool on) {
-    const int lane = threadIdx.x & 63;
-    uint64_t act = __builtin_amdgcn_ballot_w64(on);
-    while (act) {
-        const int leader = __builtin_ctzll(act);
-        const uint32_t dl = (uint32_t)__builtin_amdgcn_readlane((int)digit, leader);
-        const bool same = on && digit == dl;
-        const uint64_t grp = __builtin_amdgcn_ballot_w64(same);
-        if (lane == leader)
-            atomicAdd(&hist[dl], (uint32_t)__builtin_popcountll(grp));
-        on = on && !same;
-        act &= ~grp;
-    }
+// Entries per chunk in the workspace: k rounded up to a multiple of 4, so
+// that every chunk and row starts 16-byte aligned.
+__host__ __device__ inline int long_row_stride(int k) { return (k + 3) & ~3; }
+// Blocks per phase-A chunk (1024, 2048 or 4096) for a row of NB blocks and
+// budget k: the smallest whose candidates (chunks * stride) number at most
+// 4096, else the smallest whose candidates fit phase B (4096 always does:
+// NB <= 65536, k <= 1024).  Measured on rows of 65536 blocks with k = 128:
+// 2048-block chunks (4096 candidates) take 19.4 us for both launches,
+// 1024-block chunks (8192 candidates) 20.6 us; one workgroup per row
+// selecting from the candidates costs about twice what a chunk does, and
+// more so the more candidates it reads.
+__host__ __device__ inline int long_row_chunk(int NB, int k) {
+    const int kp = long_row_stride(k);
+    for (int lim : {4096, kLongRowMaxCand})
+        for (int ch = 1024; ch <= 4096; ch *= 2)
+            if ((NB + ch - 1) / ch * kp <= lim)
+                return ch;
+    return 4096;
+}
+__host__ __device__ inline int long_row_chunks(int NB, int k) {
+    const int ch = long_row_chunk(NB, k);
+    return (NB + ch - 1) / ch;
 }
 
-template <int THREADS>
-__device__ int topk_long_row(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
-                             int32_t *out, TopkLongScratch &ls) {
-    static_assert(THREADS * 4 >= kLongRowCand && THREADS * 2 * 32 >= kMaxTopkBlocks, "coverage");
-    constexpr int BATCH = 8;
+// The row's forced ranges [0, fs) (sink) and [fr, nvalid) (recent) and the
+// number of blocks the budget leaves to the scores.
+__device__ __forceinline__ int forced_ranges(int len, int nvalid, int k, int sink, int recent, int &fs, int &fr) {
+    fs = sink > 0 ? min(nb_of(min(sink, len)), nvalid) : 0;
+    fr = recent > 0 ? max(0, len - recent) / 16 : nvalid;
+    const int n_forced = fs + (nvalid - fr) - max(0, fs - fr);
+    return k - n_forced;
+}
+
+// Phase A for chunk `chunk` of a row (THREADS threads, KPT keys each, chunk
+// = THREADS * KPT blocks; the caller has checked chunk * THREADS * KPT <
+// nvalid).  ws_score / ws_id: this chunk's long_row_stride(k) entries.
+// Contains barriers.
+template <int THREADS, int KPT>
+__device__ void chunk_candidates(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
+                                 int chunk, float *__restrict__ ws_score, int32_t *__restrict__ ws_id, TopkScratch &sc) {
+    static_assert(KPT % 4 == 0, "16-byte loads");
+    const int tid = threadIdx.x;
+    const int nvalid = min(nb_of(len), NB);
+    int fs, fr;
+    const int need = forced_ranges(len, nvalid, k, sink, recent, fs, fr);
+    const int c0 = chunk * THREADS * KPT, c1 = c0 + THREADS * KPT;
+    const int base = c0 + tid * KPT;
+    float v[KPT];
+    if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0 && (NB & 3) == 0) {  // uniform
+        // unconditional 16-byte loads, the index clamped into the row (a
+        // clamped group lies past NB, so all of its ids are masked below)
+#pragma unroll
+        for (int u = 0; u < KPT / 4; ++u) {
+            const float4 f = *reinterpret_cast<const float4 *>(srow + min(base + 4 * u, NB - 4));
+            v[4 * u] = f.x;
+            v[4 * u + 1] = f.y;
+            v[4 * u + 2] = f.z;
+            v[4 * u + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < KPT; ++m)
+            v[m] = srow[min(base + m, nvalid - 1)];
+    }
+    uint32_t key[KPT];
+    uint64_t cand = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+        const int i = base + m;
+        const bool c = i < nvalid && i >= fs && i < fr;
+        key[m] = c ? order_key(v[m]) : 0u;
+        cand |= (uint64_t)c << m;
+    }
+    // candidates in the chunk: all of it when it lies inside [fs, min(fr, nvalid))
+    uint32_t ncand = THREADS * KPT;
+    if (c0 < fs || c1 > min(fr, nvalid))  // uniform
+        (void)wg_exclusive_scan<THREADS, uint32_t>((uint32_t)__builtin_popcountll(cand), sc.wsum, ncand);
+    const int q = min(need, (int)ncand);
+    const uint64_t take = q == (int)ncand ? cand : select_take<THREADS, KPT>(key, cand, 0ull, q, sc);
+    uint32_t tot;
+    uint32_t pos = wg_exclusive_scan<THREADS, uint32_t>((uint32_t)__builtin_popcountll(take), sc.wsum, tot);
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+        if ((take >> m) & 1u) {
+            ws_score[pos] = v[m];
+            ws_id[pos] = base + m;
+            ++pos;
+        }
+    const int kp = long_row_stride(k);
+    for (int i = (int)tot + tid; i < kp; i += THREADS)
+        ws_id[i] = -1;
+}
+
+// Phase B: the row's selection, ascending, into S[0, k) (LDS; -1 padded);
+// returns its size.  ws_score / ws_id: the row's ncand = chunks * stride
+// entries (THREADS * KPT >= ncand, KPT % 4 == 0, both 16-byte aligned).
+// Contains barriers; S is complete on return.
+template <int THREADS, int KPT>
+__device__ int long_row_select(const float *__restrict__ ws_score, const int32_t *__restrict__ ws_id, int ncand,
+                               int len, int NB, int k, int sink, int recent, int32_t *S, TopkScratch &sc) {
+    static_assert(KPT % 4 == 0, "16-byte loads");
     const int tid = threadIdx.x;
     const int nvalid = min(nb_of(len), NB);
     if (nvalid <= k) {
         for (int i = tid; i < k; i += THREADS)
-            out[i] = i < nvalid ? i : -1;
+            S[i] = i < nvalid ? i : -1;
         __syncthreads();
         return nvalid;
     }
-    const int fs = sink > 0 ? min(nb_of(min(sink, len)), nvalid) : 0;
-    const int fr = recent > 0 ? max(0, len - recent) / 16 : nvalid;
-    const int n_forced = fs + (nvalid - fr) - max(0, fs - fr);
-    const int need = k - n_forced;
-    const int nwords = (nvalid + 31) >> 5;
-    for (int w = tid; w < nwords; w += THREADS) {
-        ls.bits[w] = 0;
-        ls.eq[w] = 0;
+    int fs, fr;
+    const int need = forced_ranges(len, nvalid, k, sink, recent, fs, fr);
+    // candidates: entries with an id (padding never competes, even against
+    // a -inf score); position order is id order.  16-byte loads, the index
+    // clamped into the entries (ncand is a multiple of 4) and masked below.
+    float v[KPT];
+    int32_t ids[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT / 4; ++u) {
+        const int p = min(tid * KPT + 4 * u, ncand - 4);
+        const float4 f = *reinterpret_cast<const float4 *>(ws_score + p);
+        const int4 d = *reinterpret_cast<const int4 *>(ws_id + p);
+        v[4 * u] = f.x;
+        v[4 * u + 1] = f.y;
+        v[4 * u + 2] = f.z;
+        v[4 * u + 3] = f.w;
+        ids[4 * u] = d.x;
+        ids[4 * u + 1] = d.y;
+        ids[4 * u + 2] = d.z;
+        ids[4 * u + 3] = d.w;
     }
-    // f(id, key, is_candidate) for this thread's ids, every lane of a wave
-    // calling f together (keys of non-candidates are 0).  Thread t reads the
-    // 4-id groups t, t + THREADS, ... with BATCH groups in flight: 16-byte
-    // loads when the row is 16-byte aligned and NB a multiple of 4, else
-    // single floats.  The 16-byte loads are unconditional (group index
-    // clamped into the row, ids past the valid length masked afterwards):
-    // with each load in a branch of its own the compiler waits for every
-    // one before issuing the next.
-    const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0 && (NB & 3) == 0;  // uniform
-    const int gmax = (NB >> 2) - 1;
-    auto stream = [&](auto &&f) {
-        const int ngroups = (nvalid + 3) >> 2;
-        for (int g0 = tid; g0 < ngroups; g0 += BATCH * THREADS) {
-            float v[BATCH][4];
-            if (vec) {
-                u32x4 w[BATCH];
+    uint32_t key[KPT];
+    uint64_t cand = 0;
 #pragma unroll
-                for (int u = 0; u < BATCH; ++u)
-                    w[u] = load16(srow + 4 * min(g0 + u * THREADS, gmax));
-#pragma unroll
-                for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[u][e] = 4 * (g0 + u * THREADS) + e < nvalid ? __uint_as_float(w[u][e]) : 0.0f;
-            } else {
-#pragma unroll
-                for (int u = 0; u < BATCH; ++u) {
-                    const int g = g0 + u * THREADS;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        v[u][e] = 4 * g + e < nvalid ? srow[4 * g + e] : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * (g0 + u * THREADS) + e;
-                    const bool c = i < nvalid && i >= fs && i < fr;
-                    f(i, c ? order_key(v[u][e]) : 0u, c);
-                }
-            }
-        }
-    };
-    __syncthreads();  // bitmaps cleared
-    uint32_t remaining = 0, n_tau = 0, tau = 0;
-    if (need > 0) {
-        // 1a. a lower bound of the threshold: the need-th largest of the
-        //     per-thread maxima (at least `need` keys reach it).  (A sampled
-        //     subset of the row reads less but its radix select, over a few
-        //     thousand keys, measured slower than this one over 1024.)
-        uint32_t bound = 1u;
-        {
-            uint32_t tmax[1] = {0u}, r1, n1;
-            stream([&](int, uint32_t kk, bool) { tmax[0] = max(tmax[0], kk); });
-            if (__syncthreads_count(tmax[0] != 0u) >= need)
-                bound = radix_select<THREADS, 1>(tmax, tmax[0] != 0u ? 1ull : 0ull, (uint32_t)need, ls.sc, r1, n1);
-        }
-        // 1b. the keys that reach the bound, with their ids, into LDS (in
-        //     any order: neither the select nor the marking needs one)
-        if (tid == 0)
-            ls.n_cand = 0;
-        __syncthreads();
-        stream([&](int i, uint32_t kk, bool c) {
-            if (c && kk >= bound) {
-                const uint32_t p = atomicAdd(&ls.n_cand, 1u);
-                if (p < (uint32_t)kLongRowCand) {
-                    ls.cand_key[p] = kk;
-                    ls.cand_id[p] = i;
-                }
-            }
-        });
-        __syncthreads();
-        const uint32_t total = ls.n_cand;
-        if (total <= (uint32_t)kLongRowCand) {  // uniform
-            uint32_t ck[4];
-            uint64_t cm = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t p = (uint32_t)(tid + THREADS * u);
-                ck[u] = p < total ? ls.cand_key[p] : 0u;
-                cm |= (uint64_t)(p < total) << u;
-            }
-            tau = radix_select<THREADS, 4>(ck, cm, (uint32_t)need, ls.sc, remaining, n_tau);
-            // 2. mark from the candidate list (every key >= tau is in it)
-            const bool all_eq = n_tau == remaining;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t p = (uint32_t)(tid + THREADS * u);
-                if (p < total && ck[u] >= tau) {
-                    const int i = ls.cand_id[p];
-                    if (ck[u] > tau || all_eq)
-                        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
-                    else
-                        atomicOr(&ls.eq[i >> 5], 1u << (i & 31));
-                }
-            }
-        } else {
-            // many keys reach the bound (many equal scores): radix passes that
-            // stream the row (wave-aggregated histogram adds), then marking
-            uint32_t prefix = 0, mask = 0;
-            remaining = (uint32_t)need;
-            if (tid < 256)
-                ls.sc.hist[0][tid] = 0;
-            __syncthreads();
-            for (int pass = 0; pass < 4; ++pass) {
-                const int shift = 24 - 8 * pass;
-                uint32_t *hist = ls.sc.hist[pass & 1];
-                stream([&](int, uint32_t kk, bool c) {
-                    wave_hist_add(hist, (kk >> shift) & 255u, c && (kk & mask) == prefix);
-                });
-                if (tid < 256)
-                    ls.sc.hist[(pass + 1) & 1][tid] = 0;
-                __syncthreads();
-                if (tid < 64)
-                    pick_digit(hist, remaining, ls.sc);
-                __syncthreads();
-                prefix |= ls.sc.digit << shift;
-                mask |= 255u << shift;
-                remaining = ls.sc.remaining;
-                n_tau = ls.sc.n_tau;
-            }
-            tau = prefix;
-            const bool all_eq = n_tau == remaining;
-            stream([&](int i, uint32_t kk, bool c) {
-                if (c && kk >= tau) {
-                    if (kk > tau || all_eq)
-                        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
-                    else
-                        atomicOr(&ls.eq[i >> 5], 1u << (i & 31));
-                }
-            });
-        }
+    for (int m = 0; m < KPT; ++m) {
+        const bool c = tid * KPT + m < ncand && ids[m] >= 0;
+        key[m] = c ? order_key(v[m]) : 0u;
+        cand |= (uint64_t)c << m;
     }
-    // forced blocks: the id ranges [0, fs) and [fr, nvalid)
+    const uint64_t take = select_take<THREADS, KPT>(key, cand, 0ull, need, sc);
+    uint32_t tot;
+    uint32_t pos = wg_exclusive_scan<THREADS, uint32_t>((uint32_t)__builtin_popcountll(take), sc.wsum, tot);
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+        if ((take >> m) & 1u)
+            S[fs + pos++] = ids[m];
     for (int i = tid; i < fs; i += THREADS)
-        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
-    for (int i = fr + tid; i < nvalid; i += THREADS)
-        atomicOr(&ls.bits[i >> 5], 1u << (i & 31));
+        S[i] = i;
+    for (int i = tid; i < nvalid - fr; i += THREADS)
+        S[fs + need + i] = fr + i;
+    const int n = fs + need + (nvalid - fr);
+    for (int i = n + tid; i < k; i += THREADS)
+        S[i] = -1;
     __syncthreads();
-    // thread t owns words 2t, 2t + 1
-    const int w0i = 2 * tid, w1i = 2 * tid + 1;
-    uint32_t w0 = w0i < nwords ? ls.bits[w0i] : 0u, w1 = w1i < nwords ? ls.bits[w1i] : 0u;
-    if (need > 0 && n_tau > remaining) {  // uniform: exact ties, the lowest ids among them
-        const uint32_t e0 = w0i < nwords ? ls.eq[w0i] : 0u, e1 = w1i < nwords ? ls.eq[w1i] : 0u;
-        uint32_t n_eq;
-        const uint32_t r0 = wg_exclusive_scan<THREADS, uint32_t>(
-            (uint32_t)(__builtin_popcount(e0) + __builtin_popcount(e1)), ls.sc.wsum, n_eq);
-        const uint32_t r1 = r0 + (uint32_t)__builtin_popcount(e0);
-        auto keep = [&](uint32_t e, uint32_t r) -> uint32_t {  // the first remaining - r set bits
-            uint32_t kept = 0;
-            while (e && r < remaining) {
-                kept |= e & (0u - e);
-                e &= e - 1;
-                ++r;
-            }
-            return kept;
-        };
-        w0 |= keep(e0, r0);
-        w1 |= keep(e1, r1);
-    }
-    uint32_t n_out;
-    uint32_t o = wg_exclusive_scan<THREADS, uint32_t>((uint32_t)(__builtin_popcount(w0) + __builtin_popcount(w1)),
-                                                      ls.sc.wsum, n_out);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint32_t w = h ? w1 : w0;
-        while (w) {
-            const int bit = __builtin_ctz(w);
-            w &= w - 1;
-            if (o < (uint32_t)k)
-                out[o] = (2 * tid + h) * 32 + bit;
-            ++o;
-        }
-    }
-    n_out = min(n_out, (uint32_t)k);
-    for (int i = (int)n_out + tid; i < k; i += THREADS)
-        out[i] = -1;
-    __syncthreads();
-    return (int)n_out;
+    return n;
 }
 
 // ------------------------------------------------------------ working set

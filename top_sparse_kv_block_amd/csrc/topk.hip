@@ -19,8 +19,6 @@
 
 namespace skv {
 
-constexpr int kTopkLongThreads = 1024;
-
 template <int THREADS, int KPT>
 __global__ __launch_bounds__(THREADS) void topk_kernel(const float *__restrict__ scores,
                                                             const int32_t *__restrict__ seq_lens, int Hkv, int T,
@@ -36,21 +34,85 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(const float *__restrict__
         sel_count[row] = n;
 }
 
-// Rows longer than 16384 blocks: the long-row path (thread maxima bound the
-// threshold, the exact select runs over the few keys that reach it).
-__global__ __launch_bounds__(kTopkLongThreads) void topk_long_kernel(const float *__restrict__ scores,
-                                                                 const int32_t *__restrict__ seq_lens, int Hkv, int T,
-                                                                 int NB, int k, int sink, int recent,
-                                                                 int32_t *__restrict__ sel_blocks,
-                                                                 int32_t *__restrict__ sel_count) {
-    __shared__ TopkLongScratch ls;
+// Long rows, phase A: grid (chunks, rows), one workgroup of THREADS per
+// chunk of THREADS * KPT blocks (rows placed on XCDs as the scoring kernels
+// place them).  ws: per row, chunks * stride scores, then as many ids.
+template <int THREADS, int KPT>
+__global__ __launch_bounds__(THREADS) void topk_chunk_kernel(const float *__restrict__ scores,
+                                                             const int32_t *__restrict__ seq_lens, int Hkv, int T,
+                                                             int NB, int k, int sink, int recent,
+                                                             float *__restrict__ ws) {
+    __shared__ TopkScratch sc;
+    int row, chunk;
+    xcd_row_part(row, chunk);
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    const int nvalid = min(nb_of(len), NB);
+    // uniform: a row of at most k valid blocks takes them all without its
+    // candidates, and phase B reads no entry of a chunk past the valid part
+    if (nvalid <= k || chunk * THREADS * KPT >= nvalid)
+        return;
+    const size_t nc = (size_t)gridDim.x * long_row_stride(k);
+    float *wrow = ws + (size_t)row * 2 * nc;
+    const size_t off = (size_t)chunk * long_row_stride(k);
+    chunk_candidates<THREADS, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, chunk, wrow + off,
+                                   reinterpret_cast<int32_t *>(wrow + nc) + off, sc);
+}
+
+// The candidates phase B reads for a row: the chunks that hold valid blocks.
+__device__ __forceinline__ int long_row_ncand(int len, int NB, int k, int chunk_blocks) {
+    return (min(nb_of(len), NB) + chunk_blocks - 1) / chunk_blocks * long_row_stride(k);
+}
+
+// Long rows, phase B of the top-k: one workgroup of kLongRowThreads per row.
+template <int KPT>
+__global__ __launch_bounds__(kLongRowThreads) void topk_long_kernel(const int32_t *__restrict__ seq_lens, int Hkv,
+                                                                    int T, int NB, int k, int sink, int recent,
+                                                                    int chunk_blocks, int nchunks,
+                                                                    const float *__restrict__ ws,
+                                                                    int32_t *__restrict__ sel_blocks,
+                                                                    int32_t *__restrict__ sel_count) {
+    __shared__ TopkScratch sc;
+    __shared__ int32_t sS[kMaxK];
     const int row = blockIdx.x;
     const int len = min(max(seq_lens[row / Hkv], 0), T);
-    const float *srow = scores + (size_t)row * NB;
-    int32_t *out = sel_blocks + (size_t)row * k;
-    const int n = topk_long_row<kTopkLongThreads>(srow, len, NB, k, sink, recent, out, ls);
+    const size_t nc = (size_t)nchunks * long_row_stride(k);
+    const float *wrow = ws + (size_t)row * 2 * nc;
+    const int n = long_row_select<kLongRowThreads, KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc),
+                                                        long_row_ncand(len, NB, k, chunk_blocks), len, NB, k, sink,
+                                                        recent, sS, sc);
+    for (int i = threadIdx.x; i < k; i += kLongRowThreads)
+        sel_blocks[(size_t)row * k + i] = sS[i];
     if (threadIdx.x == 0)
         sel_count[row] = n;
+}
+
+size_t long_row_ws_bytes(const Dims &d, int k) {
+    return d.NB > kLongRowBlocks ? (size_t)d.rows() * long_row_chunks(d.NB, k) * long_row_stride(k) * 8 : 0;
+}
+
+hipError_t launch_topk_chunks(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
+                              float *ws, hipStream_t st) {
+    const int ch = long_row_chunk(d.NB, k);
+    const dim3 grid(long_row_chunks(d.NB, k), d.rows());
+    if (ch == 1024)
+        hipLaunchKernelGGL((topk_chunk_kernel<kChunkThreads, 4>), grid, dim3(kChunkThreads), 0, st, scores, lens,
+                           d.Hkv, d.T, d.NB, k, sink, recent, ws);
+    else if (ch == 2048)
+        hipLaunchKernelGGL((topk_chunk_kernel<kChunkThreads, 8>), grid, dim3(kChunkThreads), 0, st, scores, lens,
+                           d.Hkv, d.T, d.NB, k, sink, recent, ws);
+    else
+        hipLaunchKernelGGL((topk_chunk_kernel<kChunkThreads, 16>), grid, dim3(kChunkThreads), 0, st, scores, lens,
+                           d.Hkv, d.T, d.NB, k, sink, recent, ws);
+    return hipGetLastError();
+}
+
+// Keys per thread of phase B for a row's candidate count.
+int long_row_kpt(const Dims &d, int k) {
+    const int ncand = long_row_chunks(d.NB, k) * long_row_stride(k);
+    for (int kpt = 4; kpt < 32; kpt *= 2)
+        if (ncand <= kpt * kLongRowThreads)
+            return kpt;
+    return 32;
 }
 
 template <int THREADS, int KPT>
@@ -62,7 +124,7 @@ static hipError_t topk_t(const Dims &d, const float *scores, const int32_t *lens
 }
 
 hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *lens, int k, int sink, int recent,
-                       int32_t *sel, int32_t *cnt, hipStream_t st) {
+                       int32_t *sel, int32_t *cnt, void *ws, hipStream_t st) {
     const int kpt = (d.NB + 511) / 512;  // keys per thread with 512 threads
     if (kpt <= 1)
         return topk_t<512, 1>(d, scores, lens, k, sink, recent, sel, cnt, st);
@@ -76,8 +138,28 @@ hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *lens, 
         return topk_t<512, 16>(d, scores, lens, k, sink, recent, sel, cnt, st);
     if (kpt <= 32)
         return topk_t<1024, 16>(d, scores, lens, k, sink, recent, sel, cnt, st);
-    hipLaunchKernelGGL(topk_long_kernel, dim3(d.rows()), dim3(kTopkLongThreads), 0, st, scores, lens, d.Hkv, d.T, d.NB, k,
-                       sink, recent, sel, cnt);
+    hipError_t e = launch_topk_chunks(d, scores, lens, k, sink, recent, static_cast<float *>(ws), st);
+    if (e != hipSuccess)
+        return e;
+    const int ch = long_row_chunk(d.NB, k), nch = long_row_chunks(d.NB, k);
+    const float *w = static_cast<const float *>(ws);
+#define SKV_TOPK_LONG(KP)                                                                                         \
+    hipLaunchKernelGGL(topk_long_kernel<KP>, dim3(d.rows()), dim3(kLongRowThreads), 0, st, lens, d.Hkv, d.T, d.NB, \
+                       k, sink, recent, ch, nch, w, sel, cnt)
+    switch (long_row_kpt(d, k)) {
+    case 4:
+        SKV_TOPK_LONG(4);
+        break;
+    case 8:
+        SKV_TOPK_LONG(8);
+        break;
+    case 16:
+        SKV_TOPK_LONG(16);
+        break;
+    default:
+        SKV_TOPK_LONG(32);
+    }
+#undef SKV_TOPK_LONG
     return hipGetLastError();
 }
 

@@ -82,6 +82,10 @@ class LayerBuffers:
         ws = max(B.sparse_decode_attention_workspace_bytes(self.shape, k, self.splits),
                  B.sparse_decode_attention_workspace_bytes(self.shape, k, self.fused_splits))
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+        # the top-k's own workspace (rows over 16384 blocks), apart from the
+        # attention's so that a selection may run on another stream
+        tk = B.sparse_kv_topk_workspace_bytes(self.shape, k)
+        self.topk_workspace = torch.empty(tk, dtype=torch.uint8, device=device) if tk else None
 
     def reset(self):
         """Empty working set (slot table -1, stamps and clock 0)."""
@@ -98,7 +102,7 @@ class LayerBuffers:
     def topk(self, seq_lens, stream=None):
         c = self.cfg
         B.sparse_kv_topk(self.shape, self.scores, seq_lens, c.k_blocks, c.sink, c.recent, self.sel_blocks,
-                         self.sel_count, stream)
+                         self.sel_count, self.topk_workspace, stream)
 
     def cache_update(self, src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None, importance=False):
         """importance=True evicts by this step's scores (in self.scores) instead of LRU."""
@@ -123,7 +127,7 @@ class LayerBuffers:
         B.sparse_kv_select(self.shape, self.scores, seq_lens, c.k_blocks, c.sink, c.recent, c.capacity, o.sel_blocks,
                            o.sel_count, self.slot_block, self.slot_stamp, self.clock, o.sel_slot, o.sel_hit,
                            o.miss_block, o.miss_slot, o.miss_count, src_k, src_v, src_kind, self.pool_k, self.pool_v,
-                           stream)
+                           self.topk_workspace, stream)
 
     def prefetch(self, hint: "LayerBuffers", src_k, src_v, src_kind=B.SKV_SRC_DEVICE, stream=None):
         """Cross-layer prefetch: an ordinary working-set update of this layer
@@ -245,7 +249,7 @@ class Lag1Pipeline:
                                cur.sel_blocks, cur.sel_count, buf.slot_block, buf.slot_stamp, buf.clock, cur.sel_slot,
                                cur.sel_hit, cur.miss_block, cur.miss_slot,
                                cur.miss_count if miss_count is None else miss_count, None, None, src_kind,
-                               buf.pool_k, buf.pool_v, side)
+                               buf.pool_k, buf.pool_v, buf.topk_workspace, side)
         upd = torch.cuda.Event()
         upd.record(side)
         use = self.lists[(self.t - 1) % 2] if self.t > 0 else cur
