@@ -5,9 +5,7 @@ A step is one pass of the whole path for one attention layer over one batch:
 block scoring -> top-k under the budget -> working-set update -> split-K GQA
 attention that also fetches the step's misses into the pool.  By default
 stages 2-4 run as the library's fused select-attend call (same results as
-the three separate calls; --four-calls runs those instead); rows over 8192
-blocks, beyond the fused call, run the one-launch selection (top-k and
-working-set update) followed by attention.  The default
+the three separate calls; --four-calls runs those instead).  The default
 workload is the Llama-3.1-8B-shaped layer: batch 8, 32 q-heads / 8 kv-heads,
 head_dim 128, bf16 K/V, 32768-token context in 16-token blocks, a
 2048-token budget (128 blocks) and a 128-slot working set per (sequence,
@@ -602,10 +600,6 @@ def run(args):
                      mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent, num_splits=args.splits)
     buf = LayerBuffers(cfg)
     select = False
-    if args.fused and cfg.nb > 8192:
-        # rows over 8192 blocks exceed the fused call: score, the one-launch
-        # selection (top-k + working-set update) and attention run instead
-        args.fused, select = False, True
     keys_or_meta = dK
     if mode == B.SKV_SCORE_QUEST:
         keys_or_meta = torch.empty(w.batch, w.n_kv_heads, cfg.nb, 2, w.head_dim, dtype=cfg.torch_dtype,

@@ -346,8 +346,12 @@ skv_status sparse_decode_attention(const skv_shape *shape, const void *q, void *
  * resident workgroup per CU); results equal the separate calls' bit for bit
  * when both use the same num_splits.  The workspace must hold
  * sparse_decode_attention_workspace_bytes(shape, k_blocks, splits) bytes for
- * the resolved split count.
- * Limits: those of the three calls, and NB <= 8192.
+ * the resolved split count (the partials) plus, when NB > 16384,
+ * sparse_kv_topk_workspace_bytes(shape, k_blocks) (the top-k's chunk
+ * candidates, placed right after the partials: such rows first run
+ * sparse_kv_topk's chunk launch, then every workgroup of a row selects from
+ * the candidates); sparse_kv_workspace_bytes covers both.
+ * Limits: those of the three calls.
  */
 skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, const int32_t *seq_lens,
                                    int32_t k_blocks, int32_t sink_tokens, int32_t recent_tokens, int32_t capacity,
@@ -364,14 +368,15 @@ skv_status sparse_kv_select_attend(const skv_shape *shape, const float *scores, 
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments (minus workspace / workspace_bytes), same kernels and the
  * same results bit for bit as sparse_kv_select_attend with the same
- * num_splits.  The per-split partials go to a static device array of
+ * num_splits.  The per-split partials (and, past 16384 blocks, the top-k's
+ * chunk candidates) go to a static device array of
  * SKV_NOALLOC_SCRATCH_BYTES (8 MiB) that each GPU the library runs on holds
  * until the process ends; its address is looked up once per device on the
- * first call with that device current.  A call whose partials
- * (B*Hkv * splits * G * (D + 2) * 4 bytes) exceed it returns
+ * first call with that device current.  A call that needs more (the
+ * workspace size sparse_kv_select_attend would need) returns
  * SKV_ERR_SCRATCH before launching anything.  Nothing in the scratch needs
  * clearing (every workgroup writes its whole partial before the merge reads
- * it).  All calls on one GPU share that GPU's array: calls that overlap in
+ * it, every chunk its candidates before they are read).  All calls on one GPU share that GPU's array: calls that overlap in
  * time on one GPU (other streams, other host threads) race; enqueue them on
  * one stream.
  */

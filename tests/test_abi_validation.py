@@ -141,7 +141,14 @@ def test_select_attend(L):
         return L.sparse_kv_select_attend(s if s is not None else shape(), P, P, k, 0, 0, cap, P, P, P, P, P, P, P,
                                          P, P, P, P, P, P, src[0], src[1], 0, 0.1, splits, P, P, P, ws_bytes, NUL)
     assert call(src=(NUL, NUL)) == NULL                # the fused call always fetches on attend
-    assert call(shape(ctx=16 * 8193)) == UNSUPPORTED   # rows over 8192 blocks
+    assert call(shape(ctx=16 * 65537)) == UNSUPPORTED  # rows over 65536 blocks
+    # past 16384 blocks the workspace also holds the top-k's chunk candidates
+    long = B.make_shape(2, 8, 2, 64, 16 * 20000, "f32")
+    att = B.sparse_decode_attention_workspace_bytes(long, 8, 4)
+    tk = B.sparse_kv_topk_workspace_bytes(long, 8)
+    assert tk > 0
+    assert call(C.byref(long), splits=4, ws_bytes=att) == WORKSPACE
+    assert call(C.byref(long), splits=4, ws_bytes=att + tk - 1) == WORKSPACE
     assert call(k=16, cap=8) == CAPACITY
     assert call(splits=9) == SHAPE
     assert call(splits=4, ws_bytes=16) == WORKSPACE

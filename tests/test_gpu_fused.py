@@ -36,6 +36,14 @@ FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "
     ("tiny", dict(head_dim=128), 3, 0),
     ("llama8b_32k", dict(batch=2, n_q_heads=8, ctx=4096, budget=512), 3, 0),
     ("lookahead_1m", dict(ctx=16384), 3, 0),
+    # rows past 8192 blocks (32 keys per thread) and past 16384 (the top-k's
+    # chunk launch, then every workgroup selects from the candidates): Quest
+    # grown past 128K with sink / recent, ragged rows of 20000 blocks, the
+    # 1M-context rows of 65536 blocks
+    ("quest_128k", dict(batch=1, ctx=131072 + 16 * 3), 3, 0),
+    ("llama8b_32k", dict(batch=3, ctx=16 * 20000, budget=1024, capacity=100, ragged=True), 3, 0),
+    ("quest_128k", dict(batch=2, n_kv_heads=2, n_q_heads=8, ctx=16 * 40000 + 5 * 16), 3, 0),
+    ("lookahead_1m", {}, 2, 0),
 ])
 def test_fused_equals_separate_calls(name, kw, steps, splits):
     w = synth.WORKLOADS[name].scaled(steps=steps, **kw)

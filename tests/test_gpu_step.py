@@ -225,12 +225,21 @@ def test_quest_full_size_all_steps():
 
 
 @pytest.mark.timeout(900)
+def test_lookahead_1m_full_size_fused():
+    # the benchmark's path at full size (8 rows of 65536 blocks, 32 scoring
+    # query rows per kv head, matrix-core scoring): score, then the fused
+    # call (the top-k's chunk launch, selection + working-set update +
+    # attention with fetch on attend, merge + commit); all 8 steps, every
+    # row and head
+    run_workload(synth.WORKLOADS["lookahead_1m"], fused=True)
+
+
+@pytest.mark.timeout(900)
 def test_lookahead_1m_full_size_one_launch_select():
-    # the benchmark's path for rows over 8192 blocks at full size (8 rows of
-    # 65536 blocks, 32 scoring query rows per kv head, matrix-core scoring):
-    # score, the one-launch selection (top-k + working-set update), attention
-    # with fetch on attend; all 8 steps, every row and head
-    run_workload(synth.WORKLOADS["lookahead_1m"], select=True)
+    # the same workload through the selection call (the top-k's chunk
+    # launch, then selection + working-set update) and attention with fetch
+    # on attend; 4 steps, every row and head
+    run_workload(synth.WORKLOADS["lookahead_1m"], steps=4, select=True)
 
 
 @pytest.mark.timeout(900)

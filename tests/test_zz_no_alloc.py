@@ -2,9 +2,11 @@
 split partials in the library's static device scratch) equals the fused
 call with a caller workspace (sparse_kv_select_attend) bit for bit: the
 selection, the lists, the working-set state, the pool, the output and the
-lse, step after step.  Two calls in a row, the second with a smaller input
-(the scratch keeps the first call's contents), then a call whose partials
-would not fit, refused on the host with SKV_ERR_SCRATCH.  Through the C ABI.
+lse, step after step.  Calls in a row, each with a smaller input than the
+one before (the scratch keeps the previous call's contents; the first also
+holds the long-row top-k's chunk candidates after the partials), then a call
+whose partials would not fit, refused on the host with SKV_ERR_SCRATCH.
+Through the C ABI.
 """
 import numpy as np
 import pytest
@@ -31,7 +33,8 @@ def _noalloc(buf, q, lens, K, V):
 
 
 def test_noalloc_equals_the_workspace_call_on_two_calls_in_a_row():
-    cases = [("llama8b_32k", dict(batch=4, ctx=8192, budget=1024, capacity=80), 3),
+    cases = [("llama8b_32k", dict(batch=1, ctx=16 * 20000, budget=1024, capacity=80), 2),  # chunk candidates too
+             ("llama8b_32k", dict(batch=4, ctx=8192, budget=1024, capacity=80), 3),
              ("quest_128k", dict(batch=1, n_kv_heads=4, n_q_heads=16, ctx=4096), 2)]  # smaller second input
     for name, kw, steps in cases:
         w = synth.WORKLOADS[name].scaled(steps=steps, **kw)

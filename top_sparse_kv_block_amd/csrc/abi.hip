@@ -260,10 +260,11 @@ SKV_API size_t sparse_kv_workspace_bytes(const skv_shape *shape, int32_t k_block
         return 0;
     const int att = num_splits == 0 ? skv::attention_auto_splits(d.rows(), k_blocks) : num_splits;
     const int fused = num_splits == 0 ? skv::fused_auto_splits(d, k_blocks) : num_splits;
-    size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, att > fused ? att : fused);
+    size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, att);
     if (k_blocks <= d.NB && d.NB <= skv::kMaxTopkBlocks) {
-        const size_t tk = skv::long_row_ws_bytes(d, k_blocks);
-        need = tk > need ? tk : need;
+        // the fused call's (partials, then the top-k's candidates) covers the top-k's own
+        const size_t f = skv::fused_ws_bytes(d, k_blocks, fused);
+        need = f > need ? f : need;
     }
     return need;
 }
@@ -318,7 +319,7 @@ skv_status check_select_attend(const skv_shape *shape, const float *scores, cons
     if (!scores || !seq_lens || !sel_blocks || !sel_count || !slot_block || !slot_stamp || !clock || !sel_slot ||
         !sel_hit || !miss_block || !miss_slot || !miss_count || !q || !pool_k || !pool_v || !src_k || !src_v || !out)
         return SKV_ERR_NULL;
-    if (d.NB > skv::kMaxFusedBlocks)
+    if (d.NB > skv::kMaxTopkBlocks)
         return SKV_ERR_UNSUPPORTED;
     if (k_blocks < 1 || k_blocks > d.NB || k_blocks > skv::kMaxK || sink_tokens < 0 || recent_tokens < 0 ||
         capacity < 1 || num_splits < 0 || num_splits > k_blocks || num_splits > skv::kMaxSplits)
@@ -383,7 +384,7 @@ SKV_API skv_status sparse_kv_select_attend(const skv_shape *shape, const float *
                                         num_splits, out, d, splits);
     if (st != SKV_OK)
         return st;
-    const size_t need = skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits);
+    const size_t need = skv::fused_ws_bytes(d, k_blocks, splits);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return SKV_ERR_WORKSPACE;
     skv::FusedArgs f{scores,   seq_lens,  k_blocks,  sink_tokens, recent_tokens, capacity,   sel_blocks,
@@ -410,7 +411,7 @@ SKV_API skv_status sparse_kv_select_attend_noalloc(const skv_shape *shape, const
                                         num_splits, out, d, splits);
     if (st != SKV_OK)
         return st;
-    if (skv::attention_ws_bytes(d.rows(), d.G(), d.D, splits) > (size_t)SKV_NOALLOC_SCRATCH_BYTES)
+    if (skv::fused_ws_bytes(d, k_blocks, splits) > (size_t)SKV_NOALLOC_SCRATCH_BYTES)
         return SKV_ERR_SCRATCH;
     void *ws = nullptr;
     hipError_t e = scratch_on_current_device(&ws);

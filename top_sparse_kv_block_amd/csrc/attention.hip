@@ -626,9 +626,14 @@ template <typename E, int D, int GMAX> constexpr int fused_depth() {
     }
 }
 
-template <typename E, int D, int GMAX, int KPT>
-__global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>())) void select_attend_kernel(
-    const float *__restrict__ scores, const int32_t *__restrict__ seq_lens, int k, int sink, int recent, int C,
+// LONG: rows over 16384 blocks, whose top-k's first launch
+// (topk_chunk_kernel) has left each chunk's candidates in `cand`; every
+// workgroup of the row selects from those (KPT candidates per thread) and
+// plans with cache_plan_row.
+template <typename E, int D, int GMAX, int KPT, bool LONG>
+__global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 32 : KPT>())) void select_attend_kernel(
+    const float *__restrict__ scores, const float *__restrict__ cand, int chunk_blocks, int nchunks,
+    const int32_t *__restrict__ seq_lens, int k, int sink, int recent, int C,
     int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count, const int32_t *__restrict__ slot_block,
     const uint32_t *__restrict__ slot_stamp, int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit,
     int32_t *__restrict__ miss_block, int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count,
@@ -653,7 +658,9 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
                    part, out, lse);
     constexpr int depth = fused_min_waves<E, D, GMAX, KPT>() == 4 ? 1 : fused_depth<E, D, GMAX>();
 
-    const uint64_t take = topk_take<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, tsc);
+    uint64_t take = 0;
+    if constexpr (!LONG)
+        take = topk_take<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, tsc);
     // once the hits are known, each wave loads its first block (a hit from
     // its pool slot, a miss from the source) so that the load is in flight
     // while the rest of the plan is worked out
@@ -672,8 +679,17 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, KPT>()))
             }
         }
     };
-    int nn, bad;
-    const int nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad, load_first);
+    int nn, bad, nm;
+    if constexpr (LONG) {
+        const size_t nc = (size_t)nchunks * long_row_stride(k);
+        const float *wrow = cand + (size_t)row * 2 * nc;
+        const int ncand = (min(nb_of(len), NB) + chunk_blocks - 1) / chunk_blocks * long_row_stride(k);
+        nn = long_row_select<kAttnThreads, KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), ncand, len, NB,
+                                                k, sink, recent, sS, tsc);
+        nm = cache_plan_row<kAttnThreads>(sS, nn, C, NB, regs, cs, bad);
+    } else {
+        nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad, load_first);
+    }
     if (split == 0) {
         for (int i = threadIdx.x; i < k; i += kAttnThreads)
             sel_blocks[(size_t)row * k + i] = sS[i];
@@ -813,6 +829,8 @@ int attention_auto_splits(int rows, int k) {
 // The fused call redoes the row's top-k and plan in every workgroup, so it
 // prefers as many workgroups as are resident at once (one or two per CU,
 // see fused_min_waves), each wave streaming several blocks.
+static_assert(kAttnThreads == kLongRowThreads, "the fused kernel runs the long-row selection's second step");
+
 int fused_waves_per_simd(const Dims &d) {
     return (d.dtype == 1 && attn_matrix_cores<BF16>() && d.G() <= 4 && d.NB <= kAttnThreads * 8) ? 4 : 2;
 }
@@ -871,13 +889,26 @@ hipError_t launch_attention(const Dims &d, const AttnArgs &a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------- fused
-template <typename E, int D, int GMAX, int KPT>
+size_t fused_ws_bytes(const Dims &d, int k, int splits) {
+    return attention_ws_bytes(d.rows(), d.G(), d.D, splits) + long_row_ws_bytes(d, k);
+}
+
+template <typename E, int D, int GMAX, int KPT, bool LONG>
 static hipError_t fused_t(const Dims &d, const FusedArgs &f, hipStream_t st) {
     const int per = (f.k + f.splits - 1) / f.splits;
     const float scale_log2 = f.scale * 1.4426950408889634f;
     float *part = (float *)f.ws;
-    hipLaunchKernelGGL((select_attend_kernel<E, D, GMAX, KPT>), dim3(f.splits, d.rows()), dim3(kAttnThreads), 0, st,
-                       f.scores, f.seq_lens, f.k, f.sink, f.recent, f.cap, f.sel_blocks, f.sel_count, f.slot_block,
+    // rows over 16384 blocks: the chunk candidates follow the partials
+    float *cand = (float *)((char *)f.ws + attention_ws_bytes(d.rows(), d.G(), d.D, f.splits));
+    const int ch = LONG ? long_row_chunk(d.NB, f.k) : 0, nch = LONG ? long_row_chunks(d.NB, f.k) : 0;
+    if (LONG) {
+        hipError_t e = launch_topk_chunks(d, f.scores, f.seq_lens, f.k, f.sink, f.recent, cand, st);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((select_attend_kernel<E, D, GMAX, KPT, LONG>), dim3(f.splits, d.rows()), dim3(kAttnThreads), 0,
+                       st, f.scores, cand, ch, nch, f.seq_lens, f.k, f.sink, f.recent, f.cap, f.sel_blocks,
+                       f.sel_count, f.slot_block,
                        f.slot_stamp, f.sel_slot, f.sel_hit, f.miss_block, f.miss_slot, f.miss_count,
                        (const uint8_t *)f.q, (uint8_t *)f.pool_k, (uint8_t *)f.pool_v, (const uint8_t *)f.src_k,
                        (const uint8_t *)f.src_v, d.Hq, d.Hkv, d.T, f.splits, per, scale_log2, part, f.out, f.lse);
@@ -893,10 +924,23 @@ static hipError_t fused_t(const Dims &d, const FusedArgs &f, hipStream_t st) {
 template <typename E, int D, int GMAX>
 static hipError_t fused_k(const Dims &d, const FusedArgs &f, hipStream_t st) {
     if (d.NB <= kAttnThreads * 4)
-        return fused_t<E, D, GMAX, 4>(d, f, st);
+        return fused_t<E, D, GMAX, 4, false>(d, f, st);
     if (d.NB <= kAttnThreads * 8)
-        return fused_t<E, D, GMAX, 8>(d, f, st);
-    return fused_t<E, D, GMAX, 16>(d, f, st);
+        return fused_t<E, D, GMAX, 8, false>(d, f, st);
+    if (d.NB <= kAttnThreads * 16)
+        return fused_t<E, D, GMAX, 16, false>(d, f, st);
+    if (d.NB <= kAttnThreads * 32)
+        return fused_t<E, D, GMAX, 32, false>(d, f, st);
+    switch (long_row_kpt(d, f.k)) {  // phase B keys per thread (kAttnThreads == kLongRowThreads)
+    case 4:
+        return fused_t<E, D, GMAX, 4, true>(d, f, st);
+    case 8:
+        return fused_t<E, D, GMAX, 8, true>(d, f, st);
+    case 16:
+        return fused_t<E, D, GMAX, 16, true>(d, f, st);
+    default:
+        return fused_t<E, D, GMAX, 32, true>(d, f, st);
+    }
 }
 
 template <typename E, int D>

@@ -53,6 +53,12 @@ constexpr int kScoreThreads = 64 * kScoreWaves;
 constexpr int kQuestWaves = 4;
 constexpr int kQuestThreads = 64 * kQuestWaves;
 constexpr int kQuestBlocksPerWave = 4;  // wave iterations, each BPL blocks
+// matrix-core Quest scan: one tile of 16 boxes per wave, two waves per
+// workgroup.  Measured on the 128K workload (32 rows x 8192 boxes, 134 MB):
+// 20.9 us with 2 waves, 21.1 with 1, 21.5 with 8, 22.4 with 4; two tiles per
+// wave 24.0; the A operand loaded straight from memory (64 bytes per box
+// per instruction) instead of through LDS 24.3-31.4.
+constexpr int kQuestMfmaWaves = 2;
 
 template <typename E, int D, int RMAX>
 __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uint8_t *__restrict__ q,
@@ -71,15 +77,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uin
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPT, tg = lane / LPT;
 
+    // unconditional loads: under a uniform branch each ends in a wait for
+    // all loads at the branch's join, which serialises them
     u32x4 qf[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
-        if (r < R) {
-            const int rq = r / G, g = r - rq * G;
-            qf[r] = load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + sub * E::EPL) * E::bytes);
-        } else {
-            qf[r] = u32x4{0, 0, 0, 0};
-        }
+        const int rr = min(r, R - 1);
+        const int rq = rr / G, g = rr - rq * G;
+        const u32x4 v = load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + sub * E::EPL) * E::bytes);
+        qf[r] = r < R ? v : u32x4{0, 0, 0, 0};
     }
     const int len = min(max(seq_lens[b], 0), T);
     const int nvalid = nb_of(len);
@@ -104,8 +110,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_kernel(const uin
             float best = -__builtin_inff();
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
-                if (r < R)
-                    best = fmaxf(best, group_sum<LPT>(dot_chunk<E>(kv[i], qf[r], 0.0f)));
+                const float v = group_sum<LPT>(dot_chunk<E>(kv[i], qf[r], 0.0f));
+                best = r < R ? fmaxf(best, v) : best;
             }
             if (n * 16 + i * TPL + tg < len)
                 m = fmaxf(m, best);
@@ -236,15 +242,17 @@ __global__ __launch_bounds__(kQuestThreads) void score_quest_kernel(const uint8_
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % LPT, bg = lane / LPT;
 
+    // the query rows are loaded unconditionally (rows past R repeat row R - 1
+    // and are zeroed afterwards): loads under a uniform branch each end in a
+    // wait for all loads at the branch's join, which serialised these loads
+    // and delayed the boxes' (27.1 against 21.x us per 128K scan)
     u32x4 qf[RMAX];
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
-        if (r < R) {
-            const int rq = r / G, g = r - rq * G;
-            qf[r] = load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + sub * E::EPL) * E::bytes);
-        } else {
-            qf[r] = u32x4{0, 0, 0, 0};
-        }
+        const int rr = min(r, R - 1);
+        const int rq = rr / G, g = rr - rq * G;
+        const u32x4 v = load16(q + ((((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D + sub * E::EPL) * E::bytes);
+        qf[r] = r < R ? v : u32x4{0, 0, 0, 0};
     }
     const int len = min(max(seq_lens[b], 0), T);
     const int nvalid = nb_of(len);
@@ -274,18 +282,139 @@ __global__ __launch_bounds__(kQuestThreads) void score_quest_kernel(const uint8_
         float best = -__builtin_inff();
 #pragma unroll
         for (int r = 0; r < RMAX; ++r) {
-            if (r < R) {
-                u32x4 corner;
+            // computed for every row, kept only for real ones (a select, not
+            // a branch: no wait at a join)
+            u32x4 corner;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t m = neg_mask<E>(qf[r][w]);
-                    corner[w] = (lo[i][w] & m) | (hi[i][w] & ~m);
-                }
-                best = fmaxf(best, group_sum<LPT>(dot_chunk<E>(corner, qf[r], 0.0f)));
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t m = neg_mask<E>(qf[r][w]);
+                corner[w] = (lo[i][w] & m) | (hi[i][w] & ~m);
             }
+            const float v = group_sum<LPT>(dot_chunk<E>(corner, qf[r], 0.0f));
+            best = r < R ? fmaxf(best, v) : best;
         }
         if (sub == 0 && n < n1)
             srow[n] = in ? best * scale : -__builtin_inff();
+    }
+}
+
+// Quest bound on the matrix cores (bf16).  Per element the bound takes
+// q*hi where q >= 0 and q*lo where q < 0, which is q+ * hi + q- * lo with
+// q+ = max(q, 0), q- = min(q, 0) (one of the two products is zero, and the
+// other is exact in fp32).  So a block's bound for query row r is one dot
+// product over 2D elements: the block's box as stored, [lo; hi], against
+// [q-; q+] of the row, and a tile of 16 blocks x 16 query rows is a plain
+// matrix product, 2D/32 v_mfma_f32_16x16x32_bf16 per tile.  Each wave reads
+// its tile of 16 boxes (16 x 4D bytes) with fully coalesced 16-byte lane
+// loads, stages it in its own LDS tile (rows padded by 16 bytes: both access
+// patterns free of bank conflicts) and reads the A operand (block l%16,
+// elements 32c + 8(l/16) .. +8) back from there; the B operand holds the
+// same elements of [q-; q+] for query row 16t + l%16, built once from q.
+// Lane l then holds the bounds of blocks 4(l/16) .. +4 for query row
+// 16t + l%16: the max over the real rows is a DPP reduction within each
+// 16-lane row.  The vector kernel above spent as much time on its
+// per-element selects and lane reductions as on its loads.
+template <int D, int NT>
+__global__ __launch_bounds__(64 * kQuestMfmaWaves) void score_quest_mfma_kernel(const uint8_t *__restrict__ q,
+                                                               const uint8_t *__restrict__ meta,
+                                                               const int32_t *__restrict__ seq_lens,
+                                                               float *__restrict__ scores, int Hq, int Hkv, int NQ,
+                                                               int T, int NB, float scale) {
+    constexpr int KCH = 2 * D / 32;    // MFMA steps over the 2D elements of a box
+    constexpr int BB = 4 * D;          // bytes of one box (lo and hi, bf16)
+    constexpr int ROW = BB + 16;       // padded LDS row
+    constexpr int LOADS = 16 * BB / 1024;  // 16-byte lane loads per tile
+    constexpr int LPB = BB / 16;       // lanes per box in the coalesced layout
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kQuestMfmaWaves][16 * ROW];
+    int row, wgp;
+    xcd_row_part(row, wgp);
+    const int b = row / Hkv, j = row - b * Hkv;
+    const int G = Hq / Hkv;
+    const int R = NQ * G;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, rsub = lane >> 4;
+    uint8_t *my = tile[wave];
+
+    // B operand: element e = 32c + 8*rsub + i of [q-; q+] for query row
+    // 16t + col (rows past R: zeros, masked below); unconditional loads
+    u32x4 qf[NT][KCH];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int r = 16 * t + col;
+        const int rr = min(r, R - 1);
+        const int rq = rr / G, g = rr - rq * G;
+        const uint8_t *qr = q + (((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D * 2;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int e = 32 * c + 8 * rsub;  // e < D: q- (pairs with lo), else q+ (hi)
+            const u32x4 v = load16(qr + (e % D) * 2);
+            u32x4 w;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t m = ((v[x] & 0x80008000u) >> 15) * 0xffffu;  // negative halves
+                w[x] = r < R ? (e < D ? (v[x] & m) : (v[x] & ~m)) : 0u;
+            }
+            qf[t][c] = w;
+        }
+    }
+    const int len = min(max(seq_lens[b], 0), T);
+    const int nvalid = nb_of(len);
+    const uint8_t *mrow = meta + (size_t)row * NB * BB;
+    float *srow = scores + (size_t)row * NB;
+    const int n0 = (wgp * kQuestMfmaWaves + wave) * 16;  // this wave's tile of 16 boxes
+    if (n0 >= NB)
+        return;
+    if (n0 >= nvalid) {  // uniform: no valid block in the tile
+        if (lane < 16 && n0 + lane < NB)
+            srow[n0 + lane] = -__builtin_inff();
+        return;
+    }
+    u32x4 kv[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int bl = (i * 64 + lane) / LPB;  // box of this lane's 16 bytes
+        const int nb = min(n0 + bl, NB - 1);   // a partial last tile re-reads the row's last box
+        kv[i] = load_nt(mrow + (size_t)nb * BB + ((i * 64 + lane) % LPB) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int bl = (i * 64 + lane) / LPB;
+        *reinterpret_cast<u32x4 *>(my + bl * ROW + ((i * 64 + lane) % LPB) * 16) = kv[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    u32x4 af[KCH];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+        af[c] = *reinterpret_cast<const u32x4 *>(my + col * ROW + c * 64 + rsub * 16);
+    float m[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[c]),
+                                                          __builtin_bit_cast(bf16x8, qf[t][c]), st, 0, 0, 0);
+        if (16 * t + col < R) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m[i] = fmaxf(m[i], st[i]);
+        }
+    }
+    // max over the 16 query-row lanes of each 16-lane row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR8>(m[i]));
+        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR4>(m[i]));
+        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR2>(m[i]));
+        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR1>(m[i]));
+    }
+    if (col == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = n0 + 4 * rsub + i;
+            if (n < NB)
+                srow[n] = n < nvalid ? m[i] * scale : -__builtin_inff();
+        }
     }
 }
 
@@ -480,10 +609,30 @@ static hipError_t quest_t(const Dims &d, const void *q, int nq, const void *meta
     return hipGetLastError();
 }
 
+template <int D, int NT>
+static hipError_t quest_mfma_t(const Dims &d, const void *q, int nq, const void *meta, const int32_t *lens,
+                               float scale, float *scores, hipStream_t st) {
+    const int per_wg = kQuestMfmaWaves * 16;
+    dim3 grid((d.NB + per_wg - 1) / per_wg, d.rows());
+    hipLaunchKernelGGL((score_quest_mfma_kernel<D, NT>), grid, dim3(64 * kQuestMfmaWaves), 0, st, (const uint8_t *)q,
+                       (const uint8_t *)meta, lens, scores, d.Hq, d.Hkv, nq, d.T, d.NB, scale);
+    return hipGetLastError();
+}
+
+// bf16 boxes take the matrix-core kernel (the A/B build sends them to the
+// vector kernel, as for the block max).
 template <typename E, int D>
 static hipError_t quest_r(const Dims &d, const void *q, int nq, const void *meta, const int32_t *lens, float scale,
                           float *scores, hipStream_t st) {
     const int R = nq * d.G();
+#ifdef SKV_AB_VALU_BF16
+    constexpr bool kMatrixCores = false;
+#else
+    constexpr bool kMatrixCores = E::bytes == 2;
+#endif
+    if constexpr (kMatrixCores)
+        return R <= 16 ? quest_mfma_t<D, 1>(d, q, nq, meta, lens, scale, scores, st)
+                       : quest_mfma_t<D, 2>(d, q, nq, meta, lens, scale, scores, st);
     if (R <= 4)
         return quest_t<E, D, 4>(d, q, nq, meta, lens, scale, scores, st);
     if (R <= 8)

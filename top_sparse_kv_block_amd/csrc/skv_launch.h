@@ -86,10 +86,12 @@ constexpr int kMaxK = 1024;
 constexpr int kMaxCapacity = 1024;
 constexpr int kMaxGroup = 16;  // G for attention
 constexpr int kMaxSplits = 128;
-constexpr int kMaxFusedBlocks = 8192;  // NB limit of the fused select -> attend call
 
 int attention_auto_splits(int rows, int k);
 int fused_auto_splits(const Dims &d, int k);
 size_t attention_ws_bytes(int rows, int G, int D, int splits);
+// Workspace of the fused call: the partials, then (rows over 16384 blocks)
+// the top-k's chunk candidates.
+size_t fused_ws_bytes(const Dims &d, int k, int splits);
 
 }  // namespace skv

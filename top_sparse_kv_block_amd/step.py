@@ -79,8 +79,9 @@ class LayerBuffers:
         self.lse = torch.empty(b, hq, dtype=torch.float32, device=device)
         self.splits = cfg.num_splits or B.sparse_decode_attention_splits(self.shape, k)
         self.fused_splits = cfg.num_splits or B.sparse_kv_select_attend_splits(self.shape, k)
-        ws = max(B.sparse_decode_attention_workspace_bytes(self.shape, k, self.splits),
-                 B.sparse_decode_attention_workspace_bytes(self.shape, k, self.fused_splits))
+        # one workspace for the attention and the fused call (partials and,
+        # past 16384 blocks, the top-k's chunk candidates)
+        ws = B.sparse_kv_workspace_bytes(self.shape, k, cfg.num_splits)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
         # the top-k's own workspace (rows over 16384 blocks), apart from the
         # attention's so that a selection may run on another stream
@@ -278,8 +279,7 @@ def decode_step(buf: LayerBuffers, q, score_q, keys_or_meta, seq_lens, src_k, sr
     it reads them (fetch_on_attend, the default: one read and one write per
     missed block) or by the cache update's own copy pass.  fused=True runs
     stages 2-4 as the single select-attend call, select=True stages 2-3 as
-    one launch (same results either way; rows over 8192 blocks exceed the
-    fused call).
+    one launch (same results either way).
     """
     buf.score(score_q, keys_or_meta, seq_lens, stream)
     if fused:
