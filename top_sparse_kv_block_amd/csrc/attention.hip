@@ -649,6 +649,11 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     xcd_row_part(row, split);
     const int b = row / Hkv, j = row - b * Hkv;
     const int NB = T / 16;
+    // the row's scores first: their loads need neither the length nor the
+    // slot table, and run while the rest is set up
+    TopkScores<LONG ? 1 : KPT> pre;
+    if constexpr (!LONG)
+        topk_load<KPT>(scores + (size_t)row * NB, NB, pre);
     const int len = min(max(seq_lens[b], 0), T);
     SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
     load_slots<kAttnThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
@@ -660,7 +665,7 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
 
     uint64_t take = 0;
     if constexpr (!LONG)
-        take = topk_take<kAttnThreads, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, tsc);
+        take = topk_take_loaded<kAttnThreads, KPT>(pre, len, NB, k, sink, recent, tsc);
     // once the hits are known, each wave loads its first block (a hit from
     // its pool slot, a miss from the source) so that the load is in flight
     // while the rest of the plan is worked out

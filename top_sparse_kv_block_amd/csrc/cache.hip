@@ -155,6 +155,8 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
     __shared__ CacheScratch cs;
     __shared__ uint32_t sClock;
     const int row = blockIdx.x;
+    TopkScores<KPT> pre;  // issued first (no dependence on the length)
+    topk_load<KPT>(scores + (size_t)row * NB, NB, pre);
     const int len = min(max(seq_lens[row / Hkv], 0), T);
     int32_t *sb = slot_block + (size_t)row * C;
     uint32_t *ss = slot_stamp + (size_t)row * C;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(THREADS) void select_kernel(
     load_slots<THREADS>(regs, C, sb, ss);
     select_plan_clear<THREADS>(cs, ps, k, C);  // published by the top-k's barriers
     int n, bad;
-    const uint64_t take = topk_take<THREADS, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, sc);
+    const uint64_t take = topk_take_loaded<THREADS, KPT>(pre, len, NB, k, sink, recent, sc);
     const int nm = select_plan_row<THREADS, KPT>(take, k, C, NB, regs, sS, cs, ps, n, bad, [](int) {});
     select_commit<THREADS>(row, k, C, n, nm, bad, sS, cs, sel_blocks, sel_count, sb, ss, clock, sel_slot, sel_hit,
                            miss_block, miss_slot, miss_count, sClock);

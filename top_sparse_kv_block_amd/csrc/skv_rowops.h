@@ -172,15 +172,55 @@ template <int THREADS, int KPT>
 __device__ __forceinline__ uint64_t select_take(const uint32_t (&key)[KPT], uint64_t cand, uint64_t forced, int need,
                                                 TopkScratch &sc);
 
+// A thread's KPT scores of a row (ids [t*KPT, t*KPT+KPT)), loaded without
+// reading the row's length: the loads depend only on the row pointer and
+// NB, so a kernel can issue them first and let their latency run under its
+// other set-up (the length and everything before the top-k).  Ids past the
+// valid length are masked when the keys are formed.  (A load under a branch
+// on the length waited for the length first, and each scalar load for the
+// one before it.)
+template <int KPT> struct TopkScores {
+    float v[KPT];
+};
+
+template <int KPT>
+__device__ __forceinline__ void topk_load(const float *__restrict__ srow, int NB, TopkScores<KPT> &L) {
+    const int base = threadIdx.x * KPT;
+    if constexpr (KPT % 4 == 0) {
+        if ((NB & 3) == 0) {  // uniform
+            // 16-byte loads (a quarter of the instructions and cache lines
+            // touched), the index clamped into the row: a group past the end
+            // reads the row's last four scores, which its masked ids ignore.
+            // (The empty asm keeps the compiler from merging this form with
+            // the scalar one below into scalar loads.)
+            asm volatile("" ::: "memory");
+            u32x4 w[KPT / 4];
+#pragma unroll
+            for (int u = 0; u < KPT / 4; ++u)
+                __builtin_memcpy(&w[u], srow + min(base + 4 * u, NB - 4), 16);
+#pragma unroll
+            for (int u = 0; u < KPT / 4; ++u)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    L.v[4 * u + x] = __uint_as_float(w[u][x]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+        L.v[m] = srow[min(base + m, NB - 1)];
+}
+
 // Per-row selection under the budget (sink + recent blocks forced, the rest
 // by (score desc, id asc)) as bits: thread t owns ids [t*KPT, t*KPT+KPT) and
 // bit m of the result admits id t*KPT + m.  Up to four 8-bit radix passes
 // over order-preserving keys find the key of the last admitted block (ties
 // at the threshold go to the lowest ids).  A row with at most k valid blocks
-// takes all of them without reading its scores.  Contains barriers.
+// takes all of them without looking at its scores.  L: the thread's scores
+// from topk_load.  Contains barriers.
 template <int THREADS, int KPT>
-__device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
-                              TopkScratch &sc) {
+__device__ __forceinline__ uint64_t topk_take_loaded(const TopkScores<KPT> &L, int len, int NB, int k, int sink,
+                                                     int recent, TopkScratch &sc) {
     const int tid = threadIdx.x;
     const int nvalid = min(nb_of(len), NB);
     if (nvalid <= k) {
@@ -198,7 +238,8 @@ __device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, in
     uint32_t key[KPT];
     uint64_t cand = 0, forced = 0;
     const int base = tid * KPT;
-    auto classify = [&](int m, float v) {
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
         const int i = base + m;
         key[m] = 0;
         if (i < nvalid) {
@@ -206,48 +247,19 @@ __device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, in
                 forced |= 1ull << m;
             } else {
                 cand |= 1ull << m;
-                key[m] = order_key(v);
+                key[m] = order_key(L.v[m]);
             }
         }
-    };
-    if constexpr ((KPT == 4 || KPT >= 16) && KPT % 4 == 0) {
-        // 16-byte loads: a quarter of the load instructions and cache lines
-        // touched (measured: 1.4% on the whole 32K step at 4 keys per
-        // thread; at 8 the vector form spills in the fused kernel).  With a
-        // 16-byte aligned row of NB % 4 == 0 blocks (uniform) the loads are
-        // unconditional, the index clamped into the row and ids past the
-        // valid length masked afterwards, so all of a thread's loads are in
-        // flight at once (a branch around each one makes the compiler wait
-        // for it before the next).
-        const bool vec = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) && (NB & 3) == 0;
-        if (vec) {
-            float4 f[KPT / 4];
-#pragma unroll
-            for (int u = 0; u < KPT / 4; ++u)
-                f[u] = *reinterpret_cast<const float4 *>(srow + min(base + 4 * u, NB - 4));
-#pragma unroll
-            for (int u = 0; u < KPT / 4; ++u) {
-                classify(4 * u, f[u].x);
-                classify(4 * u + 1, f[u].y);
-                classify(4 * u + 2, f[u].z);
-                classify(4 * u + 3, f[u].w);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < KPT / 4; ++u) {
-                const int i = base + 4 * u;
-                classify(4 * u, i < nvalid ? srow[i] : 0.0f);
-                classify(4 * u + 1, i + 1 < nvalid ? srow[i + 1] : 0.0f);
-                classify(4 * u + 2, i + 2 < nvalid ? srow[i + 2] : 0.0f);
-                classify(4 * u + 3, i + 3 < nvalid ? srow[i + 3] : 0.0f);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < KPT; ++m)
-            classify(m, base + m < nvalid ? srow[base + m] : 0.0f);
     }
     return select_take<THREADS, KPT>(key, cand, forced, need, sc);
+}
+
+template <int THREADS, int KPT>
+__device__ __forceinline__ uint64_t topk_take(const float *__restrict__ srow, int len, int NB, int k, int sink,
+                                              int recent, TopkScratch &sc) {
+    TopkScores<KPT> L;
+    topk_load<KPT>(srow, NB, L);
+    return topk_take_loaded<THREADS, KPT>(L, len, NB, k, sink, recent, sc);
 }
 
 // The admitted bits of a thread's KPT keys: every forced key, and the `need`
@@ -310,9 +322,9 @@ __device__ __forceinline__ int topk_emit(uint64_t take, int k, int32_t *out, uin
     return (int)min(tot, (uint32_t)k);
 }
 
-// topk_take + topk_emit: the row's selection, ascending, in out[0, k).
+// topk_take_loaded + topk_emit: the row's selection, ascending, in out[0, k).
 template <int THREADS, int KPT>
-__device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent, int32_t *out,
+__device__ int topk_row(const TopkScores<KPT> &L, int len, int NB, int k, int sink, int recent, int32_t *out,
                         TopkScratch &sc) {
     const int tid = threadIdx.x;
     const int nvalid = min(nb_of(len), NB);
@@ -322,7 +334,7 @@ __device__ int topk_row(const float *__restrict__ srow, int len, int NB, int k, 
         __syncthreads();
         return nvalid;
     }
-    const uint64_t take = topk_take<THREADS, KPT>(srow, len, NB, k, sink, recent, sc);
+    const uint64_t take = topk_take_loaded<THREADS, KPT>(L, len, NB, k, sink, recent, sc);
     return topk_emit<THREADS, KPT>(take, k, out, sc.wsum, [](uint32_t, uint64_t) {});
 }
 

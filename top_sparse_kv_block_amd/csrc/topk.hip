@@ -27,9 +27,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(const float *__restrict__
                                                             int32_t *__restrict__ sel_count) {
     __shared__ TopkScratch sc;
     const int row = blockIdx.x;
+    TopkScores<KPT> pre;  // issued before the length is known
+    topk_load<KPT>(scores + (size_t)row * NB, NB, pre);
     const int len = min(max(seq_lens[row / Hkv], 0), T);
-    const int n = topk_row<THREADS, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent,
-                                              sel_blocks + (size_t)row * k, sc);
+    const int n = topk_row<THREADS, KPT>(pre, len, NB, k, sink, recent, sel_blocks + (size_t)row * k, sc);
     if (threadIdx.x == 0)
         sel_count[row] = n;
 }
