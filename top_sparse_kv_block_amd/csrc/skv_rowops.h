@@ -56,18 +56,16 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 struct TopkScratch {
-    uint32_t hist[3][256];  // passes rotate three buffers (see radix_select)
+    uint32_t hist[2][256];  // passes alternate buffers, so clearing needs no barrier of its own
     uint32_t wsum[16];
     uint32_t wlo[16], whi[16];  // per-wave key range
+    uint32_t digit, remaining, n_tau;
 };
 
-// Every wave finds the digit bin holding the `remaining`-th largest key of
-// the pass from the complete histogram: lane l reads bins 255-4l .. 252-4l,
-// a DPP scan adds the lanes, and the one lane whose bins hold that rank
-// broadcasts the digit, the rank left inside its bin and the bin's count.
-// The results are wave-uniform and equal in every wave.
-__device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remaining, uint32_t &digit,
-                                           uint32_t &rem_out, uint32_t &n_bin) {
+// Wave 0 finds the digit bin holding the `remaining`-th largest key of the
+// pass: lane l scans bins 255-4l .. 252-4l, a DPP scan adds the lanes.
+// Writes the digit, the rank left inside its bin and the bin's count.
+__device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remaining, TopkScratch &sc) {
     const int lane = threadIdx.x & 63;
     uint32_t c[4], t = 0;
 #pragma unroll
@@ -76,39 +74,28 @@ __device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remain
         t += c[u];
     }
     uint32_t run = wave_incl_scan(t) - t;  // keys in higher bins
-    int hit = -1;
-    uint32_t r = 0, n = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        if (hit < 0 && run < remaining && remaining <= run + c[u]) {
-            hit = u;
-            r = remaining - run;
-            n = c[u];
+        if (run < remaining && remaining <= run + c[u]) {
+            sc.digit = 255u - (uint32_t)(4 * lane + u);
+            sc.remaining = remaining - run;
+            sc.n_tau = c[u];
         }
         run += c[u];
     }
-    const uint64_t b = __builtin_amdgcn_ballot_w64(hit >= 0);  // one lane (1 <= remaining <= keys counted)
-    const int src = (int)__builtin_ctzll(b);
-    digit = 255u - (uint32_t)(4 * src + __builtin_amdgcn_readlane(hit, src));
-    rem_out = (uint32_t)__builtin_amdgcn_readlane((int)r, src);
-    n_bin = (uint32_t)__builtin_amdgcn_readlane((int)n, src);
 }
 
 // Radix select: the key of the `need`-th largest of the keys flagged in
 // `cand` (KPT per thread; need >= 1 and at most the number of flagged keys).
 // Up to four 8-bit passes over an LDS histogram, on the keys minus the
-// smallest flagged key.  One barrier per pass: every wave reads the whole
-// histogram and picks the digit itself, and the histograms rotate over
-// three buffers, so the one a pass clears was last read two passes earlier,
-// before the barrier of the previous pass.  Returns the key; `remaining` =
-// how many keys equal to it are admitted, `n_tau` = how many flagged keys
-// equal it.  The passes stop early once the bin holding the need-th key is
-// admitted whole (its count equals the rank still needed): the returned
-// key is then the smallest one with the decided leading bits, every flagged
-// key at or above it is admitted, and remaining == n_tau (no tie to break),
-// so the admitted set is the one the full passes give.  The last pick's
-// reads are not followed by a barrier: the caller passes one before anything
-// writes sc.hist again (another radix_select included).
+// smallest flagged key; each pass needs two barriers (the histogram buffers
+// alternate, so clearing the next one needs none).  Returns the key;
+// `remaining` = how many keys equal to it are admitted, `n_tau` = how many
+// flagged keys equal it.  The passes stop early once the bin holding the
+// need-th key is admitted whole (its count equals the rank still needed):
+// the returned key is then the smallest one with the decided leading bits,
+// every flagged key at or above it is admitted, and remaining == n_tau
+// (no tie to break), so the admitted set is the one the full passes give.
 template <int THREADS, int KPT>
 __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uint64_t cand, uint32_t need,
                                                  TopkScratch &sc, uint32_t &remaining_out, uint32_t &n_tau_out) {
@@ -146,7 +133,7 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
     for (int pass = 0; pass < passes; ++pass) {
         const int shift = max(top - 8 * (pass + 1), 0);
         const uint32_t dmask = (1u << (top - 8 * pass - shift)) - 1u;
-        uint32_t *hist = sc.hist[pass % 3];
+        uint32_t *hist = sc.hist[pass & 1];
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
             const uint32_t kr = key[m] - lo;
@@ -154,13 +141,16 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
                 atomicAdd(&hist[(kr >> shift) & dmask], 1u);
         }
         for (int i = tid; i < 256; i += THREADS)
-            sc.hist[(pass + 1) % 3][i] = 0;  // last read two passes ago
+            sc.hist[(pass + 1) & 1][i] = 0;  // last read by the previous pass's pick
         lds_barrier();
-        uint32_t digit;
-        pick_digit(hist, remaining, digit, remaining, n_tau);  // n_tau after the last pass: keys equal to tau
-        prefix |= digit << shift;
+        if (tid < 64)
+            pick_digit(hist, remaining, sc);
+        lds_barrier();
+        prefix |= sc.digit << shift;
         mask |= dmask << shift;
-        if (n_tau == remaining)  // uniform
+        remaining = sc.remaining;
+        n_tau = sc.n_tau;  // after the last pass: the keys equal to tau
+        if (n_tau == remaining)  // uniform (read from LDS after the barrier)
             break;
     }
     remaining_out = remaining;
@@ -168,6 +158,12 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
     return prefix + lo;
 }
 
+// Per-row selection under the budget (sink + recent blocks forced, the rest
+// by (score desc, id asc)) as bits: thread t owns ids [t*KPT, t*KPT+KPT) and
+// bit m of the result admits id t*KPT + m.  Up to four 8-bit radix passes
+// over order-preserving keys find the key of the last admitted block (ties
+// at the threshold go to the lowest ids).  A row with at most k valid blocks
+// takes all of them without reading its scores.  Contains barriers.
 template <int THREADS, int KPT>
 __device__ __forceinline__ uint64_t select_take(const uint32_t (&key)[KPT], uint64_t cand, uint64_t forced, int need,
                                                 TopkScratch &sc);
