@@ -216,7 +216,8 @@ skv_status sparse_kv_topk(const skv_shape *shape, const float *scores, const int
  * attends, with separate list outputs.  It is an ordinary update (clock tick
  * and stamps included); layer l+1's own update then finds the shared blocks
  * resident.  The two calls on one layer's state must not overlap in time.
- * Limits: 1 <= k_blocks <= capacity <= 1024.
+ * Limits: 1 <= k_blocks <= capacity <= 1024; NB <= 2^21 (else
+ * SKV_ERR_UNSUPPORTED).
  */
 skv_status sparse_kv_cache_update(const skv_shape *shape, int32_t k_blocks, int32_t capacity,
                                   const int32_t *sel_blocks, const int32_t *sel_count,

@@ -77,8 +77,8 @@ def test_topk(L):
     assert topk(L, long, ws=C.c_void_p(0x1010), ws_bytes=need) == WORKSPACE
 
 
-def update(L, k=8, cap=16, src=(NUL, NUL), kind=0, pool=(P, P), sel=P, fn="sparse_kv_cache_update"):
-    args = [shape(), k, cap, sel, P]
+def update(L, k=8, cap=16, src=(NUL, NUL), kind=0, pool=(P, P), sel=P, fn="sparse_kv_cache_update", s=None):
+    args = [s if s is not None else shape(), k, cap, sel, P]
     if fn == "sparse_kv_cache_update_importance":
         args.append(P)
     args += [P, P, P, P, P, P, P, P, src[0], src[1], kind, pool[0], pool[1], NUL]
@@ -94,6 +94,7 @@ def test_cache_update(L, fn):
     assert update(L, kind=3, fn=fn) == SHAPE
     assert update(L, src=(P, NUL), fn=fn) == NULL      # K without V
     assert update(L, src=(P, P), pool=(NUL, P), fn=fn) == NULL  # fetch needs the pool
+    assert update(L, fn=fn, s=shape(ctx=16 * (2 ** 21 + 1))) == UNSUPPORTED  # block ids past 21 bits
 
 
 def test_importance_needs_scores(L):

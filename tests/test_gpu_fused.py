@@ -23,6 +23,11 @@ FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "
     ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 6, 0),
     ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 4, 5),
     ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 3, 32),
+    # one split per row: the fused kernel writes the output and commits the
+    # plan itself (no merge launch)
+    ("llama8b_32k", dict(batch=2, ctx=4096, budget=512), 4, 1),
+    ("quest_128k", dict(batch=2, ctx=8192), 4, 1),
+    ("lookahead_1m", dict(ctx=16 * 20000), 3, 1),
     ("llama8b_32k", dict(batch=3, ctx=2048 + 16 * 7, budget=256, capacity=40, ragged=True), 4, 0),
     ("quest_128k", dict(batch=2, ctx=8192), 4, 0),
     # rows just past 2048 and 4096 blocks: the 8- and 16-keys-per-thread variants

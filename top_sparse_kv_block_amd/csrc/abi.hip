@@ -115,7 +115,7 @@ static skv_status cache_update_impl(const skv_shape *shape, int32_t k_blocks, in
         return SKV_ERR_SHAPE;
     if (capacity < k_blocks)
         return SKV_ERR_CAPACITY;
-    if (capacity > skv::kMaxCapacity)
+    if (capacity > skv::kMaxCapacity || d.NB > skv::kMaxUpdateBlocks)
         return SKV_ERR_UNSUPPORTED;
     if (src_kind != SKV_SRC_DEVICE && src_kind != SKV_SRC_HOST_MAPPED)
         return SKV_ERR_SHAPE;

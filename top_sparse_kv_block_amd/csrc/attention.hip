@@ -634,8 +634,9 @@ template <typename E, int D, int GMAX, int KPT, bool LONG>
 __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 32 : KPT>())) void select_attend_kernel(
     const float *__restrict__ scores, const float *__restrict__ cand, int chunk_blocks, int nchunks,
     const int32_t *__restrict__ seq_lens, int k, int sink, int recent, int C,
-    int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count, const int32_t *__restrict__ slot_block,
-    const uint32_t *__restrict__ slot_stamp, int32_t *__restrict__ sel_slot, uint8_t *__restrict__ sel_hit,
+    int32_t *__restrict__ sel_blocks, int32_t *__restrict__ sel_count, int32_t *__restrict__ slot_block,
+    uint32_t *__restrict__ slot_stamp, uint32_t *__restrict__ clock, int32_t *__restrict__ sel_slot,
+    uint8_t *__restrict__ sel_hit,
     int32_t *__restrict__ miss_block, int32_t *__restrict__ miss_slot, int32_t *__restrict__ miss_count,
     const uint8_t *__restrict__ q, uint8_t *__restrict__ pool_k, uint8_t *__restrict__ pool_v,
     const uint8_t *__restrict__ src_k, const uint8_t *__restrict__ src_v, int Hq, int Hkv, int T, int splits,
@@ -645,6 +646,7 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     __shared__ CacheScratch cs;
     __shared__ PlanScratch<kAttnThreads> ps;
     __shared__ AttnSmem<D, GMAX> S;
+    __shared__ uint32_t sNow;
     int row, split;
     xcd_row_part(row, split);
     const int b = row / Hkv, j = row - b * Hkv;
@@ -695,6 +697,11 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     } else {
         nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad, load_first);
     }
+    // one workgroup per row commits its own plan after attending (no other
+    // workgroup reads the row's table); the clock's atomic goes out now
+    const bool commit_here = splits == 1 && !bad;  // uniform
+    if (commit_here && threadIdx.x == 0)
+        sNow = atomicAdd(&clock[row], 1u) + 1u;
     if (split == 0) {
         for (int i = threadIdx.x; i < k; i += kAttnThreads)
             sel_blocks[(size_t)row * k + i] = sS[i];
@@ -716,6 +723,17 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     a.i0 = split * per_split;
     a.i1 = bad ? a.i0 : min(a.i0 + per_split, nn);  // an invalid row attends nothing
     attn_body<E, D, GMAX, depth>(a, S, first);
+    if (commit_here) {
+        __syncthreads();
+        const uint32_t now = sNow;
+        for (int i = threadIdx.x; i < nn; i += kAttnThreads) {
+            const int s = cs.slot_of[i];
+            if (s >= 0 && s < C) {
+                slot_block[(size_t)row * C + s] = sS[i];
+                slot_stamp[(size_t)row * C + s] = now;
+            }
+        }
+    }
 }
 
 // One workgroup per row: merge the row's G heads over the splits (when
@@ -913,12 +931,12 @@ static hipError_t fused_t(const Dims &d, const FusedArgs &f, hipStream_t st) {
     }
     hipLaunchKernelGGL((select_attend_kernel<E, D, GMAX, KPT, LONG>), dim3(f.splits, d.rows()), dim3(kAttnThreads), 0,
                        st, f.scores, cand, ch, nch, f.seq_lens, f.k, f.sink, f.recent, f.cap, f.sel_blocks,
-                       f.sel_count, f.slot_block,
-                       f.slot_stamp, f.sel_slot, f.sel_hit, f.miss_block, f.miss_slot, f.miss_count,
-                       (const uint8_t *)f.q, (uint8_t *)f.pool_k, (uint8_t *)f.pool_v, (const uint8_t *)f.src_k,
-                       (const uint8_t *)f.src_v, d.Hq, d.Hkv, d.T, f.splits, per, scale_log2, part, f.out, f.lse);
+                       f.sel_count, f.slot_block, f.slot_stamp, f.clock, f.sel_slot, f.sel_hit, f.miss_block,
+                       f.miss_slot, f.miss_count, (const uint8_t *)f.q, (uint8_t *)f.pool_k, (uint8_t *)f.pool_v,
+                       (const uint8_t *)f.src_k, (const uint8_t *)f.src_v, d.Hq, d.Hkv, d.T, f.splits, per,
+                       scale_log2, part, f.out, f.lse);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
+    if (e != hipSuccess || f.splits == 1)  // one split per row: the kernel wrote out / lse and committed
         return e;
     hipLaunchKernelGGL(merge_commit_kernel, dim3(d.rows()), dim3(kAttnThreads), 0, st, (const float *)part, d.Hq,
                        d.Hkv, d.D, f.splits, f.out, f.lse, 1, f.k, f.cap, f.sel_blocks, f.sel_count, f.sel_slot,

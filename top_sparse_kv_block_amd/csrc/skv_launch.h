@@ -84,6 +84,7 @@ constexpr int kMaxQueryRows = 32;  // G * n_queries for scoring
 constexpr int kMaxTopkBlocks = 65536;
 constexpr int kMaxK = 1024;
 constexpr int kMaxCapacity = 1024;
+constexpr int kMaxUpdateBlocks = 1 << 21;  // NB limit of the working-set update (block ids in 21 key bits)
 constexpr int kMaxGroup = 16;  // G for attention
 constexpr int kMaxSplits = 128;
 

@@ -542,9 +542,11 @@ struct CacheScratch {
     int32_t slot_of[kMaxK];  // slot of S[i]
     uint8_t hit[kMaxK];
     int32_t miss_i[kMaxK];   // S index of miss m
-    uint64_t key[kMaxCapacity];  // LRU key of a candidate slot, ~0 otherwise
-    int32_t dup[kDupSet];    // block ids of the unselected occupied slots
+    uint64_t key[kMaxCapacity];  // eviction keys: cache_plan_row's candidate list (slot in the low bits);
+                                 // select_plan_row's candidate list
+    int32_t dup[kDupSet];    // block ids of the unselected occupied slots; then the slot of eviction rank r
     int wsum[16];
+    int n_cand;              // cache_plan_row's candidates
 };
 
 __device__ __forceinline__ int find_sorted(const int32_t *S, int n, int32_t x) {
@@ -599,6 +601,8 @@ template <int THREADS> __device__ __forceinline__ void cache_plan_clear(CacheScr
     const int nd = 1 << dup_set_bits(C);
     for (int i = threadIdx.x; i < nd; i += THREADS)
         cs.dup[i] = -1;
+    if (threadIdx.x == 0)
+        cs.n_cand = 0;
 }
 
 // Plans one step of the row's working set for the selection S[0, nn) (in
@@ -612,7 +616,7 @@ template <int THREADS> __device__ __forceinline__ void cache_plan_clear(CacheScr
 template <int THREADS>
 __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const SlotRegs<THREADS> &r, CacheScratch &cs,
                               int &bad_out, const float *__restrict__ importance = nullptr) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     constexpr int SPT = SlotRegs<THREADS>::SPT;
     // validation and hits in one round: the selection must be ascending and
     // in range and the table's ids in [-1, NB); each occupied slot looks its
@@ -627,13 +631,19 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
         if (v < 0 || v >= NB || (i > 0 && v <= S[i - 1]))
             bad = 1;
     }
-    // the same pass also stores each slot's eviction key: ~0 for a selected
-    // (taken) slot, else empty slots first by index, then occupied slots by
-    // (stamp, block) for LRU or, with `importance` (the row's scores of this
-    // step), by (score, block): the least important block goes first
+    // the same pass lists the eviction candidates (slots whose block is not
+    // selected) with their keys: empty slots first by index, then occupied
+    // ones by (stamp, block) for LRU or, with `importance` (the row's scores
+    // of this step), by (score, block): the least important block goes
+    // first.  Key bits: 1 | order (32) | block (21) | slot (10): the slot
+    // leaves the order of a valid table's keys unchanged (they differ in
+    // (order, block) already; the host refuses NB > 2^21); one list append
+    // per wave
 #pragma unroll
     for (int u = 0; u < SPT; ++u) {
         const int s = tid + u * THREADS;
+        bool cand = false;
+        uint64_t key = 0;
         if (s < C) {
             const int32_t blk = r.blk[u];
             if (blk < -1 || blk >= NB)
@@ -644,16 +654,26 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
             if (i < 0 && blk >= 0 && dup_set_add(cs.dup, dbits, blk))
                 bad = 1;
             const uint32_t order = importance && blk >= 0 && blk < NB ? order_key(importance[blk]) : r.stamp[u];
-            cs.key[s] = i >= 0 ? ~0ull
-                               : (blk < 0 ? (uint64_t)s
-                                          : ((1ull << 63) | ((uint64_t)order << 31) | (uint64_t)blk));
+            cand = i < 0;
+            key = blk < 0 ? (uint64_t)s
+                          : ((1ull << 63) | ((uint64_t)order << 31) | ((uint64_t)blk << 10) | (uint64_t)s);
+        }
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(cand);
+        if (bal) {  // uniform over the wave
+            const int first = (int)__builtin_ctzll(bal);
+            int c0 = 0;
+            if (lane == first)
+                c0 = atomicAdd(&cs.n_cand, (int)__builtin_popcountll(bal));
+            c0 = __builtin_amdgcn_readlane(c0, first);
+            if (cand)
+                cs.key[c0 + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull))] = key;
         }
     }
     if (__syncthreads_or(bad)) {
         bad_out = 1;
         return -1;
     }
-    // misses in ascending S order: thread t owns S indices [t*per, t*per+per)
+    // hit flags and miss counts of the selection indices a thread owns ...
     const int per = (nn + THREADS - 1) / THREADS;
     int cnt = 0;
     for (int u = 0; u < per; ++u) {
@@ -664,36 +684,25 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
             cnt += h ? 0 : 1;
         }
     }
-    // the compacted miss list is written between the scan's two barriers,
-    // so the victim pass below (other threads) reads it complete
-    int nm;
-    (void)wg_exclusive_scan_publish<THREADS, int>(cnt, cs.wsum, nm, [&](int pos, int) {
-        for (int u = 0; u < per; ++u) {
-            const int i = tid * per + u;
-            if (i < nn && !cs.hit[i])
-                cs.miss_i[pos++] = i;
-        }
-    });
-    // victims: candidate rank r < #misses takes miss r (keys of a valid table
-    // are distinct; the slot index breaks ties of a corrupt one).  Q lanes
-    // share a candidate, each counting over every Q-th slot (the Q lanes
-    // then read Q neighbouring keys: different LDS banks), so the loads of
-    // one thread stay few and independent.  (The keys were written before
-    // the barrier of the validation round.)
-    if (nm > 0) {
+    // ... and, in the same round, every candidate's eviction rank among the
+    // candidates (Q lanes per candidate, each counting over every Q-th list
+    // entry; the keys are distinct), the slot of rank r going to cs.dup[r]
+    // (the duplicate set is done with); candidates outnumber the misses since
+    // C >= k
+    int32_t *victim = cs.dup;
+    {
         constexpr int Q = THREADS >= 1024 ? 8 : (THREADS >= 512 ? 4 : 1);
-        for (int base = 0; base < C * Q; base += THREADS) {
+        const int nc = cs.n_cand;
+        for (int base = 0; base < nc * Q; base += THREADS) {
             const int t = base + tid;
-            const int s = t / Q, part = t % Q;
-            const bool on = s < C;
-            const uint64_t key = on ? cs.key[s] : ~0ull;
+            const int c = t / Q, part = t % Q;
+            const bool on = c < nc;
+            const uint64_t key = on ? cs.key[c] : ~0ull;
             int rank = 0;
-            if (on && key != ~0ull) {
-#pragma unroll 8
-                for (int o = part; o < C; o += Q) {
-                    const uint64_t ok = cs.key[o];
-                    rank += (ok < key || (ok == key && o < s)) ? 1 : 0;
-                }
+            if (on) {
+#pragma unroll 4
+                for (int o = part; o < nc; o += Q)
+                    rank += cs.key[o] < key ? 1 : 0;
             }
             if constexpr (Q >= 2)
                 rank += __builtin_amdgcn_update_dpp(0, rank, DPP_QUAD_XOR1, 0xf, 0xf, false);
@@ -701,11 +710,23 @@ __device__ int cache_plan_row(const int32_t *S, int nn, int C, int NB, const Slo
                 rank += __builtin_amdgcn_update_dpp(0, rank, DPP_QUAD_XOR2, 0xf, 0xf, false);
             if constexpr (Q >= 8)
                 rank += __builtin_amdgcn_update_dpp(0, rank, DPP_ROW_HALF_MIRROR, 0xf, 0xf, false);
-            if (on && part == 0 && key != ~0ull && rank < nm)
-                cs.slot_of[cs.miss_i[rank]] = s;
+            if (on && part == 0)
+                victim[rank] = (int32_t)(key & 1023u);
         }
     }
-    __syncthreads();
+    // misses in ascending selection order: miss j takes the victim of rank
+    // j, between the scan's barriers (so the plan is complete on return)
+    int nm;
+    (void)wg_exclusive_scan_publish<THREADS, int>(cnt, cs.wsum, nm, [&](int pos, int) {
+        for (int u = 0; u < per; ++u) {
+            const int i = tid * per + u;
+            if (i < nn && !cs.hit[i]) {
+                cs.miss_i[pos] = i;
+                cs.slot_of[i] = victim[pos];
+                ++pos;
+            }
+        }
+    });
     bad_out = 0;
     return nm;
 }
