@@ -66,6 +66,7 @@ def _declare(L):
     L.oracle_gather.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_capped_step.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]
     L.oracle_append.argtypes = [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _p]
+    L.oracle_check_state.argtypes = [_i, _i, _i, _p, _p, _p, _p]
     L.oracle_attention.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _i, _p, _d, _p, _p]
     L.oracle_attention_pool.argtypes = [_i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _d, _p, _p]
 
@@ -204,6 +205,21 @@ class LRU:
         lib().oracle_lru_step(self._h, k, int(nb_limit), _ptr(sel), _ptr(cnt), _ptr(ss), _ptr(sh), _ptr(mb),
                               _ptr(ms), _ptr(mc))
         return dict(sel_slot=ss, sel_hit=sh, miss_block=mb, miss_slot=ms, miss_count=mc)
+
+
+def check_state(slot_block, slot_stamp, clock, nb_limit):
+    """Per-row consistency flags of a working-set state (see
+    ``oracle_check_state``): 1 = an id outside [-1, nb_limit), 2 = one block
+    in two slots, 4 = an occupied slot stamped ahead of the row's clock.
+    Returns (flags [rows] int32, number of flagged rows)."""
+    sb = _c(slot_block, np.int32)
+    rows, cap = sb.shape[0], sb.shape[-1]
+    sb = sb.reshape(rows, cap)
+    st = _c(np.asarray(slot_stamp).astype(np.uint32).reshape(rows, cap), np.uint32)
+    ck = _c(np.asarray(clock).astype(np.uint32).reshape(rows), np.uint32)
+    flags = np.empty(rows, dtype=np.int32)
+    n = lib().oracle_check_state(rows, cap, int(nb_limit), _ptr(sb), _ptr(st), _ptr(ck), _ptr(flags))
+    return flags, int(n)
 
 
 def capped_step(slot_block, sel, sel_count, scores, nb_limit):

@@ -661,6 +661,41 @@ int oracle_capped_step(int rows, int cap, int k_max, int nb_limit, int nb_max, c
  * its block.  Then seq_lens[b] grows by one.  A full sequence (seq_lens[b]
  * >= T_max) is left as it is.  Plain byte copies.
  */
+/*
+ * Consistency check of a working-set state (failure detection: a block
+ * table must map each resident block to one slot, KV-Cache 压缩技术的工程原理
+ * §5.2; a corrupted or mis-restored table is what its rollback / resync
+ * guards against, same page §6.1).  Per row, flags[r] is the OR of
+ *   1: a slot id outside [-1, nb_limit),
+ *   2: one block held by two slots,
+ *   4: an occupied slot whose stamp is ahead of the row's clock (every
+ *      update stamps the slots it touches with the clock value it has just
+ *      advanced to, so no stamp can exceed the clock).
+ * Returns the number of rows with a nonzero flag.
+ */
+int oracle_check_state(int rows, int cap, int nb_limit, const int32_t *slot_block, const uint32_t *slot_stamp,
+                       const uint32_t *clock, int32_t *flags)
+{
+    int bad_rows = 0;
+    for (int r = 0; r < rows; ++r) {
+        const int32_t *sb = slot_block + (size_t)r * cap;
+        const uint32_t *st = slot_stamp + (size_t)r * cap;
+        int f = 0;
+        for (int s = 0; s < cap; ++s) {
+            if (sb[s] < -1 || sb[s] >= nb_limit)
+                f |= 1;
+            for (int t = 0; t < s; ++t)
+                if (sb[s] >= 0 && sb[t] == sb[s])
+                    f |= 2;
+            if (sb[s] >= 0 && st[s] > clock[r])
+                f |= 4;
+        }
+        flags[r] = f;
+        bad_rows += f != 0;
+    }
+    return bad_rows;
+}
+
 int oracle_append(int B, int Hkv, int D, int T_max, int block, int elem_bytes, const void *new_k,
                   const void *new_v, int32_t *seq_lens, void *k, void *v, const int32_t *slot_block, int cap,
                   void *pool_k, void *pool_v)
