@@ -410,6 +410,23 @@ size_t sparse_kv_topk_workspace_bytes(const skv_shape *shape, int32_t k_blocks);
 size_t sparse_kv_workspace_bytes(const skv_shape *shape, int32_t k_blocks, int32_t num_splits);
 
 /*
+ * Helper (failure detection, not part of the step): checks a working-set
+ * state on the device and writes per row flags [B,Hkv] int32, the OR of
+ *   1: a slot id outside [-1, NB),
+ *   2: one block held by two slots (a block table maps each resident block
+ *      to one slot: KV-Cache 压缩技术的工程原理 §5.2),
+ *   4: an occupied slot whose stamp is ahead of the row's clock (every
+ *      update stamps the slots it touches with the clock value it has just
+ *      advanced to).
+ * 0 means consistent.  Use it after restoring a snapshot or when a row came
+ * back refused (miss_count = -1) to see what is wrong; the update calls
+ * refuse rows with flags 1 or 2 on their own.  Reads the state only.
+ * Limits: 1 <= capacity <= 1024.
+ */
+skv_status sparse_kv_check_state(const skv_shape *shape, int32_t capacity, const int32_t *slot_block,
+                                 const uint32_t *slot_stamp, const uint32_t *clock, int32_t *flags, void *stream);
+
+/*
  * Helper (prefill time, not part of the step): per-block element-wise key
  * minimum and maximum over the valid tokens, meta [B,Hkv,NB,2,D] in the key
  * dtype (min at [...,0,:], max at [...,1,:]); blocks past seq_lens get

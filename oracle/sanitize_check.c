@@ -33,6 +33,7 @@ int oracle_lru_step(oracle_lru *, int, int, const int32_t *, const int32_t *, in
                     int32_t *, int32_t *);
 int oracle_capped_step(int, int, int, int, int, const int32_t *, const int32_t *, const double *, int32_t *,
                        int32_t *, uint8_t *, int32_t *, int32_t *, int32_t *);
+int oracle_check_state(int, int, int, const int32_t *, const uint32_t *, const uint32_t *, int32_t *);
 int oracle_append(int, int, int, int, int, int, const void *, const void *, int32_t *, void *, void *,
                   const int32_t *, int, void *, void *);
 int oracle_gather(int, int, int, int, int, int, int, const int32_t *, const int32_t *, const int32_t *, const void *,
@@ -125,6 +126,11 @@ static void run(int dtype)
     table[1] = table[0] >= 0 ? table[0] : 2; /* row 0: a block held twice */
     table[0] = table[1];
     table[C + 0] = NB;                        /* row 1: an id past the end */
+    {
+        uint32_t clk[6] = {2, 2, 2, 2, 2, 2};
+        int32_t fl[6];
+        CHECK(oracle_check_state(P, C, NB, table, stamps, clk, fl) >= 2 && (fl[0] & 2) && (fl[1] & 1));
+    }
     oracle_lru_load(h, table, stamps);
     CHECK(oracle_lru_step(h, k, NB, sel, cnt, ss, sh, mb, ms, mc) == 0);
     CHECK(mc[0] == -1 && mc[1] == -1 && ss[0] == -1 && mb[0] == -1);

@@ -196,3 +196,12 @@ def test_workspace_sizes():
         B.sparse_decode_attention_workspace_bytes(short, 128, 0),
         B.sparse_decode_attention_workspace_bytes(short, 128, B.sparse_kv_select_attend_splits(short, 128)))
     assert B.sparse_kv_workspace_bytes(short, 128, 200) == 0  # more splits than blocks
+
+
+def test_check_state(L):
+    def call(s=None, cap=16, sb=P, flags=P):
+        return L.sparse_kv_check_state(s if s is not None else shape(), cap, sb, P, P, flags, NUL)
+    assert call(sb=NUL) == NULL
+    assert call(flags=NUL) == NULL
+    assert call(cap=0) == SHAPE
+    assert call(cap=1025) == UNSUPPORTED

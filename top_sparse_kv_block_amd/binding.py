@@ -36,7 +36,7 @@ EXPORTS = (
     "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_status_string", "sparse_kv_select_attend",
     "sparse_kv_select_attend_splits", "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
     "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read", "sparse_kv_topk_workspace_bytes",
-    "sparse_kv_workspace_bytes",
+    "sparse_kv_workspace_bytes", "sparse_kv_check_state",
 )
 
 
@@ -93,6 +93,7 @@ def load():
     L.sparse_kv_workspace_bytes.restype = _sz
     L.sparse_kv_quest_meta.argtypes = [S, _p, _p, _p, _p]
     L.sparse_kv_stream_read.argtypes = [S, _p, _p, _p]
+    L.sparse_kv_check_state.argtypes = [S, _i32, _p, _p, _p, _p, _p]
     L.sparse_kv_host_alloc.argtypes = [_sz, C.POINTER(_p), C.POINTER(_p)]
     L.sparse_kv_host_free.argtypes = [_p]
     L.sparse_kv_status_string.argtypes = [C.c_int]
@@ -100,7 +101,7 @@ def load():
     for fn in ("sparse_kv_score", "sparse_kv_topk", "sparse_kv_cache_update", "sparse_decode_attention",
                "sparse_kv_quest_meta", "sparse_kv_host_alloc", "sparse_kv_host_free", "sparse_kv_select_attend",
                "sparse_kv_cache_update_importance", "sparse_kv_append", "sparse_kv_select",
-               "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read"):
+               "sparse_kv_select_attend_noalloc", "sparse_kv_stream_read", "sparse_kv_check_state"):
         getattr(L, fn).restype = C.c_int
     _lib = L
     return L
@@ -400,6 +401,19 @@ def sparse_kv_quest_meta(shape, keys, seq_lens, meta, stream=None):
                                      _ptr(seq_lens, torch.int32, "seq_lens", numel=shape.batch),
                                      _ptr(meta, dt, "meta", numel=P * (t // 16) * 2 * d), _stream(stream))
     _check("sparse_kv_quest_meta", rc)
+
+
+def sparse_kv_check_state(shape, capacity, slot_block, slot_stamp, clock, flags, stream=None):
+    """Per-row consistency flags of a working-set state into ``flags``
+    [B, Hkv] int32 (1 id out of range, 2 block in two slots, 4 stamp ahead of
+    the clock)."""
+    P, pc = shape.batch * shape.n_kv_heads, shape.batch * shape.n_kv_heads * int(capacity)
+    rc = load().sparse_kv_check_state(C.byref(shape), int(capacity),
+                                      _ptr(slot_block, torch.int32, "slot_block", numel=pc),
+                                      _ptr(slot_stamp, torch.int32, "slot_stamp", numel=pc),
+                                      _ptr(clock, torch.int32, "clock", numel=P),
+                                      _ptr(flags, torch.int32, "flags", numel=P), _stream(stream))
+    _check("sparse_kv_check_state", rc)
 
 
 def sparse_kv_stream_read(shape, keys, sink, stream=None):

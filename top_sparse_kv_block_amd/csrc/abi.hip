@@ -426,6 +426,22 @@ SKV_API skv_status sparse_kv_select_attend_noalloc(const skv_shape *shape, const
     return hip_status(skv::launch_select_attend(d, f, (hipStream_t)stream));
 }
 
+SKV_API skv_status sparse_kv_check_state(const skv_shape *shape, int32_t capacity, const int32_t *slot_block,
+                                         const uint32_t *slot_stamp, const uint32_t *clock, int32_t *flags,
+                                         void *stream) {
+    Dims d;
+    skv_status st = check_shape(shape, d);
+    if (st != SKV_OK)
+        return st;
+    if (!slot_block || !slot_stamp || !clock || !flags)
+        return SKV_ERR_NULL;
+    if (capacity < 1)
+        return SKV_ERR_SHAPE;
+    if (capacity > skv::kMaxCapacity)
+        return SKV_ERR_UNSUPPORTED;
+    return hip_status(skv::launch_check_state(d, capacity, slot_block, slot_stamp, clock, flags, (hipStream_t)stream));
+}
+
 SKV_API skv_status sparse_kv_quest_meta(const skv_shape *shape, const void *keys, const int32_t *seq_lens, void *meta,
                                         void *stream) {
     Dims d;

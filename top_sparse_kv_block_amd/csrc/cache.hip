@@ -201,6 +201,58 @@ __global__ __launch_bounds__(kLongRowThreads) void select_long_kernel(
                            miss_block, miss_slot, miss_count, sClock);
 }
 
+// check_state_kernel: one 256-thread workgroup per row checks the row's
+// working-set state (failure detection: a block table maps each resident
+// block to one slot, KV-Cache 压缩技术的工程原理 §5.2) and writes flags[row]:
+// 1 = a slot id outside [-1, NB), 2 = a block held by two slots (an LDS set
+// of block ids, as in the update's plan), 4 = an occupied slot stamped after
+// the row's clock.  Reads only; the state is not modified.
+constexpr int kCheckThreads = 256;
+
+__global__ __launch_bounds__(kCheckThreads) void check_state_kernel(const int32_t *__restrict__ slot_block,
+                                                                    const uint32_t *__restrict__ slot_stamp,
+                                                                    const uint32_t *__restrict__ clock, int C, int NB,
+                                                                    int32_t *__restrict__ flags) {
+    __shared__ int32_t dup[kDupSet];
+    __shared__ int sflag;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    SlotRegs<kCheckThreads> regs;
+    load_slots<kCheckThreads>(regs, C, slot_block + (size_t)row * C, slot_stamp + (size_t)row * C);
+    const uint32_t now = clock[row];
+    const int bits = dup_set_bits(C);
+    for (int i = tid; i < (1 << bits); i += kCheckThreads)
+        dup[i] = -1;
+    if (tid == 0)
+        sflag = 0;
+    __syncthreads();
+    int f = 0;
+#pragma unroll
+    for (int u = 0; u < SlotRegs<kCheckThreads>::SPT; ++u) {
+        const int s = tid + u * kCheckThreads;
+        if (s < C) {
+            const int32_t blk = regs.blk[u];
+            if (blk < -1 || blk >= NB)
+                f |= 1;
+            if (blk >= 0 && dup_set_add(dup, bits, blk))
+                f |= 2;
+            if (blk >= 0 && regs.stamp[u] > now)
+                f |= 4;
+        }
+    }
+    if (f)
+        atomicOr(&sflag, f);
+    __syncthreads();
+    if (tid == 0)
+        flags[row] = sflag;
+}
+
+hipError_t launch_check_state(const Dims &d, int cap, const int32_t *slot_block, const uint32_t *slot_stamp,
+                              const uint32_t *clock, int32_t *flags, hipStream_t st) {
+    hipLaunchKernelGGL(check_state_kernel, dim3(d.rows()), dim3(kCheckThreads), 0, st, slot_block, slot_stamp, clock,
+                       cap, d.NB, flags);
+    return hipGetLastError();
+}
+
 // One wave copies one missed block: K then V, 16*D elements each.
 template <int BLOCK_BYTES>
 __global__ __launch_bounds__(256) void gather_kernel(const int32_t *__restrict__ miss_block,

@@ -42,6 +42,8 @@ hipError_t launch_select(const Dims &d, const float *scores, const int32_t *lens
                          int cap, int32_t *sel_blocks, int32_t *sel_count, int32_t *slot_block, uint32_t *slot_stamp,
                          uint32_t *clock, int32_t *sel_slot, uint8_t *sel_hit, int32_t *miss_block,
                          int32_t *miss_slot, int32_t *miss_count, void *ws, hipStream_t st);
+hipError_t launch_check_state(const Dims &d, int cap, const int32_t *slot_block, const uint32_t *slot_stamp,
+                              const uint32_t *clock, int32_t *flags, hipStream_t st);
 hipError_t launch_gather(const Dims &d, int k, int cap, const int32_t *miss_block, const int32_t *miss_slot,
                          const int32_t *miss_count, const void *src_k, const void *src_v, void *pool_k,
                          void *pool_v, hipStream_t st);
