@@ -125,12 +125,13 @@ def test_fused_refuses_corrupt_tables():
     np.testing.assert_array_equal(host(buf.pool_v), pool_v)
 
 
-@pytest.mark.parametrize("capacity", [32, 48])
-def test_fused_rows_shorter_than_the_budget(capacity):
+@pytest.mark.parametrize("capacity,ctx", [(32, 4096), (48, 4096), (40, 16 * 20000)])
+def test_fused_rows_shorter_than_the_budget(capacity, ctx):
     """Rows with at most k valid blocks take every valid block without
     reading their scores; an empty row selects and attends nothing.  Lengths:
-    full, a partial 5-block row, empty, exactly k blocks."""
-    w = synth.WORKLOADS["llama8b_32k"].scaled(batch=4, ctx=4096, budget=512, capacity=capacity, steps=3)
+    full, a partial 5-block row, empty, exactly k blocks; also with rows
+    allocated past 16384 blocks (the chunk launch skips such rows)."""
+    w = synth.WORKLOADS["llama8b_32k"].scaled(batch=4, ctx=ctx, budget=512, capacity=capacity, steps=3)
     data = synth.gen_workload(w)
     lens_np = np.array([w.ctx, 16 * 5 - 3, 0, 16 * w.k_blocks], dtype=np.int32)
     splits = B.sparse_kv_select_attend_splits(B.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx,

@@ -143,3 +143,6 @@ def test_topk_long_rows_short_valid_lengths():
     s = r.standard_normal((6, 1, nb)).astype(np.float32)
     _run(s, [16 * 130, 16 * 129 + 5, 16 * 300, 16 * 1000 + 1, 16 * 4100, 16 * 128 + 16], 128, sink=4, recent=128)
     _run(s, [16 * 130, 16 * 129 + 5, 16 * 300, 16 * 1000 + 1, 16 * 4100, 16 * 128 + 16], 120)
+    # rows of at most k valid blocks take them all (no candidates read), an
+    # empty row takes none, and a row whose valid part ends inside a chunk
+    _run(s, [0, 16 * 50, 16 * 128, 16 * 128 - 3, 16 * 1024 + 1, 16 * 2048 - 1], 128, sink=4, recent=128)
