@@ -31,11 +31,14 @@
 // working-set update's result bit for bit), then attends its share, the
 // first block of each wave loaded as soon as the plan knows its hits.  Split 0 also writes the selection and
 // the step's lists.  The slot table is only read here; merge_commit_kernel
-// applies the plan after every workgroup has read the old table.  This
-// replaces three launches and their global round trips with one: the
-// alternative, handing results between workgroups inside one launch, needs
-// a device-scope release per workgroup, which on this chip writes back the
-// whole L2 each time.
+// applies the plan after every workgroup has read the old table (with one
+// split per row the kernel applies it itself).  This replaces three
+// launches and their global round trips with one: the alternative, handing
+// results between workgroups inside one launch, needs a device-scope release
+// per workgroup, which on this chip writes back the whole L2 each time.
+// Rows over 16384 blocks first run the top-k's chunk launch
+// (topk_chunk_kernel); every workgroup of such a row then selects from the
+// chunk candidates and plans with the standalone update's routine.
 //
 // merge_commit_kernel: one workgroup per row merges the splits' partials
 // (weights exp2(m_s - m*) formed once in LDS) and, when asked, commits the
