@@ -654,10 +654,16 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     xcd_row_part(row, split);
     const int b = row / Hkv, j = row - b * Hkv;
     const int NB = T / 16;
-    // the row's scores first: their loads need neither the length nor the
-    // slot table, and run while the rest is set up
+    // the row's scores (a long row: its chunk candidates) first: their loads
+    // need neither the length nor the slot table, and run while the rest is
+    // set up
     TopkScores<LONG ? 1 : KPT> pre;
-    if constexpr (!LONG)
+    LongCands<LONG ? KPT : 4> cands;
+    const int nc = nchunks * long_row_stride(k);
+    const float *wrow = cand + (size_t)row * 2 * nc;
+    if constexpr (LONG)
+        long_row_load<KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), nc, cands);
+    else
         topk_load<KPT>(scores + (size_t)row * NB, NB, pre);
     const int len = min(max(seq_lens[b], 0), T);
     SlotRegs<kAttnThreads> regs;  // in flight while the top-k runs
@@ -691,11 +697,8 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     };
     int nn, bad, nm;
     if constexpr (LONG) {
-        const size_t nc = (size_t)nchunks * long_row_stride(k);
-        const float *wrow = cand + (size_t)row * 2 * nc;
         const int ncand = (min(nb_of(len), NB) + chunk_blocks - 1) / chunk_blocks * long_row_stride(k);
-        nn = long_row_select<kAttnThreads, KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), ncand, len, NB,
-                                                k, sink, recent, sS, tsc);
+        nn = long_row_select<kAttnThreads, KPT>(cands, ncand, len, NB, k, sink, recent, sS, tsc);
         nm = cache_plan_row<kAttnThreads>(sS, nn, C, NB, regs, cs, bad);
     } else {
         nm = select_plan_row<kAttnThreads, KPT>(take, k, C, NB, regs, sS, cs, ps, nn, bad, load_first);

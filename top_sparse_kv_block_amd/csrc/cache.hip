@@ -184,17 +184,18 @@ __global__ __launch_bounds__(kLongRowThreads) void select_long_kernel(
     __shared__ CacheScratch cs;
     __shared__ uint32_t sClock;
     const int row = blockIdx.x;
+    const int nc = nchunks * long_row_stride(k);
+    const float *wrow = ws + (size_t)row * 2 * nc;
+    LongCands<KPT> cands;  // issued before the length is known
+    long_row_load<KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), nc, cands);
     const int len = min(max(seq_lens[row / Hkv], 0), T);
     int32_t *sb = slot_block + (size_t)row * C;
     uint32_t *ss = slot_stamp + (size_t)row * C;
     SlotRegs<THREADS> regs;  // in flight while the selection runs
     load_slots<THREADS>(regs, C, sb, ss);
     cache_plan_clear<THREADS>(cs, k, C);  // published by the selection's barriers
-    const size_t nc = (size_t)nchunks * long_row_stride(k);
-    const float *wrow = ws + (size_t)row * 2 * nc;
     const int ncand = (min(nb_of(len), NB) + chunk_blocks - 1) / chunk_blocks * long_row_stride(k);
-    const int n = long_row_select<THREADS, KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), ncand, len, NB, k,
-                                                sink, recent, sS, sc);
+    const int n = long_row_select<THREADS, KPT>(cands, ncand, len, NB, k, sink, recent, sS, sc);
     int bad;
     const int nm = cache_plan_row<THREADS>(sS, n, C, NB, regs, cs, bad);
     select_commit<THREADS>(row, k, C, n, nm, bad, sS, cs, sel_blocks, sel_count, sb, ss, clock, sel_slot, sel_hit,

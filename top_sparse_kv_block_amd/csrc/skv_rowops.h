@@ -387,24 +387,17 @@ __device__ __forceinline__ int forced_ranges(int len, int nvalid, int k, int sin
     return k - n_forced;
 }
 
-// Phase A for chunk `chunk` of a row (THREADS threads, KPT keys each, chunk
-// = THREADS * KPT blocks; the caller has checked chunk * THREADS * KPT <
-// nvalid).  ws_score / ws_id: this chunk's long_row_stride(k) entries.
-// Contains barriers.
+// Phase A's scores for chunk `chunk` of a row: thread t's KPT blocks from
+// chunk * THREADS * KPT + t * KPT, read before the row's length is known
+// (indexes clamped into the NB allocated scores; what lies past the valid
+// part is masked by chunk_candidates).
 template <int THREADS, int KPT>
-__device__ void chunk_candidates(const float *__restrict__ srow, int len, int NB, int k, int sink, int recent,
-                                 int chunk, float *__restrict__ ws_score, int32_t *__restrict__ ws_id, TopkScratch &sc) {
+__device__ __forceinline__ void chunk_load(const float *__restrict__ srow, int NB, int chunk, float (&v)[KPT]) {
     static_assert(KPT % 4 == 0, "16-byte loads");
-    const int tid = threadIdx.x;
-    const int nvalid = min(nb_of(len), NB);
-    int fs, fr;
-    const int need = forced_ranges(len, nvalid, k, sink, recent, fs, fr);
-    const int c0 = chunk * THREADS * KPT, c1 = c0 + THREADS * KPT;
-    const int base = c0 + tid * KPT;
-    float v[KPT];
+    const int base = chunk * THREADS * KPT + threadIdx.x * KPT;
     if ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0 && (NB & 3) == 0) {  // uniform
-        // unconditional 16-byte loads, the index clamped into the row (a
-        // clamped group lies past NB, so all of its ids are masked below)
+        // 16-byte loads; a clamped group lies past NB, so all of its ids are
+        // masked
 #pragma unroll
         for (int u = 0; u < KPT / 4; ++u) {
             const float4 f = *reinterpret_cast<const float4 *>(srow + min(base + 4 * u, NB - 4));
@@ -416,8 +409,23 @@ __device__ void chunk_candidates(const float *__restrict__ srow, int len, int NB
     } else {
 #pragma unroll
         for (int m = 0; m < KPT; ++m)
-            v[m] = srow[min(base + m, nvalid - 1)];
+            v[m] = srow[min(base + m, NB - 1)];
     }
+}
+
+// Phase A for chunk `chunk` of a row (THREADS threads, KPT keys each, chunk
+// = THREADS * KPT blocks; the caller has checked chunk * THREADS * KPT <
+// nvalid), over the scores chunk_load read.  ws_score / ws_id: this chunk's
+// long_row_stride(k) entries.  Contains barriers.
+template <int THREADS, int KPT>
+__device__ void chunk_candidates(const float (&v)[KPT], int len, int NB, int k, int sink, int recent, int chunk,
+                                 float *__restrict__ ws_score, int32_t *__restrict__ ws_id, TopkScratch &sc) {
+    const int tid = threadIdx.x;
+    const int nvalid = min(nb_of(len), NB);
+    int fs, fr;
+    const int need = forced_ranges(len, nvalid, k, sink, recent, fs, fr);
+    const int c0 = chunk * THREADS * KPT, c1 = c0 + THREADS * KPT;
+    const int base = c0 + tid * KPT;
     uint32_t key[KPT];
     uint64_t cand = 0;
 #pragma unroll
@@ -447,14 +455,44 @@ __device__ void chunk_candidates(const float *__restrict__ srow, int len, int NB
         ws_id[i] = -1;
 }
 
-// Phase B: the row's selection, ascending, into S[0, k) (LDS; -1 padded);
-// returns its size.  ws_score / ws_id: the row's ncand = chunks * stride
-// entries (THREADS * KPT >= ncand, KPT % 4 == 0, both 16-byte aligned).
-// Contains barriers; S is complete on return.
-template <int THREADS, int KPT>
-__device__ int long_row_select(const float *__restrict__ ws_score, const int32_t *__restrict__ ws_id, int ncand,
-                               int len, int NB, int k, int sink, int recent, int32_t *S, TopkScratch &sc) {
+// Phase B's candidates for a row: thread t's KPT entries from t * KPT of the
+// row's nc = chunks * stride entries (THREADS * KPT >= nc; nc a multiple of
+// 4; both arrays 16-byte aligned), read before the row's length is known
+// (indexes clamped into the nc entries; long_row_select masks the entries
+// past the chunks the length covers).
+template <int KPT>
+struct LongCands {
+    float v[KPT];
+    int32_t id[KPT];
+};
+
+template <int KPT>
+__device__ __forceinline__ void long_row_load(const float *__restrict__ ws_score, const int32_t *__restrict__ ws_id,
+                                              int nc, LongCands<KPT> &c) {
     static_assert(KPT % 4 == 0, "16-byte loads");
+#pragma unroll
+    for (int u = 0; u < KPT / 4; ++u) {
+        const int p = min((int)threadIdx.x * KPT + 4 * u, nc - 4);
+        const float4 f = *reinterpret_cast<const float4 *>(ws_score + p);
+        const int4 d = *reinterpret_cast<const int4 *>(ws_id + p);
+        c.v[4 * u] = f.x;
+        c.v[4 * u + 1] = f.y;
+        c.v[4 * u + 2] = f.z;
+        c.v[4 * u + 3] = f.w;
+        c.id[4 * u] = d.x;
+        c.id[4 * u + 1] = d.y;
+        c.id[4 * u + 2] = d.z;
+        c.id[4 * u + 3] = d.w;
+    }
+}
+
+// Phase B: the row's selection, ascending, into S[0, k) (LDS; -1 padded);
+// returns its size.  c: what long_row_load read; ncand: the entries of the
+// chunks that hold valid blocks (the rest is not current).  Contains
+// barriers; S is complete on return.
+template <int THREADS, int KPT>
+__device__ int long_row_select(const LongCands<KPT> &c, int ncand, int len, int NB, int k, int sink, int recent,
+                               int32_t *S, TopkScratch &sc) {
     const int tid = threadIdx.x;
     const int nvalid = min(nb_of(len), NB);
     if (nvalid <= k) {
@@ -465,25 +503,10 @@ __device__ int long_row_select(const float *__restrict__ ws_score, const int32_t
     }
     int fs, fr;
     const int need = forced_ranges(len, nvalid, k, sink, recent, fs, fr);
-    // candidates: entries with an id (padding never competes, even against
-    // a -inf score); position order is id order.  16-byte loads, the index
-    // clamped into the entries (ncand is a multiple of 4) and masked below.
-    float v[KPT];
-    int32_t ids[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT / 4; ++u) {
-        const int p = min(tid * KPT + 4 * u, ncand - 4);
-        const float4 f = *reinterpret_cast<const float4 *>(ws_score + p);
-        const int4 d = *reinterpret_cast<const int4 *>(ws_id + p);
-        v[4 * u] = f.x;
-        v[4 * u + 1] = f.y;
-        v[4 * u + 2] = f.z;
-        v[4 * u + 3] = f.w;
-        ids[4 * u] = d.x;
-        ids[4 * u + 1] = d.y;
-        ids[4 * u + 2] = d.z;
-        ids[4 * u + 3] = d.w;
-    }
+    // candidates: current entries with an id (padding never competes, even
+    // against a -inf score); position order is id order
+    const float *v = c.v;
+    const int32_t *ids = c.id;
     uint32_t key[KPT];
     uint64_t cand = 0;
 #pragma unroll

@@ -53,6 +53,8 @@ __global__ __launch_bounds__(THREADS) void topk_chunk_kernel(const float *__rest
     __shared__ TopkScratch sc;
     int row, chunk;
     xcd_row_part(row, chunk);
+    float v[KPT];  // issued before the length is known
+    chunk_load<THREADS, KPT>(scores + (size_t)row * NB, NB, chunk, v);
     const int len = min(max(seq_lens[row / Hkv], 0), T);
     const int nvalid = min(nb_of(len), NB);
     // uniform: a row of at most k valid blocks takes them all without its
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(THREADS) void topk_chunk_kernel(const float *__rest
     const size_t nc = (size_t)gridDim.x * long_row_stride(k);
     float *wrow = ws + (size_t)row * 2 * nc;
     const size_t off = (size_t)chunk * long_row_stride(k);
-    chunk_candidates<THREADS, KPT>(scores + (size_t)row * NB, len, NB, k, sink, recent, chunk, wrow + off,
+    chunk_candidates<THREADS, KPT>(v, len, NB, k, sink, recent, chunk, wrow + off,
                                    reinterpret_cast<int32_t *>(wrow + nc) + off, sc);
 }
 
@@ -82,12 +84,13 @@ __global__ __launch_bounds__(kLongRowThreads) void topk_long_kernel(const int32_
     __shared__ TopkScratch sc;
     __shared__ int32_t sS[kMaxK];
     const int row = blockIdx.x;
-    const int len = min(max(seq_lens[row / Hkv], 0), T);
-    const size_t nc = (size_t)nchunks * long_row_stride(k);
+    const int nc = nchunks * long_row_stride(k);
     const float *wrow = ws + (size_t)row * 2 * nc;
-    const int n = long_row_select<kLongRowThreads, KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc),
-                                                        long_row_ncand(len, NB, k, chunk_blocks), len, NB, k, sink,
-                                                        recent, sS, sc);
+    LongCands<KPT> cands;  // issued before the length is known
+    long_row_load<KPT>(wrow, reinterpret_cast<const int32_t *>(wrow + nc), nc, cands);
+    const int len = min(max(seq_lens[row / Hkv], 0), T);
+    const int n = long_row_select<kLongRowThreads, KPT>(cands, long_row_ncand(len, NB, k, chunk_blocks), len, NB, k,
+                                                        sink, recent, sS, sc);
     for (int i = threadIdx.x; i < k; i += kLongRowThreads)
         sel_blocks[(size_t)row * k + i] = sS[i];
     if (threadIdx.x == 0)
