@@ -59,6 +59,7 @@ struct TopkScratch {
     uint32_t hist[2][256];  // passes alternate buffers, so clearing needs no barrier of its own
     uint32_t wsum[16];
     uint32_t wlo[16], whi[16];  // per-wave key range
+    uint32_t wbeta[16];         // per-wave lower bound (small budgets)
     uint32_t digit, remaining, n_tau;
 };
 
@@ -88,7 +89,9 @@ __device__ __forceinline__ void pick_digit(const uint32_t *hist, uint32_t remain
 // Radix select: the key of the `need`-th largest of the keys flagged in
 // `cand` (KPT per thread; need >= 1 and at most the number of flagged keys).
 // Up to four 8-bit passes over an LDS histogram, on the keys minus the
-// smallest flagged key; each pass needs two barriers (the histogram buffers
+// smallest flagged key (for a small need: minus a lower bound on the
+// need-th key, counting only the keys above it); each pass needs two
+// barriers (the histogram buffers
 // alternate, so clearing the next one needs none).  Returns the key;
 // `remaining` = how many keys equal to it are admitted, `n_tau` = how many
 // flagged keys equal it.  The passes stop early once the bin holding the
@@ -104,6 +107,7 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
     // from the highest one in which the keys differ, so even the first pass
     // spreads them over the bins (the leading bits of raw keys are shared by
     // most scores of a row, and colliding LDS atomics serialise)
+    constexpr int WAVES = THREADS / 64;
     uint32_t lo = 0xffffffffu, hi = 0;
 #pragma unroll
     for (int m = 0; m < KPT; ++m)
@@ -111,19 +115,49 @@ __device__ __forceinline__ uint32_t radix_select(const uint32_t (&key)[KPT], uin
             lo = min(lo, key[m]);
             hi = max(hi, key[m]);
         }
+    // A small budget (at most four keys per wave) also gets a lower bound
+    // beta on the need-th largest key, so that the passes count only the
+    // few keys at or above it instead of every key of the row (at 8192 keys
+    // and one LDS atomic per key the first pass cost more than the rest of
+    // the selection).  Each wave takes the m-th largest of its lanes'
+    // largest keys, m = ceil(need / waves): its m lanes at or above that
+    // value hold at least m keys, so all waves together hold at least need
+    // keys at or above the smallest of the waves' values.  A wave with fewer
+    // than m lanes holding keys gives 0, which bounds nothing.
+    const bool bound = need <= 4u * WAVES;  // uniform
+    uint32_t beta = 0;
+    if (bound) {
+        const int mm = ((int)need + WAVES - 1) / WAVES;
+        uint32_t v = hi;
+        for (int it = 0; it < mm; ++it) {
+            beta = wave_max_u32(v);
+            if (lane == __builtin_ctzll(__builtin_amdgcn_ballot_w64(v == beta)))
+                v = 0;  // one lane holding the maximum drops out
+        }
+    }
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
     if (lane == 0) {
         sc.wlo[wave] = lo;
         sc.whi[wave] = hi;
+        sc.wbeta[wave] = beta;
     }
     for (int i = tid; i < 256; i += THREADS)
         sc.hist[0][i] = 0;
     lds_barrier();
+    beta = 0xffffffffu;
 #pragma unroll
-    for (int w = 0; w < THREADS / 64; ++w) {
+    for (int w = 0; w < WAVES; ++w) {
         lo = min(lo, sc.wlo[w]);
         hi = max(hi, sc.whi[w]);
+        beta = min(beta, sc.wbeta[w]);
+    }
+    if (bound && beta > lo) {  // uniform: no key below beta can be admitted
+#pragma unroll
+        for (int m = 0; m < KPT; ++m)
+            if (key[m] < beta)
+                cand &= ~(1ull << m);
+        lo = beta;
     }
     const int top = hi > lo ? 32 - __builtin_clz(hi - lo) : 1;  // significant bits of the range
     const int passes = (top + 7) / 8;
