@@ -63,6 +63,26 @@ def test_topk_sink_and_recent(sink, recent):
     _run(s, [131072, 131072 - 5, 1000], 32, sink=sink, recent=recent)
 
 
+# Budgets of at most four keys per wave first bound the threshold from below
+# with each wave's m-th largest lane maximum; the cases put ties at the
+# threshold, the best blocks in one lane (contiguous ids), waves without any
+# candidate (short valid parts, forced ranges) and -inf scores against it.
+@pytest.mark.parametrize("nb", [2048, 8192, 16384])
+@pytest.mark.parametrize("k", [1, 5, 17, 32, 33, 64])
+def test_topk_small_budgets(nb, k):
+    r = np.random.default_rng(nb * 7 + k)
+    s = r.standard_normal((2, 4, nb)).astype(np.float32)
+    s[0, 1] = np.round(s[0, 1] * 2) / 2  # few distinct values: ties at the threshold
+    s[0, 2, 100:140] = 9.0 + r.random(40).astype(np.float32)  # the best blocks in one or two lanes
+    s[0, 3, :] = 1.0
+    s[0, 3, 5 * nb // 8:] = 2.0  # the best keys all in the last waves, equal
+    s[1, 0, ::3] = -np.inf
+    s[1, 1, :] = -np.inf
+    s[1, 1, 7::97] = r.standard_normal(len(range(7, nb, 97))).astype(np.float32)
+    _run(s, [nb * 16, 16 * min(nb, 600) + 3], k)
+    _run(s, [nb * 16 - 5, nb * 16], k, sink=16 * (k // 8), recent=16 * (k // 3))
+
+
 def test_topk_rejects_too_many_forced_blocks():
     shape = B.make_shape(1, 1, 1, 64, 1024, "f32")
     t = lambda *a, **kw: torch.zeros(*a, device="cuda", **kw)
