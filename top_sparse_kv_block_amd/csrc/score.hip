@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_blockmax_mfma_kernel(cons
 // bit-select per packed word) and takes a plain dot product with q.
 template <typename E> __device__ __forceinline__ uint32_t neg_mask(uint32_t qw);
 template <> __device__ __forceinline__ uint32_t neg_mask<BF16>(uint32_t qw) {
-    return ((qw & 0x80008000u) >> 15) * 0xffffu;
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, qw) >> (s16x2){15, 15});  // one packed shift
 }
 template <> __device__ __forceinline__ uint32_t neg_mask<F32>(uint32_t qw) {
     return (uint32_t)((int32_t)qw >> 31);
@@ -307,13 +308,16 @@ __global__ __launch_bounds__(kQuestThreads) void score_quest_kernel(const uint8_
 // matrix product, 2D/32 v_mfma_f32_16x16x32_bf16 per tile.  Each wave reads
 // its tile of 16 boxes (16 x 4D bytes) with fully coalesced 16-byte lane
 // loads, stages it in its own LDS tile (rows padded by 16 bytes: both access
-// patterns free of bank conflicts) and reads the A operand (block l%16,
-// elements 32c + 8(l/16) .. +8) back from there; the B operand holds the
+// patterns free of bank conflicts) and reads the B operand (block l%16,
+// elements 32c + 8(l/16) .. +8) back from there; the A operand holds the
 // same elements of [q-; q+] for query row 16t + l%16, built once from q.
-// Lane l then holds the bounds of blocks 4(l/16) .. +4 for query row
-// 16t + l%16: the max over the real rows is a DPP reduction within each
-// 16-lane row.  The vector kernel above spent as much time on its
-// per-element selects and lane reductions as on its loads.
+// With the query tile as the product's left operand and the boxes as its
+// right one, lane l holds the bounds of query rows 16t + 4(l/16) .. +4 for
+// block l%16: the max over the group's rows is taken in the lane (and
+// across the four 16-lane rows only when there are more than four query
+// rows).  The vector kernel above spent as much time on its per-element
+// selects and lane reductions as on its loads; with the boxes as the left
+// operand the max over the rows cost four DPP steps per lane and score.
 template <int D, int NT>
 __global__ __launch_bounds__(64 * kQuestMfmaWaves) void score_quest_mfma_kernel(const uint8_t *__restrict__ q,
                                                                const uint8_t *__restrict__ meta,
@@ -336,26 +340,22 @@ __global__ __launch_bounds__(64 * kQuestMfmaWaves) void score_quest_mfma_kernel(
     uint8_t *my = tile[wave];
 
     // B operand: element e = 32c + 8*rsub + i of [q-; q+] for query row
-    // 16t + col (rows past R: zeros, masked below); unconditional loads
-    u32x4 qf[NT][KCH];
+    // 16t + col (rows past R: zeros, masked below).  Its loads go first
+    // (unconditional), then the length, then the tile's box loads; the
+    // operand is formed only once all of them are in flight.  (Formed
+    // before the box loads, the compiler waited for the query before
+    // issuing most of them, and each wave's tile arrived a full load
+    // latency late.)
+    constexpr int QL = D / 32;  // 16-byte query loads per lane and query tile
+    u32x4 qv[NT][QL];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int r = 16 * t + col;
-        const int rr = min(r, R - 1);
+        const int rr = min(16 * t + col, R - 1);
         const int rq = rr / G, g = rr - rq * G;
         const uint8_t *qr = q + (((size_t)b * NQ + rq) * Hq + (size_t)j * G + g) * D * 2;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            const int e = 32 * c + 8 * rsub;  // e < D: q- (pairs with lo), else q+ (hi)
-            const u32x4 v = load16(qr + (e % D) * 2);
-            u32x4 w;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t m = ((v[x] & 0x80008000u) >> 15) * 0xffffu;  // negative halves
-                w[x] = r < R ? (e < D ? (v[x] & m) : (v[x] & ~m)) : 0u;
-            }
-            qf[t][c] = w;
-        }
+        for (int c = 0; c < QL; ++c)
+            qv[t][c] = load16(qr + (32 * c + 8 * rsub) * 2);
     }
     const int len = min(max(seq_lens[b], 0), T);
     const int nvalid = nb_of(len);
@@ -370,51 +370,61 @@ __global__ __launch_bounds__(64 * kQuestMfmaWaves) void score_quest_mfma_kernel(
         return;
     }
     u32x4 kv[LOADS];
+    static_assert(64 % LPB == 0, "a lane reads the same 16 bytes of its box in every load");
+    const uint32_t part = (uint32_t)(lane % LPB) * 16;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-        const int bl = (i * 64 + lane) / LPB;  // box of this lane's 16 bytes
-        const int nb = min(n0 + bl, NB - 1);   // a partial last tile re-reads the row's last box
-        kv[i] = load_nt(mrow + (size_t)nb * BB + ((i * 64 + lane) % LPB) * 16);
+        const int bl = i * (64 / LPB) + lane / LPB;  // box of this lane's 16 bytes
+        const uint32_t nb = (uint32_t)min(n0 + bl, NB - 1);  // a partial last tile re-reads the row's last box
+        kv[i] = load_nt(mrow + (nb * (uint32_t)BB + part));  // a row's boxes span far less than 4 GiB
     }
+    __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the box loads
+    // rows of a query tile past R hold row R - 1's query; their products
+    // are never read (the maximum below skips them)
+    u32x4 qf[NT][KCH];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const u32x4 v = qv[t][c % QL];
+            u32x4 w;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t m = neg_mask<BF16>(v[x]);
+                w[x] = c < QL ? (v[x] & m) : (v[x] & ~m);  // c < QL: q- (pairs with lo), else q+ (hi)
+            }
+            qf[t][c] = w;
+        }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int bl = (i * 64 + lane) / LPB;
         *reinterpret_cast<u32x4 *>(my + bl * ROW + ((i * 64 + lane) % LPB) * 16) = kv[i];
     }
     __builtin_amdgcn_wave_barrier();
-    u32x4 af[KCH];
+    u32x4 bf[KCH];
 #pragma unroll
     for (int c = 0; c < KCH; ++c)
-        af[c] = *reinterpret_cast<const u32x4 *>(my + col * ROW + c * 64 + rsub * 16);
-    float m[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        bf[c] = *reinterpret_cast<const u32x4 *>(my + col * ROW + c * 64 + rsub * 16);
+    // query rows x boxes: lane l holds the bounds of query rows
+    // 16t + 4(l/16) .. +4 for block n0 + l%16
+    float best = -__builtin_inff();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         f32x4 st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int c = 0; c < KCH; ++c)
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[c]),
-                                                          __builtin_bit_cast(bf16x8, qf[t][c]), st, 0, 0, 0);
-        if (16 * t + col < R) {
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[t][c]),
+                                                          __builtin_bit_cast(bf16x8, bf[c]), st, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                m[i] = fmaxf(m[i], st[i]);
-        }
+        for (int i = 0; i < 4; ++i)
+            best = 16 * t + 4 * rsub + i < R ? fmaxf(best, st[i]) : best;
     }
-    // max over the 16 query-row lanes of each 16-lane row
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR8>(m[i]));
-        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR4>(m[i]));
-        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR2>(m[i]));
-        m[i] = fmaxf(m[i], dpp<DPP_ROW_ROR1>(m[i]));
-    }
-    if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = n0 + 4 * rsub + i;
-            if (n < NB)
-                srow[n] = n < nvalid ? m[i] * scale : -__builtin_inff();
-        }
+    if (R > 4)  // uniform: query rows in more than the first 16 lanes
+        best = rows_max(best);
+    if (lane < 16) {
+        const int n = n0 + lane;
+        if (n < NB)
+            srow[n] = n < nvalid ? best * scale : -__builtin_inff();
     }
 }
 
