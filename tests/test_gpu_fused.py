@@ -49,6 +49,9 @@ FIELDS = ("out", "lse", "sel_blocks", "sel_count", "slot_block", "slot_stamp", "
     ("llama8b_32k", dict(batch=3, ctx=16 * 20000, budget=1024, capacity=100, ragged=True), 3, 0),
     ("quest_128k", dict(batch=2, n_kv_heads=2, n_q_heads=8, ctx=16 * 40000 + 5 * 16), 3, 0),
     ("lookahead_1m", {}, 2, 0),
+    # the largest budget over 40000 blocks: 4096-block chunks, 10240
+    # candidates per row (32 per thread in the selection)
+    ("lookahead_1m", dict(n_kv_heads=2, n_q_heads=16, ctx=16 * 40000, budget=16 * 1024, capacity=1024), 2, 0),
 ])
 def test_fused_equals_separate_calls(name, kw, steps, splits):
     w = synth.WORKLOADS[name].scaled(steps=steps, **kw)

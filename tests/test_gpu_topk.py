@@ -95,7 +95,7 @@ def test_topk_rejects_too_many_forced_blocks():
 # Rows longer than 16384 blocks are selected in two launches: each chunk of
 # 1024, 2048 or 4096 blocks keeps its best blocks in the workspace, then one
 # workgroup per row selects from those.  The cases cover every chunk size,
-# 4 to 32 candidates per thread in the second launch, a row length not a
+# 4, 8 and 32 candidates per thread in the second launch, a row length not a
 # multiple of 4 (scalar loads), a budget not a multiple of 4 (padded chunk
 # stride) and k = 1.
 @pytest.mark.parametrize("nb,k", [(16385, 64), (32768, 1024), (65536, 128), (65536, 1), (65536, 1024),

@@ -965,8 +965,6 @@ static hipError_t fused_k(const Dims &d, const FusedArgs &f, hipStream_t st) {
         return fused_t<E, D, GMAX, 4, true>(d, f, st);
     case 8:
         return fused_t<E, D, GMAX, 8, true>(d, f, st);
-    case 16:
-        return fused_t<E, D, GMAX, 16, true>(d, f, st);
     default:
         return fused_t<E, D, GMAX, 32, true>(d, f, st);
     }

@@ -346,9 +346,6 @@ hipError_t launch_select(const Dims &d, const float *scores, const int32_t *lens
     case 8:
         SKV_SELECT_LONG(8);
         break;
-    case 16:
-        SKV_SELECT_LONG(16);
-        break;
     default:
         SKV_SELECT_LONG(32);
     }

@@ -117,13 +117,13 @@ hipError_t launch_topk_chunks(const Dims &d, const float *scores, const int32_t 
     return hipGetLastError();
 }
 
-// Keys per thread of phase B for a row's candidate count.
+// Keys per thread of phase B for a row's candidate count: 4, 8 or 32.  (No
+// row of 16385 to 65536 blocks with k <= 1024 has 4097 to 8192 candidates:
+// a chunk size that fails the 4096 bound and meets the 16384 one gives more
+// than 8192.)
 int long_row_kpt(const Dims &d, int k) {
     const int ncand = long_row_chunks(d.NB, k) * long_row_stride(k);
-    for (int kpt = 4; kpt < 32; kpt *= 2)
-        if (ncand <= kpt * kLongRowThreads)
-            return kpt;
-    return 32;
+    return ncand <= 4 * kLongRowThreads ? 4 : ncand <= 8 * kLongRowThreads ? 8 : 32;
 }
 
 template <int THREADS, int KPT>
@@ -163,9 +163,6 @@ hipError_t launch_topk(const Dims &d, const float *scores, const int32_t *lens, 
         break;
     case 8:
         SKV_TOPK_LONG(8);
-        break;
-    case 16:
-        SKV_TOPK_LONG(16);
         break;
     default:
         SKV_TOPK_LONG(32);
