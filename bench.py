@@ -92,7 +92,9 @@ def score_launch_bytes(w) -> int:
 
 
 def _score_kernel_name(w) -> str:
-    """The exact-scoring kernel the library runs for this workload's dtype."""
+    """The scoring kernel the library runs for this workload's scoring mode and dtype."""
+    if w.scoring == "quest":
+        return "score_quest_mfma_kernel" if w.dtype == "bf16" else "score_quest_kernel"
     return "score_blockmax_mfma_kernel" if w.dtype == "bf16" else "score_blockmax_kernel"
 
 
@@ -923,8 +925,7 @@ def run(args):
                       "attention": round(float(stage[:, 3].mean()), 2)} if select else
                      {name: round(float(v), 2) for name, v in
                       zip(("score", "topk", "cache_update", "attention"), stage.mean(axis=0))}),
-        "roofline": {"bound": "hbm", "kernel": _score_kernel_name(w) if mode == B.SKV_SCORE_BLOCKMAX
-                     else "score_quest_kernel",
+        "roofline": {"bound": "hbm", "kernel": _score_kernel_name(w),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(score_avg_s * 1e6, 2),
