@@ -56,7 +56,7 @@ constexpr int kQuestBlocksPerWave = 4;  // wave iterations, each BPL blocks
 // matrix-core Quest scan: one tile of 16 boxes per wave, two waves per
 // workgroup.  Measured on the 128K workload (32 rows x 8192 boxes, 134 MB):
 // 20.9 us with 2 waves, 21.1 with 1, 21.5 with 8, 22.4 with 4; two tiles per
-// wave 24.0; the A operand loaded straight from memory (64 bytes per box
+// wave 24.0; the box operand loaded straight from memory (64 bytes per box
 // per instruction) instead of through LDS 24.3-31.4.
 constexpr int kQuestMfmaWaves = 2;
 
