@@ -120,10 +120,16 @@ def merge_launch_bytes(w, splits: int) -> int:
 
 
 def _sources_sha(kernel: str = "score") -> str:
+    """Hash of the kernel's source files without their // comments and blank
+    lines, so that counters taken on a kernel stay valid across edits of its
+    comments (no counted code changes) and expire with any code change."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
