@@ -40,10 +40,10 @@
 // (topk_chunk_kernel); every workgroup of such a row then selects from the
 // chunk candidates and plans with the standalone update's routine.
 //
-// merge_commit_kernel: one workgroup per row merges the splits' partials
-// (weights exp2(m_s - m*) formed once in LDS) and, when asked, commits the
-// working-set plan (new blocks and stamps for the selected slots, the
-// clock advanced by a device atomic).
+// merge_commit_kernel: one workgroup per (row, head) merges the head's
+// split partials (weights exp2(m_s - m*) formed once by one wave) and, when
+// asked, the row's first one commits the working-set plan (new blocks and
+// stamps for the selected slots, the clock advanced by a device atomic).
 #include "skv_rowops.h"
 
 namespace skv {
@@ -742,14 +742,21 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     }
 }
 
-// One workgroup per row: merge the row's G heads over the splits (when
-// splits > 1), then commit the row's working-set plan (when commit is set):
-// every selected slot gets its block and the new stamp, the clock advances.
-// The kernel is a chain of dependent steps, so every global read it needs
-// (commit operands, the clock advance, and the row's partials, staged in
-// LDS when they fit) is issued before the first barrier.
-constexpr int kMergeStage = 12288;  // floats of partials staged in LDS (48 KiB)
+// One workgroup per (row, head), rows placed on XCDs as the fused kernel
+// places them (so a row's partials are read where they were written):
+// merge the head's partials over the splits (when splits > 1); the row's
+// head-0 workgroup also commits the row's working-set plan (when commit is
+// set): every selected slot gets its block and the new stamp, the clock
+// advances.  The kernel is a chain of dependent steps, so every global read
+// it needs (commit operands, the clock advance, and the head's partials,
+// staged in LDS when they fit) is issued before the first barrier; wave 0
+// then forms the splits' weights exp2(m_s - M) and the denominator in
+// registers.  (One workgroup per row merging all G heads read 33 KB per
+// row at 32 splits x 8 heads, past the LDS stage, from global memory
+// behind four barriers: 7 us on the 1M-context rows.)
+constexpr int kMergeStage = 12288;  // floats of one head's partials staged in LDS (48 KiB)
 constexpr int kCommitPerThread = kMaxK / kAttnThreads;
+static_assert(kMaxSplits <= 128, "wave 0 holds two splits per lane");
 
 __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
     const float *__restrict__ part, int Hq, int Hkv, int D, int splits, float *__restrict__ out,
@@ -758,19 +765,22 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
     const int32_t *__restrict__ miss_count, int32_t *__restrict__ slot_block, uint32_t *__restrict__ slot_stamp,
     uint32_t *__restrict__ clock) {
     __shared__ float stage[kMergeStage];
-    __shared__ float sw[kMaxGroup][kMaxSplits];  // m_s, then the weight exp2(m_s - M)
-    __shared__ float sl[kMaxGroup][kMaxSplits];
-    __shared__ float shM[kMaxGroup], shL[kMaxGroup];
+    __shared__ float sw[kMaxSplits];  // the weight exp2(m_s - M) of each split
+    __shared__ float shM, shL;
     __shared__ uint32_t sNow;
-    const int row = blockIdx.x, tid = threadIdx.x;
+    int row, g;
+    xcd_row_part(row, g);  // grid (G, rows)
+    const int tid = threadIdx.x;
     const int b = row / Hkv, j = row - b * Hkv;
     const int G = Hq / Hkv;
-    const int W = G * (D + 2);
-    const float *p = part + (size_t)row * splits * W;
-    const bool staged = splits > 1 && splits * W <= kMergeStage;
+    const int HW = D + 2;      // floats of one head's partial: acc[D], m, l
+    const int W = G * HW;      // floats of one split of the row
+    const float *p = part + (size_t)row * splits * W + (size_t)g * HW;  // split s at p + s * W
+    const bool staged = splits > 1 && splits * HW <= kMergeStage;
+    const bool committer = commit && g == 0;  // uniform over the workgroup
 
     int mc = -1, n = 0, c_slot[kCommitPerThread], c_blk[kCommitPerThread];
-    if (commit) {  // reads first, decisions after: none of these addresses depends on another read
+    if (committer) {  // reads first, decisions after: none of these addresses depends on another read
         mc = miss_count[row];
         n = sel_count[row];
 #pragma unroll
@@ -781,53 +791,55 @@ __global__ __launch_bounds__(kAttnThreads) void merge_commit_kernel(
         }
     }
     if (staged) {
-#pragma unroll 8
-        for (int t = tid; t < splits * W; t += kAttnThreads)
-            stage[t] = p[t];
+#pragma unroll 4
+        for (int t = tid; t < splits * HW; t += kAttnThreads) {
+            const int s = t / HW;
+            stage[t] = p[(size_t)s * W + (t - s * HW)];
+        }
     }
-    const bool do_commit = commit && mc >= 0;  // uniform over the workgroup
+    const bool do_commit = committer && mc >= 0;  // uniform over the workgroup
     if (do_commit && tid == 0)
         sNow = atomicAdd(&clock[row], 1u) + 1u;
     n = min(max(n, 0), k);
-    const float *src = staged ? stage : p;  // LDS or global, same layout [splits][G][D + 2]
+    // split s's partial at src + s * stride, staged or in place
+    const float *src = staged ? stage : p;
+    const int stride = staged ? HW : W;
     if (splits > 1) {
         __syncthreads();
-        for (int t = tid; t < splits * G; t += kAttnThreads) {
-            const int s = t / G, g = t - s * G;
-            sw[g][s] = src[s * W + g * (D + 2) + D];
-            sl[g][s] = src[s * W + g * (D + 2) + D + 1];
+        if (tid < 64) {
+            const int s0 = tid, s1 = tid + 64;
+            const float m0 = s0 < splits ? src[s0 * stride + D] : -__builtin_inff();
+            const float m1 = s1 < splits ? src[s1 * stride + D] : -__builtin_inff();
+            const float M = wave_max(fmaxf(m0, m1));
+            float w0 = 0.0f, w1 = 0.0f, l = 0.0f;
+            if (M != -__builtin_inff()) {
+                w0 = s0 < splits ? exp2f(m0 - M) : 0.0f;
+                w1 = s1 < splits ? exp2f(m1 - M) : 0.0f;
+                l = (s0 < splits ? w0 * src[s0 * stride + D + 1] : 0.0f) +
+                    (s1 < splits ? w1 * src[s1 * stride + D + 1] : 0.0f);
+            }
+            const float L = rows_sum(group_sum<16>(l));
+            if (s0 < splits)
+                sw[s0] = L > 0.0f ? w0 : 0.0f;
+            if (s1 < splits)
+                sw[s1] = L > 0.0f ? w1 : 0.0f;
+            if (tid == 0) {
+                shM = M;
+                shL = L;
+            }
         }
         __syncthreads();
-        if (tid < G) {
-            float M = -__builtin_inff();
-            for (int s = 0; s < splits; ++s)
-                M = fmaxf(M, sw[tid][s]);
-            float L = 0.0f;
-            if (M != -__builtin_inff())
-                for (int s = 0; s < splits; ++s)
-                    L = __builtin_fmaf(exp2f(sw[tid][s] - M), sl[tid][s], L);
-            shM[tid] = M;
-            shL[tid] = L;
-        }
-        __syncthreads();
-        for (int t = tid; t < splits * G; t += kAttnThreads) {
-            const int s = t / G, g = t - s * G;
-            sw[g][s] = shL[g] > 0.0f ? exp2f(sw[g][s] - shM[g]) : 0.0f;
-        }
-        __syncthreads();
-        float *o = out + ((size_t)b * Hq + (size_t)j * G) * D;
-        for (int idx = tid; idx < G * D; idx += kAttnThreads) {
-            const int g = idx / D, d = idx - g * D;
-            const float L = shL[g];
+        const float L = shL;
+        float *o = out + ((size_t)b * Hq + (size_t)j * G + g) * D;
+        for (int d = tid; d < D; d += kAttnThreads) {
             float a = 0.0f;
 #pragma unroll 8
             for (int s = 0; s < splits; ++s)
-                a = __builtin_fmaf(sw[g][s], src[s * W + g * (D + 2) + d], a);
-            o[idx] = L > 0.0f ? a / L : 0.0f;
+                a = __builtin_fmaf(sw[s], src[s * stride + d], a);
+            o[d] = L > 0.0f ? a / L : 0.0f;
         }
-        if (lse && tid < G)
-            lse[(size_t)b * Hq + (size_t)j * G + tid] =
-                shL[tid] > 0.0f ? shM[tid] * kLn2 + logf(shL[tid]) : -__builtin_inff();
+        if (lse && tid == 0)
+            lse[(size_t)b * Hq + (size_t)j * G + g] = L > 0.0f ? shM * kLn2 + logf(L) : -__builtin_inff();
     }
     if (do_commit) {
         __syncthreads();
@@ -895,8 +907,8 @@ static hipError_t attn_t(const Dims &d, const AttnArgs &a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1)
         return e;
-    hipLaunchKernelGGL(merge_commit_kernel, dim3(d.rows()), dim3(kAttnThreads), 0, st, (const float *)part, d.Hq,
-                       d.Hkv, d.D, a.splits, a.out, a.lse, 0, a.k, a.cap, nullptr, nullptr, nullptr, nullptr, nullptr,
+    hipLaunchKernelGGL(merge_commit_kernel, dim3(d.G(), d.rows()), dim3(kAttnThreads), 0, st, (const float *)part,
+                       d.Hq, d.Hkv, d.D, a.splits, a.out, a.lse, 0, a.k, a.cap, nullptr, nullptr, nullptr, nullptr, nullptr,
                        nullptr, nullptr);
     return hipGetLastError();
 }
@@ -944,8 +956,8 @@ static hipError_t fused_t(const Dims &d, const FusedArgs &f, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || f.splits == 1)  // one split per row: the kernel wrote out / lse and committed
         return e;
-    hipLaunchKernelGGL(merge_commit_kernel, dim3(d.rows()), dim3(kAttnThreads), 0, st, (const float *)part, d.Hq,
-                       d.Hkv, d.D, f.splits, f.out, f.lse, 1, f.k, f.cap, f.sel_blocks, f.sel_count, f.sel_slot,
+    hipLaunchKernelGGL(merge_commit_kernel, dim3(d.G(), d.rows()), dim3(kAttnThreads), 0, st, (const float *)part,
+                       d.Hq, d.Hkv, d.D, f.splits, f.out, f.lse, 1, f.k, f.cap, f.sel_blocks, f.sel_count, f.sel_slot,
                        f.miss_count, f.slot_block, f.slot_stamp, f.clock);
     return hipGetLastError();
 }
