@@ -684,6 +684,13 @@ __global__ __launch_bounds__(kAttnThreads, (fused_min_waves<E, D, GMAX, LONG ? 3
     first.have = false;
     auto load_first = [&](int nn) {
         if constexpr (attn_matrix_cores<E>() && depth == 1) {
+            // Every load issued before (scores, slot table, query) has long
+            // landed.  Waiting for them here costs nothing and tells the
+            // compiler that none is pending: otherwise, where this branch
+            // rejoins, it assumes an older load may still be in flight and
+            // makes the rest of the plan wait for this block's loads before
+            // reusing that load's registers.
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             const int i0 = split * per_split;
             const int i = i0 + (threadIdx.x >> 6);
             if (i < min(i0 + per_split, nn)) {
