@@ -50,7 +50,9 @@ KERNEL_SOURCES = {
 }
 KERNEL_NAMES = {"score": "score_blockmax", "select_attend": "select_attend_kernel",
                 "merge_commit": "merge_commit_kernel"}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama8b_32k_step_traffic.json")
+def traffic_file(workload: str) -> str:
+    """The counter-traffic summary of a workload's step (JSON; a markdown twin beside it)."""
+    return os.path.join(ROOT, "profiles", f"{workload}_step_traffic.json")
 
 
 # ---------------------------------------------------------------- byte model
@@ -133,11 +135,17 @@ def _sources_sha(kernel: str = "score") -> str:
     return h.hexdigest()[:16]
 
 
+def _kernel_names(w) -> dict:
+    """Kernel-name patterns of the step's three counted kernels: the scan of
+    this workload's scoring mode, the fused select-attend, the merge."""
+    return dict(KERNEL_NAMES, score="score_quest" if w.scoring == "quest" else "score_blockmax")
+
+
 def _traffic(w):
     """Counter-derived HBM bytes per scoring launch, if the counters were
     taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(w.name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -229,21 +237,27 @@ def pmc_pass(args):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda() \
         if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda()
     q, sq, dK, dV, dlens = dev(data["q"]), dev(data["score_q"]), dev(data["K"]), dev(data["V"]), dev(data["seq_lens"])
+    mode = B.SKV_SCORE_QUEST if w.scoring == "quest" else B.SKV_SCORE_BLOCKMAX
     cfg = StepConfig(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype, w.k_blocks, w.capacity,
-                     n_queries=w.n_score_queries)
+                     mode=mode, n_queries=w.n_score_queries, sink=w.sink, recent=w.recent)
     buf = LayerBuffers(cfg)
+    keys_or_meta = dK
+    if mode == B.SKV_SCORE_QUEST:  # the Quest scan reads the per-block boxes
+        keys_or_meta = torch.empty(w.batch, w.n_kv_heads, cfg.nb, 2, w.head_dim, dtype=cfg.torch_dtype,
+                                   device="cuda")
+        B.sparse_kv_quest_meta(cfg.shape, dK, dlens, keys_or_meta)
     n = COPY_MIB << 20
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     for t in range(args.steps):
-        B.sparse_kv_score(cfg.shape, B.SKV_SCORE_BLOCKMAX, sq[t], cfg.n_queries, dK, dlens, cfg.softmax_scale,
+        B.sparse_kv_score(cfg.shape, mode, sq[t], cfg.n_queries, keys_or_meta, dlens, cfg.softmax_scale,
                           buf.scores)
     buf.reset()
     misses = torch.zeros(n_fused, dtype=torch.int64, device="cuda")
     for t in range(n_fused):
-        buf.score(sq[t], dK, dlens)
+        buf.score(sq[t], keys_or_meta, dlens)
         buf.select_attend(q[t], dlens, dK, dV)
         misses[t] = buf.miss_count.sum()
     torch.cuda.synchronize()
@@ -278,17 +292,17 @@ def _dispatch_order(r):
 XCHECK_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_MISS_sum")
 
 
-def _xcheck(path, steps):
+def _xcheck(path, steps, names):
     """Raw counters of a third --pmc run (XCHECK_COUNTERS): L2-to-memory
     read requests, their 32-byte and 128-byte ('bubble') parts, and L2
-    misses (reads and writes), per kernel."""
+    misses (reads and writes), per kernel (`names`: kernel-name patterns)."""
     rows = _counter_rows(path)
     out = {}
     for counter in XCHECK_COUNTERS:
         rs = [r for r in rows if r.get("Counter_Name") == counter]
         copy = [float(r["Counter_Value"]) for r in rs if "copybuffer" in r["Kernel_Name"].lower()]
         per = {}
-        for kname, pat in KERNEL_NAMES.items():
+        for kname, pat in names.items():
             ks = sorted((r for r in rs if pat in r["Kernel_Name"]), key=_dispatch_order)
             vals = [float(r["Counter_Value"]) for r in ks][-steps:]
             per[kname] = float(np.mean(vals)) if vals else None
@@ -307,6 +321,7 @@ def traffic_summary(fetch_dir, write_dir, misses_file, workload, xcheck_dir=None
     from top_sparse_kv_block_amd import synth
 
     w = synth.WORKLOADS[workload]
+    names = _kernel_names(w)
     with open(misses_file) as f:
         mf = json.load(f)
     steps, splits, miss = mf["steps"], mf["splits"], mf["misses"]
@@ -321,7 +336,7 @@ def traffic_summary(fetch_dir, write_dir, misses_file, workload, xcheck_dir=None
             raise SystemExit(f"{counter}: no calibration copy dispatch")
         factor = (COPY_MIB << 20) / (max(copy) * 1024.0)
         per = {}
-        for kname, pat in KERNEL_NAMES.items():
+        for kname, pat in names.items():
             ks = sorted((r for r in rows if pat in r["Kernel_Name"]), key=_dispatch_order)
             vals = [float(r["Counter_Value"]) for r in ks][-steps:]
             if not vals:
@@ -330,17 +345,17 @@ def traffic_summary(fetch_dir, write_dir, misses_file, workload, xcheck_dir=None
                               dispatches=len(vals))
         counters[counter] = dict(copy_kib=max(copy), factor=factor, kernels=per)
     kernels = {}
-    for kname in KERNEL_NAMES:
+    for kname in names:
         fetch = counters["FETCH_SIZE"]["kernels"][kname]["bytes"]
         write = counters["WRITE_SIZE"]["kernels"][kname]["bytes"]
         a = float(np.mean(algo[kname]))
-        kernels[kname] = dict(kernel=KERNEL_NAMES[kname], source_sha=_sources_sha(kname),
+        kernels[kname] = dict(kernel=names[kname], source_sha=_sources_sha(kname),
                               bytes_per_launch=int(round(fetch + write)), fetch_bytes=int(round(fetch)),
                               write_bytes=int(round(write)), algorithmic_bytes_per_launch=int(round(a)),
                               ratio=round((fetch + write) / a, 4))
     xc = None
     if xcheck_dir:
-        xc = _xcheck(xcheck_dir, steps)
+        xc = _xcheck(xcheck_dir, steps, names)
         # read requests against the copy's reads; L2 misses against the
         # copy's reads and writes (a write also misses once per line)
         for counter, copy_bytes in (("TCC_EA0_RDREQ_sum", float(COPY_MIB << 20)),
@@ -350,28 +365,30 @@ def traffic_summary(fetch_dir, write_dir, misses_file, workload, xcheck_dir=None
                 continue
             unit = copy_bytes / c["copy"]  # bytes per request / per miss of the calibration copy
             c["bytes_per_unit"] = unit
-            for kname in KERNEL_NAMES:
+            for kname in names:
                 v = c["kernels"][kname]
                 kernels[kname][f"bytes_from_{counter}"] = int(round(v * unit)) if v is not None else None
     res = dict(workload=w.name, steps=steps, splits=splits, miss_blocks_per_step=float(np.mean(miss)),
                kernels=kernels, counters=counters, xcheck=xc)
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    out_json = traffic_file(w.name)
+    pdir = "pmc" if w.name == "llama8b_32k" else f"pmc_{w.name}"  # the counter runs' output folders
+    os.makedirs(os.path.dirname(out_json), exist_ok=True)
+    with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
-    md = TRAFFIC_FILE.replace(".json", ".md")
+    md = out_json.replace(".json", ".md")
     with open(md, "w") as f:
         f.write(f"# HBM traffic of the step's kernels, {w.name} workload\n\n"
                 "Counter runs (one MI355X; `$REPO` is the repository root), then the summary:\n\n```\n"
-                "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_fetch -o f -- "
+                f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/{pdir}_fetch -o f -- "
                 f"python3 $REPO/bench.py --pmc-pass --steps {steps} --warmup {mf['warmup']} --workload {w.name} "
-                "--pmc-out $REPO/gpurun_out/pmc_misses.json\n"
-                "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_write -o w -- "
+                f"--pmc-out $REPO/gpurun_out/{pdir}_misses.json\n"
+                f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/{pdir}_write -o w -- "
                 f"python3 $REPO/bench.py --pmc-pass --steps {steps} --warmup {mf['warmup']} --workload {w.name}\n"
                 "cd /tmp && rocprofv3 --pmc " + " ".join(XCHECK_COUNTERS) + " --output-format csv -d "
-                "$REPO/gpurun_out/pmc_xcheck -o x -- "
+                f"$REPO/gpurun_out/{pdir}_xcheck -o x -- "
                 f"python3 $REPO/bench.py --pmc-pass --steps {steps} --warmup {mf['warmup']} --workload {w.name}\n"
-                "python3 bench.py --traffic-summary gpurun_out/pmc_fetch gpurun_out/pmc_write "
-                "gpurun_out/pmc_misses.json gpurun_out/pmc_xcheck\n```\n\n"
+                f"python3 bench.py --workload {w.name} --traffic-summary gpurun_out/{pdir}_fetch "
+                f"gpurun_out/{pdir}_write gpurun_out/{pdir}_misses.json gpurun_out/{pdir}_xcheck\n```\n\n"
                 f"Calibration: a plain device copy of {COPY_MIB} MiB; each counter is scaled so that the copy "
                 f"reads (writes) exactly {COPY_MIB} MiB.  Scale factors: FETCH_SIZE "
                 f"{counters['FETCH_SIZE']['factor']:.4f}, WRITE_SIZE {counters['WRITE_SIZE']['factor']:.4f}.  The "
