@@ -47,9 +47,14 @@ KERNEL_SOURCES = {
     "select_attend": ("top_sparse_kv_block_amd/csrc/attention.hip", "top_sparse_kv_block_amd/csrc/skv_rowops.h",
                       "top_sparse_kv_block_amd/csrc/skv_device.h"),
     "merge_commit": ("top_sparse_kv_block_amd/csrc/attention.hip", "top_sparse_kv_block_amd/csrc/skv_device.h"),
+    "topk_chunk": ("top_sparse_kv_block_amd/csrc/topk.hip", "top_sparse_kv_block_amd/csrc/skv_rowops.h",
+                   "top_sparse_kv_block_amd/csrc/skv_device.h"),
 }
 KERNEL_NAMES = {"score": "score_blockmax", "select_attend": "select_attend_kernel",
                 "merge_commit": "merge_commit_kernel"}
+LONG_ROW_BLOCKS = 16384  # rows past this run the top-k's chunk launch before the fused kernel
+
+
 def traffic_file(workload: str) -> str:
     """The counter-traffic summary of a workload's step (JSON; a markdown twin beside it)."""
     return os.path.join(ROOT, "profiles", f"{workload}_step_traffic.json")
@@ -100,16 +105,33 @@ def _score_kernel_name(w) -> str:
     return "score_blockmax_mfma_kernel" if w.dtype == "bf16" else "score_blockmax_kernel"
 
 
+def chunk_candidate_bytes(w) -> int:
+    """Bytes of the chunk candidates of rows past LONG_ROW_BLOCKS blocks
+    ((score, id) pairs; the library's top-k workspace size), else 0."""
+    if w.nb_max <= LONG_ROW_BLOCKS:
+        return 0
+    from top_sparse_kv_block_amd import binding as B
+    shape = B.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx, w.dtype)
+    return int(B.sparse_kv_topk_workspace_bytes(shape, w.k_blocks))
+
+
 def fused_launch_bytes(w, misses: float, splits: int) -> int:
-    """Algorithmic bytes of one select-attend launch: the row's scores and
-    slot table (with stamps) read once, every selected block's K and V read
-    once (hits from the pool, misses from the source), each miss written
-    into its pool slot, q read, the split partials and the step's lists
-    written."""
+    """Algorithmic bytes of one select-attend launch: the row's scores (past
+    LONG_ROW_BLOCKS blocks: its chunk candidates) and slot table (with
+    stamps) read once, every selected block's K and V read once (hits from
+    the pool, misses from the source), each miss written into its pool
+    slot, q read, the split partials and the step's lists written."""
     P, e, D, G = w.rows, w.elem_bytes, w.head_dim, w.group
     blk = 16 * D * e
-    return int(P * w.nb_max * 4 + P * w.capacity * 8 + P * w.k_blocks * blk * 2 + misses * blk * 2
+    sel_in = chunk_candidate_bytes(w) or P * w.nb_max * 4
+    return int(sel_in + P * w.capacity * 8 + P * w.k_blocks * blk * 2 + misses * blk * 2
                + w.batch * w.n_q_heads * D * e + P * splits * G * (D + 2) * 4 + P * w.k_blocks * 17 + P * 8)
+
+
+def chunk_launch_bytes(w) -> int:
+    """Algorithmic bytes of the top-k's chunk launch: every score read once,
+    the chunk candidates written."""
+    return int(w.rows * w.nb_max * 4 + chunk_candidate_bytes(w))
 
 
 def merge_launch_bytes(w, splits: int) -> int:
@@ -136,9 +158,13 @@ def _sources_sha(kernel: str = "score") -> str:
 
 
 def _kernel_names(w) -> dict:
-    """Kernel-name patterns of the step's three counted kernels: the scan of
-    this workload's scoring mode, the fused select-attend, the merge."""
-    return dict(KERNEL_NAMES, score="score_quest" if w.scoring == "quest" else "score_blockmax")
+    """Kernel-name patterns of the step's counted kernels: the scan of this
+    workload's scoring mode, the fused select-attend, the merge, and (rows
+    past LONG_ROW_BLOCKS blocks) the top-k's chunk launch."""
+    names = dict(KERNEL_NAMES, score="score_quest" if w.scoring == "quest" else "score_blockmax")
+    if w.nb_max > LONG_ROW_BLOCKS:
+        names["topk_chunk"] = "topk_chunk_kernel"
+    return names
 
 
 def _traffic(w):
@@ -327,7 +353,8 @@ def traffic_summary(fetch_dir, write_dir, misses_file, workload, xcheck_dir=None
     steps, splits, miss = mf["steps"], mf["splits"], mf["misses"]
     algo = {"score": [score_launch_bytes(w)] * steps,
             "select_attend": [fused_launch_bytes(w, m, splits) for m in miss],
-            "merge_commit": [merge_launch_bytes(w, splits)] * steps}
+            "merge_commit": [merge_launch_bytes(w, splits)] * steps,
+            "topk_chunk": [chunk_launch_bytes(w)] * steps}
     counters = {}
     for counter, path in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == counter]
